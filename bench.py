@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Benchmark: NVFP4 sparse-MLA decode on one MI355X.
+
+One step = the whole hot path for one decode step of the workload: the
+quantize-append of the step's new rows (one per token) plus one sparse
+decode launch over every token's selected rows.  Inputs are synthetic and
+seeded (synth/), resident in HBM before timing starts.
+
+Default workload: 15 query tokens (one per sequence), 32 heads, top-2048
+distinct picks from each sequence's 146,000 rows, 2.2M-row NVFP4 pool.
+
+Timing: W untimed warm-up steps, then K timed steps.  By default the caches
+are cold for every step: a 1 GiB read sweep runs between steps (outside the
+per-step events) so neither the 256 MB Infinity Cache nor L2 holds the
+gathered rows.  Every launch is bracketed by HIP events on the stream the
+kernels run on.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--warm] [--no-comparators] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-MLA decode µs/step + gathered HBM GB/s (NVFP4 KV, top-2048)"
+HBM_PEAK_GBS = 8000.0
+ROW_BYTES = 352
+FP8_ROW_BYTES = 576
+
+DESCRIPTIONS = {
+    "tiny": "1 token x 16 heads, 256 picks of a 4,096-row NVFP4 pool",
+    "decode15": "15 tokens (1 per sequence) x 32 heads, top-2048 of 146,000 rows each, 2.2M-row NVFP4 pool",
+    "padded35": "35 tokens x 32 heads, contexts 256..8192 rows, 2048-slot lists padded with -1",
+    "batch128": "128 tokens x 32 heads, top-2048 of 140K-146K rows via a 64-row block table, 1.63M-row pool",
+    "prefill4k": "4096 tokens from 4 sequences x 32 heads, causal top-2048 (128 recent + 1920 older)",
+}
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode15")
+    ap.add_argument("--warm", action="store_true", help="no cache flush between steps")
+    ap.add_argument("--splits", type=int, default=0, help="force the split count (0 = launch sizer)")
+    ap.add_argument("--no-comparators", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+class Timer:
+    """Per-launch HIP events on torch's current stream (the stream the library uses)."""
+
+    def __init__(self, torch, n):
+        self.torch = torch
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+
+    def mark(self, i, k):
+        self.ev[i][k].record()
+
+    def spans(self, a, b):
+        return [e[a].elapsed_time(e[b]) for e in self.ev]
+
+
+def _gpu_run(args):
+    import torch
+
+    import nvfp4_compressed_sparse_mla_amd as mla
+    from synth import make_workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = make_workload(args.workload, dev)
+    T, H, K = w.tokens, w.heads, w.topk
+    rows = w.pool_rows
+    cache = torch.empty((rows, ROW_BYTES), dtype=torch.uint8, device=dev)
+    mla.quantize_append(w.latent, w.rope, torch.arange(rows, dtype=torch.int64, device=dev), cache)
+    keep = w.append_slots >= 0
+    app_slots = w.append_slots.clone()
+    app_idx = torch.where(keep, w.append_slots, torch.zeros_like(w.append_slots))
+    app_lat = w.latent[app_idx].contiguous()      # each token's own row, same values: the step is repeatable
+    app_rope = w.rope[app_idx].contiguous()
+    splits = args.splits or mla.num_splits(T, H, K)
+    ws = mla.make_workspace(T, H, K, dev, splits)
+    out = torch.empty((T, H, 512), dtype=w.q.dtype, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    flush = None if args.warm else torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+    if flush is not None:
+        flush.fill_(1.0)
+    valid = w.valid_slots()
+    gathered = valid * ROW_BYTES
+
+    def do_flush():
+        if flush is not None:
+            flush.sum()
+
+    def step(tm=None, i=0):
+        if tm:
+            tm.mark(i, 0)
+        mla.quantize_append(app_lat, app_rope, app_slots, cache)
+        if tm:
+            tm.mark(i, 1)
+        mla.sparse_decode(w.q, cache, w.indices, w.sm_scale, block_table=w.block_table,
+                          token_seq=w.token_seq, block_size=w.block_size, workspace=ws,
+                          num_splits=splits, out=out, lse=lse)
+        if tm:
+            tm.mark(i, 2)
+
+    for _ in range(args.warmup):
+        do_flush()
+        step()
+    torch.cuda.synchronize()
+    tm = Timer(torch, args.steps)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        do_flush()
+        step(tm, i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = tm.spans(0, 2)
+    dec_ms = tm.spans(1, 2)
+    app_ms = tm.spans(0, 1)
+    res = {
+        "T": T, "H": H, "K": K, "rows": rows, "splits": splits, "valid": valid, "gathered": gathered,
+        "step_ms": statistics.mean(step_ms), "decode_ms": statistics.mean(dec_ms),
+        "decode_ms_median": statistics.median(dec_ms),
+        "decode_ms_p10": sorted(dec_ms)[len(dec_ms) // 10],
+        "decode_ms_p90": sorted(dec_ms)[(9 * len(dec_ms)) // 10],
+        "append_ms": statistics.mean(app_ms), "wall_ms_per_iter": 1e3 * wall / args.steps,
+    }
+
+    if not args.no_comparators:
+        res["comparators"] = _comparators(args, torch, mla, w, cache, dev, splits, do_flush)
+    return res, w
+
+
+def _comparators(args, torch, mla, w, cache, dev, splits, do_flush):
+    """FP8-576 rows (same values, 576-byte rows) and the staged path
+    (gather-dequant the selected NVFP4 rows into an FP8 buffer, then FP8 decode)."""
+    T, H, K = w.tokens, w.heads, w.topk
+    n = max(10, args.steps // 2)
+    c8 = torch.empty((w.pool_rows, FP8_ROW_BYTES), dtype=torch.uint8, device=dev)
+    mla.fp8_quantize_append(w.latent, w.rope, torch.arange(w.pool_rows, device=dev), c8, 1.0)
+    ws = mla.make_workspace(T, H, K, dev, splits)
+    staged_rows = torch.empty((T * K, FP8_ROW_BYTES), dtype=torch.uint8, device=dev)
+    staged_idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    out = torch.empty((T, H, 512), dtype=w.q.dtype, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+
+    def fp8_decode():
+        mla.sparse_decode(w.q, c8, w.indices, w.sm_scale, fmt="fp8", block_table=w.block_table,
+                          token_seq=w.token_seq, block_size=w.block_size, workspace=ws,
+                          num_splits=splits, out=out, lse=lse)
+
+    def staged(tm=None, i=0):
+        mla.gather_dequant_fp8(cache, w.indices, 1.0, block_table=w.block_table, token_seq=w.token_seq,
+                               block_size=w.block_size, rows=staged_rows, staged_indices=staged_idx)
+        if tm:
+            tm.mark(i, 1)
+        mla.sparse_decode(w.q, staged_rows, staged_idx, w.sm_scale, fmt="fp8", workspace=ws,
+                          num_splits=splits, out=out, lse=lse)
+
+    r = {}
+    for _ in range(3):
+        do_flush(); fp8_decode(); do_flush(); staged()
+    torch.cuda.synchronize()
+    tm = Timer(torch, n)
+    for i in range(n):
+        do_flush()
+        tm.mark(i, 0)
+        fp8_decode()
+        tm.mark(i, 2)
+    torch.cuda.synchronize()
+    r["fp8_576_decode_us"] = 1e3 * statistics.mean(tm.spans(0, 2))
+    tm = Timer(torch, n)
+    for i in range(n):
+        do_flush()
+        tm.mark(i, 0)
+        staged(tm, i)
+        tm.mark(i, 2)
+    torch.cuda.synchronize()
+    r["staged_total_us"] = 1e3 * statistics.mean(tm.spans(0, 2))
+    r["staged_gather_dequant_us"] = 1e3 * statistics.mean(tm.spans(0, 1))
+    r["staged_fp8_decode_us"] = 1e3 * statistics.mean(tm.spans(1, 2))
+    return r
+
+
+def _cpu_baseline(w, seconds):
+    """The oracle as it stands, on the host cores, over a bounded sample of the
+    same workload: per pass, decode the sampled tokens' selected rows from
+    their 352-byte encodings and run the FP64 attention."""
+    import numpy as np
+
+    from oracle import attention, codec
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    idx = w.indices.cpu().numpy().astype(np.int64)
+    bt = None if w.block_table is None else w.block_table.cpu().numpy().astype(np.int64)
+    seq = None if w.token_seq is None else w.token_seq.cpu().numpy().astype(np.int64)
+    q = w.q.float().cpu().numpy().astype(np.float64)
+    tokens = list(range(w.tokens))
+    # the encoded rows the sample touches (setup, not timed): the pool is already encoded
+    per_tok = []
+    for t in tokens:
+        v = idx[t][idx[t] >= 0]
+        rows = attention.physical_rows(v, None if seq is None else int(seq[t]), bt, w.block_size)
+        sel = __import__("torch").from_numpy(rows).to(w.latent.device)
+        lat16 = w.latent.index_select(0, sel).cpu().numpy().astype(np.float64)
+        rope16 = w.rope.index_select(0, sel).cpu().numpy().astype(np.float64)
+        per_tok.append(codec.nvfp4_encode_rows(lat16, rope16))
+    done_bytes = 0
+    n_tok = 0
+    t0 = time.perf_counter()
+    while True:
+        for t in tokens:
+            enc = per_tok[t]
+            lat, rope = codec.nvfp4_decode_rows(enc)
+            attention.sparse_mla_token(q[t], lat, rope, w.sm_scale)
+            done_bytes += enc.shape[0] * ROW_BYTES
+            n_tok += 1
+            if time.perf_counter() - t0 > seconds:
+                break
+        if time.perf_counter() - t0 > seconds:
+            break
+    el = time.perf_counter() - t0
+    return {
+        "value": done_bytes / el / 1e9, "unit": "GB/s", "cores": blas_threads,
+        "kind": "oracle",
+        "sample": f"{n_tok} token-passes of the {w.name} workload ({n_tok / max(1, len(tokens)):.1f} steps), "
+                  f"NVFP4 row decode + FP64 attention, {el:.1f} s; host os.cpu_count()={os.cpu_count()}",
+        "us_per_step": 1e6 * el * len(tokens) / max(1, n_tok),
+    }
+
+
+def main():
+    args = _parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this implementation runs on one GPU only; the decode path shards "
+                                   "by token/sequence or by head with no exchange, and no multi-GPU "
+                                   "figure is produced", "n_gpus": args.gpus}))
+        sys.exit(2)
+    res, w = _gpu_run(args)
+    dec_s = res["decode_ms"] * 1e-3
+    achieved = res["gathered"] / dec_s / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(res["gathered"] / (res["step_ms"] * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["step_ms"], 5),
+        "us_per_step": round(1e3 * res["step_ms"], 3),
+        "decode_us": round(1e3 * res["decode_ms"], 3),
+        "decode_us_median": round(1e3 * res["decode_ms_median"], 3),
+        "decode_us_p10_p90": [round(1e3 * res["decode_ms_p10"], 3), round(1e3 * res["decode_ms_p90"], 3)],
+        "append_us": round(1e3 * res["append_ms"], 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "cache_state": "warm" if args.warm else "cold (1 GiB sweep between steps)",
+        "config": {"workload": f"{args.workload}: {DESCRIPTIONS.get(args.workload, '')}",
+                   "tokens": res["T"], "heads": res["H"], "topk": res["K"], "pool_rows": res["rows"],
+                   "valid_slots": res["valid"], "gathered_bytes": res["gathered"],
+                   "splits": res["splits"], "cache": "nvfp4-352"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "sparse_decode_kernel", "bytes_per_launch": res["gathered"]},
+    }
+    if "comparators" in res:
+        line["comparators"] = {k: round(v, 3) for k, v in res["comparators"].items()}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = _cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,221 @@
+/*
+ * mla_nvfp4.h -- C ABI of the NVFP4 sparse-MLA decode library for gfx950.
+ *
+ * The operation (Prime Inference write-up, "Making room for low-latency
+ * decode" and "A native NVFP4 sparse-MLA decode kernel"; the wireai.ir
+ * article's 4-bit-caches section):
+ *
+ *   * an MLA cache row holds a 512-value latent stored as four-bit E2M1 values
+ *     with one FP8 (E4M3) scale per group of 16, plus 64 FP8 rope values:
+ *     352 bytes instead of 576;
+ *   * each query token attends only to the positions its sparse indexer chose
+ *     (a fixed-width list, up to 2048 slots, empty slots padded);
+ *   * the chosen rows are unpacked on chip; attention uses FP16 operands with
+ *     FP32 softmax and accumulation;
+ *   * each token's rows are split over several cooperating workgroups whose
+ *     partial results are merged inside the same launch.
+ *
+ * Row layout (bytes): [0,256) latent nibbles, element 2i in the low nibble
+ * of byte i; [256,288) the 32 group scales; [288,352) the 64 rope bytes.
+ * The 576-byte FP8 comparison row is [0,512) latent then [512,576) rope,
+ * each byte E4M3(value / kv_scale).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked "device" must point to device memory of the current
+ *     HIP device; the caller owns every buffer, the library allocates
+ *     nothing per call and keeps no state beyond cached device properties.
+ *   - All work is enqueued on `stream` (a hipStream_t passed as void*,
+ *     NULL = the default stream) and returns without synchronising.
+ *   - Arguments are checked on the host before any HIP call; on a bad
+ *     argument nothing is enqueued and an MLA_ERR_* code is returned.  A
+ *     launch failure reported by the runtime returns MLA_ERR_HIP.
+ *   - Index values are checked on the device: a negative index, an index
+ *     at or beyond cache_rows, or a block-table entry that is negative or
+ *     out of range makes that slot masked (it is never read).
+ *   - No C++ exception crosses this boundary.
+ */
+#ifndef MLA_NVFP4_H
+#define MLA_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum mla_status {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, stride or alignment */
+    MLA_ERR_UNSUPPORTED = 2,  /* enum value or head count not supported       */
+    MLA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required   */
+    MLA_ERR_HIP = 4           /* the HIP runtime reported an error            */
+};
+
+enum mla_dtype { MLA_F16 = 0, MLA_BF16 = 1 };
+enum mla_cache_fmt { MLA_CACHE_NVFP4_352 = 0, MLA_CACHE_FP8_576 = 1 };
+
+#define MLA_LATENT_DIM 512
+#define MLA_ROPE_DIM 64
+#define MLA_QK_DIM 576
+#define MLA_NVFP4_ROW_BYTES 352
+#define MLA_FP8_ROW_BYTES 576
+#define MLA_MAX_TOPK 2048
+
+/*
+ * mla_nvfp4_quantize_append -- encode n rows and store each at its slot.
+ *
+ * Defined by the row format above (write-up, "Making room for low-latency
+ * decode").  For row i with slot_mapping[i] >= 0 and < cache_rows, the
+ * 352-byte row cache[slot_mapping[i]] receives:
+ *   scale_g = E4M3(amax_g / 6) of the exact quotient (round to nearest
+ *             even, saturating at 448), amax_g = max |latent| of group g;
+ *   code_j  = E2M1(latent_j / scale_g) rounded to nearest even, saturating
+ *             at 6, magnitude 0 when scale_g is 0; the sign bit copies the
+ *             input's sign bit;
+ *   rope_k  = E4M3(rope_k), round to nearest even, saturating.
+ * Rows with a negative or out-of-range slot are skipped.
+ *
+ *   latent            device, [n, 512] elements of `dtype`, row stride
+ *                     latent_row_stride elements (>= 512), 16-byte aligned
+ *                     rows (stride a multiple of 8 elements).
+ *   rope              device, [n, 64], row stride rope_row_stride (>= 64,
+ *                     a multiple of 8), 16-byte aligned.
+ *   dtype             MLA_F16 or MLA_BF16.
+ *   slot_mapping      device, [n] int64.
+ *   cache             device, [cache_rows, 352] bytes, 16-byte aligned.
+ * The result is bit-exact and deterministic.  Two rows naming the same
+ * slot race (one of them wins).
+ */
+int mla_nvfp4_quantize_append(const void* latent, int64_t latent_row_stride,
+                              const void* rope, int64_t rope_row_stride,
+                              int dtype, int64_t n,
+                              const int64_t* slot_mapping,
+                              uint8_t* cache, int64_t cache_rows,
+                              void* stream);
+
+/*
+ * mla_fp8_quantize_append -- the comparison format: 576-byte FP8 rows,
+ * byte = E4M3(value / kv_scale) (round to nearest even, saturating), for
+ * the 512 latent values then the 64 rope values.  The FP8 row is the format
+ * the write-up's NVFP4 rows replace ("Making room for low-latency decode").
+ * Arguments as for mla_nvfp4_quantize_append; cache is [cache_rows, 576];
+ * kv_scale must be a positive power of two (so the quotient is exact).
+ */
+int mla_fp8_quantize_append(const void* latent, int64_t latent_row_stride,
+                            const void* rope, int64_t rope_row_stride,
+                            int dtype, int64_t n,
+                            const int64_t* slot_mapping,
+                            uint8_t* cache, int64_t cache_rows,
+                            float kv_scale, void* stream);
+
+/*
+ * mla_sparse_decode_num_splits -- the launch sizer.  Number of workgroups
+ * that share one token's selected rows for a call with these sizes
+ * (num_splits = 0 in mla_sparse_decode).  The split count follows the token
+ * batch the way the write-up's cluster size does (wireai.ir, 4-bit-caches
+ * section, second decision).  Returns >= 1, or 0 on bad arguments.
+ */
+int32_t mla_sparse_decode_num_splits(int64_t num_tokens, int32_t num_heads,
+                                     int32_t topk);
+
+/*
+ * mla_sparse_decode_workspace_size -- bytes of device workspace
+ * mla_sparse_decode needs for these sizes; num_splits = 0 means the launch
+ * sizer's choice.  The workspace must be zero-filled before its first use;
+ * every completed call leaves it in that state again.  Returns 0 on bad
+ * arguments.
+ */
+size_t mla_sparse_decode_workspace_size(int64_t num_tokens, int32_t num_heads,
+                                        int32_t topk, int32_t num_splits);
+
+/*
+ * mla_sparse_decode -- sparse MLA decode attention over a compressed cache.
+ *
+ * For token t and head h, with the valid slots j of indices[t] (index >= 0;
+ * a row listed twice counts twice) mapped to cache rows r_j, keys
+ * k_j = [latent(r_j); rope(r_j)] (576 values) and values v_j = latent(r_j):
+ *   s_j        = sm_scale * (q[t,h] . k_j)
+ *   out[t,h]   = sum_j exp(s_j - m) v_j / sum_j exp(s_j - m),  m = max_j s_j
+ *   lse[t,h]   = m + ln(sum_j exp(s_j - m))
+ * A token with no valid slot gets out = 0 and lse = -inf.  Rows are decoded
+ * on chip to FP16 (exactly: every E2M1 x E4M3 product is an FP16 value);
+ * products accumulate in FP32; softmax runs in FP32; the probabilities
+ * enter the value product as FP16.
+ *
+ *   q                 device, [T, H, 576] of q_dtype; element (t,h,d) at
+ *                     q + t*q_stride_t + h*q_stride_h + d (strides in
+ *                     elements, multiples of 8; 16-byte aligned base).
+ *   q_dtype           MLA_F16 or MLA_BF16 (bf16 is converted to FP16 on load).
+ *   num_tokens (T)    >= 0.  num_heads (H): 16, 32, 64 or 128.
+ *   cache             device, [cache_rows, 352] (NVFP4) or [cache_rows, 576]
+ *                     (FP8), 16-byte aligned.
+ *   cache_fmt         MLA_CACHE_NVFP4_352 or MLA_CACHE_FP8_576.
+ *   kv_scale          FP8 format only: value = E4M3 byte * kv_scale; ignored
+ *                     for NVFP4.
+ *   indices           device, [T, topk] int32, row stride idx_stride_t
+ *                     (>= topk); negative = masked pad.  1 <= topk <= 2048.
+ *   block_table       optional (NULL = indices are physical cache rows).
+ *                     device, [bt_rows, bt_cols] int32, row stride bt_stride;
+ *                     logical position p of sequence b is physical row
+ *                     block_table[b, p / block_size] * block_size
+ *                     + p % block_size.  block_size >= 1.
+ *   token_seq         device, [T] int32 sequence of each token; required
+ *                     with a block table, ignored without one.  A token whose
+ *                     sequence is outside [0, bt_rows) has every slot masked.
+ *   sm_scale          softmax scale applied to q . k.
+ *   out               device, [T, H, 512] of q_dtype, contiguous, 16-byte aligned.
+ *   lse               device, [T, H] float, contiguous; may be NULL.
+ *   workspace         device, workspace_bytes >= the size query's answer for
+ *                     (T, H, topk, num_splits); zero-filled before first use.
+ *   num_splits        0 = launch sizer's choice; otherwise 1..64.
+ * Calls that overlap in time must not share a workspace.
+ */
+int mla_sparse_decode(const void* q, int q_dtype, int64_t num_tokens,
+                      int32_t num_heads, int64_t q_stride_t, int64_t q_stride_h,
+                      const uint8_t* cache, int cache_fmt, int64_t cache_rows,
+                      float kv_scale,
+                      const int32_t* indices, int32_t topk, int64_t idx_stride_t,
+                      const int32_t* block_table, int32_t block_size,
+                      int64_t bt_stride, int32_t bt_rows, int32_t bt_cols,
+                      const int32_t* token_seq,
+                      float sm_scale, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes,
+                      int32_t num_splits, void* stream);
+
+/*
+ * mla_nvfp4_gather_dequant_fp8 -- first step of the staged comparator the
+ * write-up measures against its native kernel (mo.ai.kr article, KV-cache
+ * section; wireai.ir, 4-bit-caches section): unpack the selected NVFP4
+ * rows into an FP8 buffer in device memory ahead of an FP8 attention call.
+ *
+ * For token t and slot j: if the slot is valid (same rules and optional
+ * block table as mla_sparse_decode) the NVFP4 row is decoded and
+ * re-encoded as a 576-byte FP8 row E4M3(value / fp8_scale) (round to
+ * nearest even, saturating) at fp8_rows[t*topk + j], and
+ * staged_indices[t*topk + j] = t*topk + j; a masked slot gets a zero row
+ * and index -1.  fp8_scale must be a positive power of two.
+ *
+ *   fp8_rows          device, [T*topk, 576] bytes, 16-byte aligned.
+ *   staged_indices    device, [T, topk] int32 (contiguous).
+ * mla_sparse_decode(cache = fp8_rows, cache_fmt = MLA_CACHE_FP8_576,
+ * kv_scale = fp8_scale, indices = staged_indices, idx_stride_t = topk)
+ * then completes the staged path.
+ */
+int mla_nvfp4_gather_dequant_fp8(const uint8_t* cache, int64_t cache_rows,
+                                 const int32_t* indices, int64_t num_tokens,
+                                 int32_t topk, int64_t idx_stride_t,
+                                 const int32_t* block_table, int32_t block_size,
+                                 int64_t bt_stride, int32_t bt_rows, int32_t bt_cols,
+                                 const int32_t* token_seq,
+                                 float fp8_scale, uint8_t* fp8_rows,
+                                 int32_t* staged_indices, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* mla_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_NVFP4_H */

@@ -1,0 +1,169 @@
+"""NVFP4-compressed sparse MLA decode for MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/mla_nvfp4.h: it checks
+tensor shapes and dtypes and passes device pointers and the current HIP
+stream.  Every step of the computation runs in the library's HIP kernels;
+PyTorch only provides device memory and streams.
+
+    quantize_append(latent, rope, slots, cache)        352-byte NVFP4 rows
+    fp8_quantize_append(latent, rope, slots, cache)    576-byte FP8 rows
+    sparse_decode(q, cache, indices, sm_scale, ...)    -> (out, lse)
+    gather_dequant_fp8(cache, indices, ...)            staged comparator step
+"""
+
+from __future__ import annotations
+
+import torch
+
+from ._lib import MlaError, check, load  # noqa: F401
+
+LATENT_DIM = 512
+ROPE_DIM = 64
+QK_DIM = 576
+NVFP4_ROW_BYTES = 352
+FP8_ROW_BYTES = 576
+MAX_TOPK = 2048
+
+F16, BF16 = 0, 1
+FMT_NVFP4, FMT_FP8 = 0, 1
+_FMT = {"nvfp4": FMT_NVFP4, "fp8": FMT_FP8}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"expected float16 or bfloat16, got {t.dtype}")
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _rows2d(x: torch.Tensor, width: int, name: str) -> torch.Tensor:
+    if x.dim() != 2 or x.shape[1] != width or x.stride(1) != 1:
+        raise ValueError(f"{name} must be [n, {width}] with unit column stride")
+    return x
+
+
+def _append(fn_name, latent, rope, slots, cache, row_bytes, extra=()):
+    lib = load()
+    _rows2d(latent, LATENT_DIM, "latent")
+    _rows2d(rope, ROPE_DIM, "rope")
+    if latent.dtype != rope.dtype:
+        raise TypeError("latent and rope must share a dtype")
+    if slots.dtype != torch.int64 or slots.dim() != 1 or slots.shape[0] != latent.shape[0]:
+        raise ValueError("slots must be int64 [n]")
+    if rope.shape[0] != latent.shape[0]:
+        raise ValueError("latent and rope must have the same number of rows")
+    if cache.dtype != torch.uint8 or cache.dim() != 2 or cache.shape[1] != row_bytes or not cache.is_contiguous():
+        raise ValueError(f"cache must be contiguous uint8 [rows, {row_bytes}]")
+    slots = slots.contiguous()
+    st = getattr(lib, fn_name)(_ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0),
+                               _dtype_code(latent), latent.shape[0], _ptr(slots), _ptr(cache),
+                               cache.shape[0], *extra, _stream(cache))
+    check(st, fn_name)
+
+
+def quantize_append(latent: torch.Tensor, rope: torch.Tensor, slots: torch.Tensor,
+                    cache: torch.Tensor) -> None:
+    """Encode rows to 352-byte NVFP4 and write them at ``slots`` (negative = skip)."""
+    _append("mla_nvfp4_quantize_append", latent, rope, slots, cache, NVFP4_ROW_BYTES)
+
+
+def fp8_quantize_append(latent, rope, slots, cache, kv_scale: float = 1.0) -> None:
+    """Encode rows to 576-byte FP8 (E4M3 of value / kv_scale) at ``slots``."""
+    _append("mla_fp8_quantize_append", latent, rope, slots, cache, FP8_ROW_BYTES, (float(kv_scale),))
+
+
+def num_splits(tokens: int, heads: int, topk: int) -> int:
+    return int(load().mla_sparse_decode_num_splits(tokens, heads, topk))
+
+
+def workspace_size(tokens: int, heads: int, topk: int, splits: int = 0) -> int:
+    n = int(load().mla_sparse_decode_workspace_size(tokens, heads, topk, splits))
+    if n == 0:
+        raise MlaError("workspace size query rejected its arguments")
+    return n
+
+
+def make_workspace(tokens: int, heads: int, topk: int, device, splits: int = 0) -> torch.Tensor:
+    """A zero-filled workspace for ``sparse_decode`` (reusable across calls)."""
+    return torch.zeros(workspace_size(tokens, heads, topk, splits), dtype=torch.uint8, device=device)
+
+
+def sparse_decode(q: torch.Tensor, cache: torch.Tensor, indices: torch.Tensor, sm_scale: float, *,
+                  fmt: str = "nvfp4", kv_scale: float = 1.0, block_table=None, token_seq=None,
+                  block_size: int = 64, workspace=None, num_splits: int = 0, out=None, lse=None):
+    """Sparse MLA decode; returns (out [T, H, 512] in q's dtype, lse [T, H] float32)."""
+    lib = load()
+    if q.dim() != 3 or q.shape[2] != QK_DIM or q.stride(2) != 1:
+        raise ValueError("q must be [T, H, 576] with unit last stride")
+    T, H = q.shape[0], q.shape[1]
+    fmt_code = _FMT[fmt]
+    row_bytes = NVFP4_ROW_BYTES if fmt_code == FMT_NVFP4 else FP8_ROW_BYTES
+    if cache.dtype != torch.uint8 or cache.dim() != 2 or cache.shape[1] != row_bytes or not cache.is_contiguous():
+        raise ValueError(f"cache must be contiguous uint8 [rows, {row_bytes}]")
+    if indices.dtype != torch.int32 or indices.dim() != 2 or indices.shape[0] != T or indices.stride(1) != 1:
+        raise ValueError("indices must be int32 [T, topk] with unit last stride")
+    topk = indices.shape[1]
+    bt_ptr = ts_ptr = None
+    bt_stride = bt_rows = bt_cols = 0
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+            raise ValueError("block_table must be int32 [seqs, blocks] with unit last stride")
+        if token_seq is None or token_seq.dtype != torch.int32 or token_seq.shape != (T,):
+            raise ValueError("token_seq must be int32 [T] when a block table is given")
+        token_seq = token_seq.contiguous()
+        bt_ptr, ts_ptr = block_table.data_ptr(), token_seq.data_ptr()
+        bt_stride, bt_rows, bt_cols = block_table.stride(0), block_table.shape[0], block_table.shape[1]
+    if out is None:
+        out = torch.empty((T, H, LATENT_DIM), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = make_workspace(T, H, topk, q.device, num_splits)
+    st = lib.mla_sparse_decode(
+        q.data_ptr(), _dtype_code(q), T, H, q.stride(0), q.stride(1),
+        cache.data_ptr(), fmt_code, cache.shape[0], float(kv_scale),
+        indices.data_ptr(), topk, indices.stride(0),
+        bt_ptr, int(block_size), bt_stride, bt_rows, bt_cols, ts_ptr,
+        float(sm_scale), out.data_ptr(), lse.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), int(num_splits), _stream(q))
+    check(st, "mla_sparse_decode")
+    return out, lse
+
+
+def gather_dequant_fp8(cache: torch.Tensor, indices: torch.Tensor, fp8_scale: float = 1.0, *,
+                       block_table=None, token_seq=None, block_size: int = 64,
+                       rows=None, staged_indices=None):
+    """Staged comparator step 1: selected NVFP4 rows -> FP8 rows [T*topk, 576] in HBM."""
+    lib = load()
+    if cache.dtype != torch.uint8 or cache.dim() != 2 or cache.shape[1] != NVFP4_ROW_BYTES:
+        raise ValueError("cache must be uint8 [rows, 352]")
+    T, topk = indices.shape
+    if rows is None:
+        rows = torch.empty((T * topk, FP8_ROW_BYTES), dtype=torch.uint8, device=cache.device)
+    if staged_indices is None:
+        staged_indices = torch.empty((T, topk), dtype=torch.int32, device=cache.device)
+    bt_ptr = ts_ptr = None
+    bt_stride = bt_rows = bt_cols = 0
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+            raise ValueError("block_table must be int32 [seqs, blocks] with unit last stride")
+        if token_seq is None or token_seq.dtype != torch.int32 or token_seq.shape != (T,):
+            raise ValueError("token_seq must be int32 [T] when a block table is given")
+        token_seq = token_seq.contiguous()
+        bt_ptr, ts_ptr = block_table.data_ptr(), token_seq.data_ptr()
+        bt_stride, bt_rows, bt_cols = block_table.stride(0), block_table.shape[0], block_table.shape[1]
+    st = lib.mla_nvfp4_gather_dequant_fp8(
+        cache.data_ptr(), cache.shape[0], indices.data_ptr(), T, topk, indices.stride(0),
+        bt_ptr, int(block_size), bt_stride, bt_rows, bt_cols, ts_ptr, float(fp8_scale),
+        rows.data_ptr(), staged_indices.data_ptr(), _stream(cache))
+    check(st, "mla_nvfp4_gather_dequant_fp8")
+    return rows, staged_indices

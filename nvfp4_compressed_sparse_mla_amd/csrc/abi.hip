@@ -1,0 +1,201 @@
+// The C ABI (declared in include/mla_nvfp4.h): argument checks on the host,
+// then one launch on the caller's stream.  Every check happens before the
+// first HIP call, so a bad call enqueues nothing; no C++ exception leaves
+// this file.
+#include "../../include/mla_nvfp4.h"
+#include "mla_launch.h"
+
+#include <math.h>
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool pow2_scale(float s) {
+  if (!(s > 0.0f) || !isfinite(s)) return false;
+  int e = 0;
+  return frexpf(s, &e) == 0.5f && e >= -20 && e <= 20;
+}
+
+int head_groups(int32_t H) {
+  if (H == 16 || H == 32) return 1;
+  if (H == 64) return 2;
+  if (H == 128) return 4;
+  return 0;
+}
+
+int quantize_checks(const void* latent, int64_t ls, const void* rope, int64_t rs, int dtype,
+                    int64_t n, const int64_t* slots, const uint8_t* cache, int64_t cache_rows) {
+  if (dtype != MLA_F16 && dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (n < 0 || cache_rows < 0) return MLA_ERR_INVALID_ARG;
+  if (n == 0) return MLA_OK;
+  if (!latent || !rope || !slots || !cache) return MLA_ERR_INVALID_ARG;
+  if (ls < MLA_LATENT_DIM || rs < MLA_ROPE_DIM || (ls % 8) || (rs % 8)) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(latent) || !aligned16(rope) || !aligned16(cache)) return MLA_ERR_INVALID_ARG;
+  if (n > (int64_t)0x7FFFFFFF * 8) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported value";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int mla_nvfp4_quantize_append(const void* latent, int64_t latent_row_stride, const void* rope,
+                              int64_t rope_row_stride, int dtype, int64_t n,
+                              const int64_t* slot_mapping, uint8_t* cache, int64_t cache_rows,
+                              void* stream) {
+  int st = quantize_checks(latent, latent_row_stride, rope, rope_row_stride, dtype, n, slot_mapping,
+                           cache, cache_rows);
+  if (st != MLA_OK || n == 0) return st;
+  hipError_t e = mla::launch_nvfp4_quantize(latent, latent_row_stride, rope, rope_row_stride,
+                                            dtype == MLA_BF16, n, slot_mapping, cache, cache_rows,
+                                            (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_fp8_quantize_append(const void* latent, int64_t latent_row_stride, const void* rope,
+                            int64_t rope_row_stride, int dtype, int64_t n,
+                            const int64_t* slot_mapping, uint8_t* cache, int64_t cache_rows,
+                            float kv_scale, void* stream) {
+  int st = quantize_checks(latent, latent_row_stride, rope, rope_row_stride, dtype, n, slot_mapping,
+                           cache, cache_rows);
+  if (st != MLA_OK) return st;
+  if (!pow2_scale(kv_scale)) return MLA_ERR_INVALID_ARG;
+  if (n == 0) return MLA_OK;
+  hipError_t e = mla::launch_fp8_quantize(latent, latent_row_stride, rope, rope_row_stride,
+                                          dtype == MLA_BF16, n, slot_mapping, cache, cache_rows,
+                                          kv_scale, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int32_t mla_sparse_decode_num_splits(int64_t num_tokens, int32_t num_heads, int32_t topk) {
+  if (num_tokens < 0 || head_groups(num_heads) == 0 || topk < 1 || topk > MLA_MAX_TOPK) return 0;
+  return mla::decode_auto_splits(num_tokens, num_heads, topk);
+}
+
+size_t mla_sparse_decode_workspace_size(int64_t num_tokens, int32_t num_heads, int32_t topk,
+                                        int32_t num_splits) {
+  if (num_tokens < 0 || head_groups(num_heads) == 0 || topk < 1 || topk > MLA_MAX_TOPK) return 0;
+  if (num_splits < 0 || num_splits > 64) return 0;
+  const int S = num_splits ? num_splits : mla::decode_auto_splits(num_tokens, num_heads, topk);
+  return mla::decode_workspace_bytes(num_tokens, num_heads, S);
+}
+
+int mla_sparse_decode(const void* q, int q_dtype, int64_t num_tokens, int32_t num_heads,
+                      int64_t q_stride_t, int64_t q_stride_h, const uint8_t* cache, int cache_fmt,
+                      int64_t cache_rows, float kv_scale, const int32_t* indices, int32_t topk,
+                      int64_t idx_stride_t, const int32_t* block_table, int32_t block_size,
+                      int64_t bt_stride, int32_t bt_rows, int32_t bt_cols, const int32_t* token_seq,
+                      float sm_scale,
+                      void* out, float* lse, void* workspace, size_t workspace_bytes,
+                      int32_t num_splits, void* stream) {
+  if (q_dtype != MLA_F16 && q_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (cache_fmt != MLA_CACHE_NVFP4_352 && cache_fmt != MLA_CACHE_FP8_576) return MLA_ERR_UNSUPPORTED;
+  const int G = head_groups(num_heads);
+  if (G == 0) return MLA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || topk < 1 || topk > MLA_MAX_TOPK) return MLA_ERR_INVALID_ARG;
+  if (num_splits < 0 || num_splits > 64) return MLA_ERR_INVALID_ARG;
+  if (cache_rows < 0 || cache_rows > 0x7FFFFFFF) return MLA_ERR_INVALID_ARG;
+  if (!isfinite(sm_scale)) return MLA_ERR_INVALID_ARG;
+  if (cache_fmt == MLA_CACHE_FP8_576 && !pow2_scale(kv_scale)) return MLA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return MLA_OK;
+  if (!q || !cache || !indices || !out) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(cache) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
+  if (q_stride_h < MLA_QK_DIM || (q_stride_h % 8) || (q_stride_t % 8) ||
+      q_stride_t < (int64_t)num_heads * q_stride_h)
+    return MLA_ERR_INVALID_ARG;
+  if (idx_stride_t < topk) return MLA_ERR_INVALID_ARG;
+  if (block_table) {
+    if (!token_seq || block_size < 1 || bt_rows < 1 || bt_cols < 1 || bt_stride < bt_cols)
+      return MLA_ERR_INVALID_ARG;
+  }
+  const int S = num_splits ? num_splits : mla::decode_auto_splits(num_tokens, num_heads, topk);
+  if (S > 1) {
+    const int cap = mla::decode_resident_capacity();
+    if (cap <= 0) return MLA_ERR_HIP;
+    if (num_tokens * G * S > cap) return MLA_ERR_INVALID_ARG;  // the in-launch merge needs co-residency
+  }
+  if (num_tokens * G * S > 0x7FFFFFFF) return MLA_ERR_INVALID_ARG;
+  const size_t need = mla::decode_workspace_bytes(num_tokens, num_heads, S);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
+
+  mla::DecodeParams p;
+  p.q = q;
+  p.q_st = q_stride_t;
+  p.q_sh = q_stride_h;
+  p.T = num_tokens;
+  p.H = num_heads;
+  p.G = G;
+  p.cache = cache;
+  p.cache_rows = cache_rows;
+  p.kv_scale = cache_fmt == MLA_CACHE_FP8_576 ? kv_scale : 1.0f;
+  p.idx = indices;
+  p.topk = topk;
+  p.idx_st = idx_stride_t;
+  p.bt = block_table;
+  p.bs = block_table ? block_size : 1;
+  p.bt_cols = block_table ? bt_cols : 0;
+  p.bt_rows = block_table ? bt_rows : 0;
+  p.bt_st = block_table ? bt_stride : 0;
+  p.tok_seq = block_table ? token_seq : nullptr;
+  p.sm_log2 = sm_scale * 1.4426950408889634f * p.kv_scale;
+  p.out = out;
+  p.lse = lse;
+  const int64_t tg = num_tokens * G;
+  size_t ctr = ((size_t)tg * 2 * sizeof(uint32_t) + 255) & ~(size_t)255;
+  size_t pl = ((size_t)tg * S * 32 * sizeof(float) + 255) & ~(size_t)255;
+  p.counters = reinterpret_cast<uint32_t*>(workspace);
+  p.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ctr);
+  p.part_o = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ctr + pl);
+  p.S = S;
+  hipError_t e = mla::launch_decode(p, cache_fmt, q_dtype == MLA_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_nvfp4_gather_dequant_fp8(const uint8_t* cache, int64_t cache_rows, const int32_t* indices,
+                                 int64_t num_tokens, int32_t topk, int64_t idx_stride_t,
+                                 const int32_t* block_table, int32_t block_size, int64_t bt_stride,
+                                 int32_t bt_rows, int32_t bt_cols, const int32_t* token_seq,
+                                 float fp8_scale,
+                                 uint8_t* fp8_rows, int32_t* staged_indices, void* stream) {
+  if (num_tokens < 0 || topk < 1 || topk > MLA_MAX_TOPK || cache_rows < 0) return MLA_ERR_INVALID_ARG;
+  if (!pow2_scale(fp8_scale)) return MLA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return MLA_OK;
+  if (!cache || !indices || !fp8_rows || !staged_indices) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(cache) || !aligned16(fp8_rows)) return MLA_ERR_INVALID_ARG;
+  if (idx_stride_t < topk) return MLA_ERR_INVALID_ARG;
+  if (block_table && (!token_seq || block_size < 1 || bt_rows < 1 || bt_cols < 1 || bt_stride < bt_cols))
+    return MLA_ERR_INVALID_ARG;
+  if ((num_tokens * topk + 31) / 32 > 0x7FFFFFFF) return MLA_ERR_INVALID_ARG;
+  mla::StagedParams p;
+  p.cache = cache;
+  p.cache_rows = cache_rows;
+  p.idx = indices;
+  p.T = num_tokens;
+  p.topk = topk;
+  p.idx_st = idx_stride_t;
+  p.bt = block_table;
+  p.bs = block_table ? block_size : 1;
+  p.bt_cols = block_table ? bt_cols : 0;
+  p.bt_rows = block_table ? bt_rows : 0;
+  p.bt_st = block_table ? bt_stride : 0;
+  p.tok_seq = block_table ? token_seq : nullptr;
+  p.inv_scale = 1.0f / fp8_scale;
+  p.rows = fp8_rows;
+  p.sidx = staged_indices;
+  hipError_t e = mla::launch_gather_dequant_fp8(p, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // extern "C"

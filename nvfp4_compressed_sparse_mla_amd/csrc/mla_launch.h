@@ -1,0 +1,64 @@
+// Host-side launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct DecodeParams {
+  const void* q;
+  int64_t q_st, q_sh;       // strides in elements
+  int64_t T;
+  int H, G;                 // heads, head groups of 32
+  const uint8_t* cache;
+  int64_t cache_rows;
+  float kv_scale;           // FP8 rows: value = byte * kv_scale (1 for NVFP4)
+  const int32_t* idx;
+  int topk;
+  int64_t idx_st;
+  const int32_t* bt;        // optional block table
+  int bs, bt_rows, bt_cols;
+  int64_t bt_st;
+  const int32_t* tok_seq;
+  float sm_log2;            // sm_scale * log2(e) * kv_scale
+  void* out;
+  float* lse;
+  uint32_t* counters;       // [T*G][2]
+  float* part_lse;          // [T*G][S][32]
+  float* part_o;            // [T*G][S][32][512]
+  int S;                    // splits per (token, head group)
+};
+
+// capacity of co-resident decode workgroups on the current device
+int decode_resident_capacity();
+int decode_auto_splits(int64_t T, int H, int topk);
+size_t decode_workspace_bytes(int64_t T, int H, int S);
+
+hipError_t launch_decode(const DecodeParams& p, int fmt, bool bf16, hipStream_t stream);
+
+hipError_t launch_nvfp4_quantize(const void* latent, int64_t ls, const void* rope, int64_t rs,
+                                 bool bf16, int64_t n, const int64_t* slots, uint8_t* cache,
+                                 int64_t cache_rows, hipStream_t stream);
+hipError_t launch_fp8_quantize(const void* latent, int64_t ls, const void* rope, int64_t rs,
+                               bool bf16, int64_t n, const int64_t* slots, uint8_t* cache,
+                               int64_t cache_rows, float kv_scale, hipStream_t stream);
+
+struct StagedParams {
+  const uint8_t* cache;
+  int64_t cache_rows;
+  const int32_t* idx;
+  int64_t T;
+  int topk;
+  int64_t idx_st;
+  const int32_t* bt;
+  int bs, bt_rows, bt_cols;
+  int64_t bt_st;
+  const int32_t* tok_seq;
+  float inv_scale;
+  uint8_t* rows;
+  int32_t* sidx;
+};
+hipError_t launch_gather_dequant_fp8(const StagedParams& p, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,140 @@
+// Quantize-append kernels: fp16/bf16 rows -> 352-byte NVFP4 rows (and the
+// 576-byte FP8 comparison rows).
+//
+// Format (Prime Inference write-up, "Making room for low-latency decode"):
+// 512 latent values at four bits with one FP8 scale per 16 values, 64 rope
+// values in FP8, 352 bytes per row.  One wave quantizes two rows: lane
+// (row, g) owns latent group g (16 values), its scale byte, and rope values
+// 2g and 2g+1, so every load and store of a row is contiguous across the
+// row's 32 lanes.
+#include "mla_device.h"
+#include "mla_launch.h"
+
+namespace mla {
+
+// Sixteen fp16 or bf16 values as floats (exact), plus their sign bits.
+template <bool kBf16>
+__device__ __forceinline__ void load16(const uint16_t* p, float (&v)[16], uint32_t& signs) {
+  const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(p + 8);
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  signs = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if constexpr (kBf16) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    } else {
+      const half2_t h = as_half2(w[i]);
+      v[2 * i] = (float)h.x;
+      v[2 * i + 1] = (float)h.y;
+    }
+    signs |= ((w[i] >> 15) & 1u) << (2 * i);
+    signs |= ((w[i] >> 31) & 1u) << (2 * i + 1);
+  }
+}
+
+template <bool kBf16>
+__device__ __forceinline__ float load_scalar(const uint16_t* p) {
+  if constexpr (kBf16) return bf16_to_float(*p);
+  else return (float)__builtin_bit_cast(half_t, *p);
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(256) void nvfp4_quantize_append_kernel(
+    const uint16_t* __restrict__ latent, int64_t lat_stride, const uint16_t* __restrict__ rope,
+    int64_t rope_stride, int64_t n, const int64_t* __restrict__ slots, uint8_t* __restrict__ cache,
+    int64_t cache_rows) {
+  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int g = threadIdx.x & 31;
+  if (row >= n) return;
+  const int64_t slot = slots[row];
+  if (slot < 0 || slot >= cache_rows) return;
+
+  float v[16];
+  uint32_t signs;
+  load16<kBf16>(latent + row * lat_stride + 16 * g, v, signs);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+  // scale = E4M3(amax / 6): the correctly rounded float32 quotient rounds to
+  // the same E4M3 value as the exact quotient (an FP16/BF16 amax never puts
+  // it on or across an E4M3 rounding midpoint).
+  const uint32_t sc = e4m3_mag_rne(__fdiv_rn(amax, 6.0f));
+  const float s = e4m3_mag_value(sc);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t nib = e2m1_mag(__builtin_fabsf(v[i]), s) | (((signs >> i) & 1u) << 3);
+    if (i < 8) lo |= nib << (4 * i);
+    else hi |= nib << (4 * (i - 8));
+  }
+  uint8_t* dst = cache + slot * kRowBytes;
+  *reinterpret_cast<u32x2*>(dst + 8 * g) = (u32x2){lo, hi};
+  dst[kScaleOff + g] = (uint8_t)sc;
+  const uint16_t* rp = rope + row * rope_stride + 2 * g;
+  uint32_t r0 = e4m3_encode(load_scalar<kBf16>(rp));
+  uint32_t r1 = e4m3_encode(load_scalar<kBf16>(rp + 1));
+  *reinterpret_cast<uint16_t*>(dst + kRopeOff + 2 * g) = (uint16_t)(r0 | (r1 << 8));
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(256) void fp8_quantize_append_kernel(
+    const uint16_t* __restrict__ latent, int64_t lat_stride, const uint16_t* __restrict__ rope,
+    int64_t rope_stride, int64_t n, const int64_t* __restrict__ slots, uint8_t* __restrict__ cache,
+    int64_t cache_rows, float inv_scale) {
+  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int g = threadIdx.x & 31;
+  if (row >= n) return;
+  const int64_t slot = slots[row];
+  if (slot < 0 || slot >= cache_rows) return;
+  float v[16];
+  uint32_t signs;
+  load16<kBf16>(latent + row * lat_stride + 16 * g, v, signs);
+  uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    // inv_scale is a power of two, so v * inv_scale is the exact quotient
+    uint32_t b = e4m3_mag_rne(__builtin_fabsf(v[i]) * inv_scale) | (((signs >> i) & 1u) << 7);
+    w[i >> 2] |= b << (8 * (i & 3));
+  }
+  uint8_t* dst = cache + slot * kFp8RowBytes;
+  *reinterpret_cast<u32x4*>(dst + 16 * g) = (u32x4){w[0], w[1], w[2], w[3]};
+  const uint16_t* rp = rope + row * rope_stride + 2 * g;
+  uint32_t r0 = e4m3_encode(load_scalar<kBf16>(rp) * inv_scale);
+  uint32_t r1 = e4m3_encode(load_scalar<kBf16>(rp + 1) * inv_scale);
+  *reinterpret_cast<uint16_t*>(dst + kLatent + 2 * g) = (uint16_t)(r0 | (r1 << 8));
+}
+
+hipError_t launch_nvfp4_quantize(const void* latent, int64_t ls, const void* rope, int64_t rs,
+                                 bool bf16, int64_t n, const int64_t* slots, uint8_t* cache,
+                                 int64_t cache_rows, hipStream_t stream) {
+  dim3 grid((unsigned)((n + 7) / 8)), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(nvfp4_quantize_append_kernel<true>, grid, block, 0, stream,
+                       (const uint16_t*)latent, ls, (const uint16_t*)rope, rs, n, slots, cache,
+                       cache_rows);
+  else
+    hipLaunchKernelGGL(nvfp4_quantize_append_kernel<false>, grid, block, 0, stream,
+                       (const uint16_t*)latent, ls, (const uint16_t*)rope, rs, n, slots, cache,
+                       cache_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_quantize(const void* latent, int64_t ls, const void* rope, int64_t rs,
+                               bool bf16, int64_t n, const int64_t* slots, uint8_t* cache,
+                               int64_t cache_rows, float kv_scale, hipStream_t stream) {
+  dim3 grid((unsigned)((n + 7) / 8)), block(256);
+  const float inv = 1.0f / kv_scale;
+  if (bf16)
+    hipLaunchKernelGGL(fp8_quantize_append_kernel<true>, grid, block, 0, stream,
+                       (const uint16_t*)latent, ls, (const uint16_t*)rope, rs, n, slots, cache,
+                       cache_rows, inv);
+  else
+    hipLaunchKernelGGL(fp8_quantize_append_kernel<false>, grid, block, 0, stream,
+                       (const uint16_t*)latent, ls, (const uint16_t*)rope, rs, n, slots, cache,
+                       cache_rows, inv);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -71,24 +71,6 @@ class Workload:
     def valid_slots(self) -> int:
         return int((self.indices >= 0).sum().item())
 
-    def physical_indices(self) -> np.ndarray:
-        """Index lists translated to physical rows on the host (-1 stays -1).
-
-        Plain table lookup used to find which pool rows a token touches; it
-        is input bookkeeping, not part of the method.
-        """
-        idx = self.indices.cpu().numpy().astype(np.int64)
-        if self.block_table is None:
-            return idx
-        bt = self.block_table.cpu().numpy().astype(np.int64)
-        seq = self.token_seq.cpu().numpy().astype(np.int64)
-        out = np.full_like(idx, -1)
-        for t in range(idx.shape[0]):
-            v = idx[t] >= 0
-            p = idx[t][v]
-            out[t][v] = bt[seq[t], p // self.block_size] * self.block_size + p % self.block_size
-        return out
-
 
 def _torch_gen(device, seed: int, chunk: int) -> torch.Generator:
     g = torch.Generator(device=device)

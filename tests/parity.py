@@ -1,0 +1,104 @@
+"""Helpers that run the oracle on the inputs a GPU test used and compare.
+
+The oracle sees only the generator's fp16/bf16 inputs (copied to the host);
+it encodes the touched rows itself, and the GPU's cache bytes for those
+rows are compared with the oracle's encoding bit for bit before anything
+else.  Nothing the HIP path produced is ever fed to the oracle.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import attention, codec
+
+# tolerance from the problem statement: attention output max |err| <=
+# 1e-2 * max |ref| per token, log-sum-exp |err| <= 1e-3 (-inf exactly)
+OUT_RTOL = 1e-2
+LSE_ATOL = 1e-3
+ENC_CHUNK = 2048
+
+
+def encode_rows(lat16: np.ndarray, rope16: np.ndarray, fmt: str = "nvfp4", kv_scale: float = 1.0):
+    """Oracle encoding of rows, in chunks (rows are independent)."""
+    out = []
+    for i in range(0, lat16.shape[0], ENC_CHUNK):
+        l = lat16[i:i + ENC_CHUNK].astype(np.float64)
+        r = rope16[i:i + ENC_CHUNK].astype(np.float64)
+        out.append(codec.nvfp4_encode_rows(l, r) if fmt == "nvfp4" else codec.fp8_encode_rows(l, r, kv_scale))
+    width = codec.ROW_BYTES if fmt == "nvfp4" else codec.FP8_ROW_BYTES
+    return np.concatenate(out, axis=0) if out else np.zeros((0, width), np.uint8)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy()
+
+
+def physical_lists(indices, block_table, token_seq, block_size, tokens):
+    """Per token: the physical rows of its valid slots (oracle's mapping, A4)."""
+    idx = indices.cpu().numpy().astype(np.int64)
+    bt = None if block_table is None else block_table.cpu().numpy().astype(np.int64)
+    seq = None if token_seq is None else token_seq.cpu().numpy().astype(np.int64)
+    lists = []
+    for t in tokens:
+        v = idx[t][idx[t] >= 0]
+        lists.append(attention.physical_rows(v, None if seq is None else int(seq[t]), bt, block_size))
+    return lists
+
+
+def oracle_reference(latent, rope, q, indices, sm_scale, tokens=None, block_table=None,
+                     token_seq=None, block_size=64, gpu_cache=None, fmt="nvfp4", kv_scale=1.0):
+    """Oracle (out, lse) for the chosen tokens; checks the GPU cache bytes of touched rows.
+
+    latent/rope: the fp16/bf16 source tensors of the whole pool (any device).
+    """
+    T = q.shape[0]
+    tokens = list(range(T)) if tokens is None else list(tokens)
+    lists = physical_lists(indices, block_table, token_seq, block_size, tokens)
+    touched = np.unique(np.concatenate(lists)) if any(len(l) for l in lists) else np.zeros(0, np.int64)
+    sel = torch.from_numpy(touched).to(latent.device)
+    lat16 = host(latent.index_select(0, sel)) if len(touched) else np.zeros((0, 512))
+    rope16 = host(rope.index_select(0, sel)) if len(touched) else np.zeros((0, 64))
+    enc = encode_rows(lat16, rope16, fmt, kv_scale)
+    if gpu_cache is not None and len(touched):
+        got = gpu_cache.index_select(0, sel).cpu().numpy()
+        bad = np.nonzero((got != enc).any(axis=1))[0]
+        assert bad.size == 0, f"{bad.size} cache rows differ from the oracle encoding, e.g. row {touched[bad[0]]}"
+    if fmt == "nvfp4":
+        lat, rp = codec.nvfp4_decode_rows(enc)
+    else:
+        lat, rp = codec.fp8_decode_rows(enc, kv_scale)
+    K = max(1, max((len(l) for l in lists), default=1))
+    cidx = np.full((len(tokens), K), -1, dtype=np.int64)
+    for i, l in enumerate(lists):
+        cidx[i, :len(l)] = np.searchsorted(touched, l)
+    qh = host(q)[tokens]
+    return attention.sparse_mla(qh, lat, rp, cidx, sm_scale)
+
+
+def assert_close(out_gpu, lse_gpu, ref_out, ref_lse, tokens=None, what=""):
+    """Per-token tolerance check; returns the worst relative errors seen."""
+    o = out_gpu.float().cpu().numpy().astype(np.float64)
+    l = lse_gpu.cpu().numpy().astype(np.float64)
+    if tokens is not None:
+        o, l = o[tokens], l[tokens]
+    worst_o, worst_l = 0.0, 0.0
+    for i in range(ref_out.shape[0]):
+        ro, rl = ref_out[i], ref_lse[i]
+        empty = np.isneginf(rl)
+        assert np.array_equal(np.isneginf(l[i]), empty), f"{what} token {i}: -inf pattern differs"
+        if empty.all():
+            assert np.all(o[i] == 0.0), f"{what} token {i}: empty token output not zero"
+            continue
+        scale = np.abs(ro).max()
+        err = np.abs(o[i] - ro).max()
+        assert np.isfinite(err) and err <= OUT_RTOL * scale, f"{what} token {i}: max|err| {err:.3e} > 1e-2 * {scale:.3e}"
+        le = np.abs(l[i][~empty] - rl[~empty]).max() if (~empty).any() else 0.0
+        assert le <= LSE_ATOL, f"{what} token {i}: lse err {le:.3e}"
+        assert np.all(o[i][empty] == 0.0)
+        worst_o = max(worst_o, err / scale)
+        worst_l = max(worst_l, le)
+    return worst_o, worst_l

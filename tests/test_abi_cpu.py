@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching the GPU (no compute calls here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from nvfp4_compressed_sparse_mla_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_nvfp4.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"^\s*(?:int|int32_t|size_t|const char\*)\s+(mla_\w+)\s*\(", text, re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libmla_nvfp4.so is not built; run __graft_entry__.build() first")
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = _declared()
+    assert len(names) == 7, names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_status_strings(lib):
+    assert lib.mla_status_string(0) == b"ok"
+    assert lib.mla_status_string(3).startswith(b"workspace")
+    assert lib.mla_status_string(99) == b"unknown status"
+
+
+def _quant(lib, **kw):
+    a = dict(latent=0x1000, ls=512, rope=0x2000, rs=64, dtype=0, n=4, slots=0x3000, cache=0x4000,
+             rows=100, stream=None)
+    a.update(kw)
+    return lib.mla_nvfp4_quantize_append(a["latent"], a["ls"], a["rope"], a["rs"], a["dtype"], a["n"],
+                                         a["slots"], a["cache"], a["rows"], a["stream"])
+
+
+def test_quantize_rejects_bad_arguments(lib):
+    assert _quant(lib, dtype=7) == UNSUPPORTED
+    assert _quant(lib, n=-1) == INVALID
+    assert _quant(lib, n=0, latent=None, rope=None, slots=None, cache=None) == OK
+    assert _quant(lib, latent=None) == INVALID
+    assert _quant(lib, cache=None) == INVALID
+    assert _quant(lib, latent=0x1001) == INVALID            # not 16-byte aligned
+    assert _quant(lib, ls=256) == INVALID                   # stride below 512
+    assert _quant(lib, rs=60) == INVALID
+    assert lib.mla_fp8_quantize_append(0x1000, 512, 0x2000, 64, 0, 4, 0x3000, 0x4000, 10,
+                                       ctypes.c_float(3.0), None) == INVALID   # not a power of two
+
+
+def _decode(lib, **kw):
+    a = dict(q=0x1000, qd=0, T=2, H=32, qst=32 * 576, qsh=576, cache=0x2000, fmt=0, rows=100,
+             kv=1.0, idx=0x3000, topk=64, ist=64, bt=None, bs=64, bst=0, brows=0, bcols=0, ts=None,
+             sm=0.04, out=0x4000, lse=0x5000, ws=0x6000, wsb=1 << 30, splits=1, stream=None)
+    a.update(kw)
+    return lib.mla_sparse_decode(a["q"], a["qd"], a["T"], a["H"], a["qst"], a["qsh"], a["cache"],
+                                 a["fmt"], a["rows"], a["kv"], a["idx"], a["topk"], a["ist"], a["bt"],
+                                 a["bs"], a["bst"], a["brows"], a["bcols"], a["ts"], a["sm"], a["out"], a["lse"],
+                                 a["ws"], a["wsb"], a["splits"], a["stream"])
+
+
+def test_decode_rejects_bad_arguments(lib):
+    assert _decode(lib, qd=5) == UNSUPPORTED
+    assert _decode(lib, fmt=3) == UNSUPPORTED
+    assert _decode(lib, H=24) == UNSUPPORTED
+    assert _decode(lib, topk=0) == INVALID
+    assert _decode(lib, topk=4096, ist=4096) == INVALID
+    assert _decode(lib, T=-1) == INVALID
+    assert _decode(lib, T=0, q=None, cache=None, idx=None, out=None) == OK
+    assert _decode(lib, q=None) == INVALID
+    assert _decode(lib, out=0x4004) == INVALID
+    assert _decode(lib, qsh=500) == INVALID
+    assert _decode(lib, qst=576) == INVALID                 # heads would overlap
+    assert _decode(lib, ist=10) == INVALID
+    assert _decode(lib, bt=0x7000) == INVALID               # block table without token_seq
+    assert _decode(lib, bt=0x7000, ts=0x8000, brows=0, bcols=4, bst=4) == INVALID
+    assert _decode(lib, splits=65) == INVALID
+    assert _decode(lib, fmt=1, kv=0.3) == INVALID
+    assert _decode(lib, sm=float("inf")) == INVALID
+    assert _decode(lib, ws=None) == WORKSPACE
+    assert _decode(lib, wsb=16) == WORKSPACE
+
+
+def test_workspace_size_arithmetic(lib):
+    # one split: only the counters (T*G*2 u32) rounded up to 256 bytes
+    assert lib.mla_sparse_decode_workspace_size(15, 32, 2048, 1) == 256
+    # S splits add an lse block [T*G*S*32] f32 and an O block [T*G*S*32*512] f32
+    s = 4
+    lse = 15 * s * 32 * 4
+    expect = 256 + ((lse + 255) // 256) * 256 + 15 * s * 32 * 512 * 4
+    assert lib.mla_sparse_decode_workspace_size(15, 32, 2048, s) == expect
+    assert lib.mla_sparse_decode_workspace_size(15, 64, 2048, 1) == 256       # 2 head groups
+    assert lib.mla_sparse_decode_workspace_size(15, 24, 2048, 1) == 0
+    assert lib.mla_sparse_decode_workspace_size(15, 32, 0, 1) == 0
+    assert lib.mla_sparse_decode_workspace_size(15, 32, 2048, 99) == 0
+
+
+def test_gather_dequant_rejects_bad_arguments(lib):
+    f = lib.mla_nvfp4_gather_dequant_fp8
+    assert f(0x1000, 10, 0x2000, 1, 8, 8, None, 64, 0, 0, 0, None, ctypes.c_float(0.0), 0x3000, 0x4000, None) == INVALID
+    assert f(0x1000, 10, 0x2000, 1, 0, 8, None, 64, 0, 0, 0, None, ctypes.c_float(1.0), 0x3000, 0x4000, None) == INVALID
+    assert f(0x1000, 10, 0x2000, 0, 8, 8, None, 64, 0, 0, 0, None, ctypes.c_float(1.0), 0x3000, 0x4000, None) == OK
+    assert f(0x1000, 10, None, 1, 8, 8, None, 64, 0, 0, 0, None, ctypes.c_float(1.0), 0x3000, 0x4000, None) == INVALID

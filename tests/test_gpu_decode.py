@@ -1,0 +1,206 @@
+"""GPU sparse MLA decode vs the oracle.
+
+Small cases run the oracle on every token; the full-size workloads (the
+15-token decode point over a 2.2M-row pool, the 128-token block-table batch,
+the 4096-token prefill chunk) run in the launch configuration the benchmark
+times and are checked on sampled tokens.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_compressed_sparse_mla_amd as mla
+from synth import make_custom, make_workload
+import parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _fill(w, fmt="nvfp4", kv_scale=1.0):
+    rows = w.latent.shape[0]
+    slots = torch.arange(rows, dtype=torch.int64, device=DEV)
+    if fmt == "nvfp4":
+        cache = torch.empty((rows, 352), dtype=torch.uint8, device=DEV)
+        mla.quantize_append(w.latent, w.rope, slots, cache)
+    else:
+        cache = torch.empty((rows, 576), dtype=torch.uint8, device=DEV)
+        mla.fp8_quantize_append(w.latent, w.rope, slots, cache, kv_scale)
+    return cache
+
+
+def _run(w, cache, fmt="nvfp4", kv_scale=1.0, num_splits=0, workspace=None):
+    out, lse = mla.sparse_decode(w.q, cache, w.indices, w.sm_scale, fmt=fmt, kv_scale=kv_scale,
+                                 block_table=w.block_table, token_seq=w.token_seq,
+                                 block_size=w.block_size, num_splits=num_splits, workspace=workspace)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _check(w, cache, out, lse, tokens=None, fmt="nvfp4", kv_scale=1.0, what=""):
+    ref_o, ref_l = parity.oracle_reference(w.latent, w.rope, w.q, w.indices, w.sm_scale, tokens=tokens,
+                                           block_table=w.block_table, token_seq=w.token_seq,
+                                           block_size=w.block_size, gpu_cache=cache, fmt=fmt,
+                                           kv_scale=kv_scale)
+    eo, el = parity.assert_close(out, lse, ref_o, ref_l, tokens=tokens, what=what or w.name)
+    print(f"[{what or w.name}] worst out err / max|ref| = {eo:.2e}, worst lse err = {el:.2e}", flush=True)
+    return eo, el
+
+
+def test_tiny_full_parity():
+    w = make_workload("tiny", DEV)
+    cache = _fill(w)
+    out, lse = _run(w, cache)
+    _check(w, cache, out, lse)
+
+
+@pytest.mark.parametrize("pad_random", [False, True])
+def test_padded35_full_parity(pad_random):
+    w = make_workload("padded35", DEV, pad_random=pad_random)
+    cache = _fill(w)
+    out, lse = _run(w, cache)
+    eo, el = _check(w, cache, out, lse)
+    empty = [t for t in range(w.tokens) if (w.indices[t] >= 0).sum() == 0]
+    assert len(empty) == 1
+    assert torch.all(out[empty[0]] == 0) and torch.all(torch.isneginf(lse[empty[0]]))
+
+
+@pytest.mark.parametrize("topk,valid", [(1, [1, 0, 1]), (7, [7, 3, 0]), (33, [33, 32, 1]),
+                                        (100, [64, 65, 100]), (2048, [2048, 1, 777])])
+def test_ragged_tiles_and_tails(topk, valid):
+    w = make_custom(3000, 3, 32, topk, seed=topk, device=DEV, valid_per_token=valid)
+    cache = _fill(w)
+    out, lse = _run(w, cache)
+    _check(w, cache, out, lse, what=f"topk{topk}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16, 64])
+def test_split_count_invariance(splits):
+    w = make_custom(5000, 4, 32, 2048, seed=11, device=DEV, valid_per_token=[2048, 1500, 90, 0])
+    cache = _fill(w)
+    ref_out, ref_lse = _run(w, cache, num_splits=1)
+    out, lse = _run(w, cache, num_splits=splits)
+    _check(w, cache, out, lse, what=f"splits{splits}")
+    assert torch.allclose(out.float(), ref_out.float(), atol=2e-3, rtol=2e-3)
+    fin = torch.isfinite(ref_lse)
+    assert torch.equal(fin, torch.isfinite(lse))
+    assert torch.allclose(lse[fin], ref_lse[fin], atol=1e-4)
+
+
+def test_workspace_reuse_across_calls():
+    w = make_custom(4000, 5, 32, 512, seed=12, device=DEV)
+    cache = _fill(w)
+    ws = mla.make_workspace(5, 32, 512, DEV, splits=6)
+    first = _run(w, cache, num_splits=6, workspace=ws)
+    for _ in range(3):
+        again = _run(w, cache, num_splits=6, workspace=ws)
+        assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1])
+    # the counters are back to zero after every call
+    assert torch.all(ws[:256] == 0)
+
+
+@pytest.mark.parametrize("heads", [16, 64, 128])
+def test_head_counts(heads):
+    w = make_custom(2000, 2, heads, 300, seed=heads, device=DEV, valid_per_token=[300, 150])
+    cache = _fill(w)
+    out, lse = _run(w, cache)
+    _check(w, cache, out, lse, what=f"H{heads}")
+
+
+def test_bf16_queries():
+    w = make_custom(3000, 3, 32, 700, seed=13, device=DEV, q_dtype=torch.bfloat16)
+    cache = _fill(w)
+    out, lse = _run(w, cache)
+    assert out.dtype == torch.bfloat16
+    _check(w, cache, out, lse, what="bf16")
+
+
+def test_duplicates_and_out_of_range_indices():
+    w = make_custom(1000, 2, 32, 64, seed=14, device=DEV)
+    idx = w.indices.clone()
+    idx[0, 10:20] = idx[0, 0]                       # a row listed 11 times counts 11 times
+    idx[1, 5] = 1000                                # past the pool: masked by the guard
+    idx[1, 6] = 2**31 - 1
+    cache = _fill(w)
+    w.indices = idx
+    out, lse = _run(w, cache)
+    ref_idx = idx.clone()
+    ref_idx[1, 5] = -1
+    ref_idx[1, 6] = -1
+    w.indices = ref_idx
+    _check(w, cache, out, lse, what="dups")
+
+
+def test_block_table_small():
+    w = make_custom(64 * 40, 3, 32, 200, seed=15, device=DEV)
+    rng = np.random.default_rng(15)
+    bt = np.stack([rng.permutation(40)[:30] for _ in range(2)]).astype(np.int32)
+    bt[1, 25:] = -1                                 # unassigned blocks
+    seq = np.array([0, 1, 0], dtype=np.int32)
+    idx = np.stack([rng.choice(30 * 64, 200, replace=False) for _ in range(3)]).astype(np.int32)
+    idx[1] = rng.choice(25 * 64, 200, replace=False)
+    idx[2, 150:] = -1
+    w.indices = torch.from_numpy(idx).to(DEV)
+    w.block_table = torch.from_numpy(bt).to(DEV)
+    w.token_seq = torch.from_numpy(seq).to(DEV)
+    cache = _fill(w)
+    out, lse = _run(w, cache)
+    _check(w, cache, out, lse, what="blocktable")
+
+
+def test_fp8_rows_path():
+    w = make_custom(3000, 3, 32, 512, seed=16, device=DEV, valid_per_token=[512, 200, 1])
+    for kv in (1.0, 0.5):
+        cache = _fill(w, "fp8", kv)
+        out, lse = _run(w, cache, fmt="fp8", kv_scale=kv)
+        _check(w, cache, out, lse, fmt="fp8", kv_scale=kv, what=f"fp8 kv={kv}")
+
+
+def test_staged_path_matches_oracle_on_staged_rows():
+    from oracle import attention, codec
+    w = make_custom(3000, 3, 32, 256, seed=17, device=DEV, valid_per_token=[256, 100, 0])
+    cache = _fill(w)
+    rows, sidx = mla.gather_dequant_fp8(cache, w.indices, 1.0)
+    out, lse = mla.sparse_decode(w.q, rows, sidx, w.sm_scale, fmt="fp8", kv_scale=1.0)
+    torch.cuda.synchronize()
+    pool = parity.encode_rows(parity.host(w.latent), parity.host(w.rope))
+    ref_rows, ref_idx = codec.staged_fp8_rows(pool, w.indices.cpu().numpy())
+    assert np.array_equal(rows.cpu().numpy(), ref_rows)
+    lat, rp = codec.fp8_decode_rows(ref_rows)
+    ro, rl = attention.sparse_mla(parity.host(w.q), lat, rp, ref_idx, w.sm_scale)
+    parity.assert_close(out, lse, ro, rl, what="staged")
+
+
+# ------------------------------------------------------------ full-size workloads
+
+def test_decode15_full_size_sampled():
+    w = make_workload("decode15", DEV)
+    cache = _fill(w)
+    out, lse = _run(w, cache)
+    _check(w, cache, out, lse, tokens=[0, 7, 14])
+
+
+def test_batch128_full_size_sampled():
+    w = make_workload("batch128", DEV)
+    cache = _fill(w)
+    out, lse = _run(w, cache)
+    _check(w, cache, out, lse, tokens=[0, 63, 127])
+    # FP8-576 comparison pool of the same shapes
+    c8 = _fill(w, "fp8")
+    o8, l8 = _run(w, c8, fmt="fp8")
+    _check(w, c8, o8, l8, tokens=[5], fmt="fp8", what="batch128-fp8")
+
+
+@pytest.mark.parametrize("qdt", [torch.float16, torch.bfloat16])
+def test_prefill4k_full_size_sampled(qdt):
+    w = make_workload("prefill4k", DEV, q_dtype=qdt)
+    cache = torch.zeros((w.pool_rows, 352), dtype=torch.uint8, device=DEV)
+    # cached rows first, then the chunk's 4096 new rows through quantize-append
+    new = torch.zeros(w.pool_rows, dtype=torch.bool, device=DEV)
+    new[w.append_slots] = True
+    old_slots = torch.nonzero(~new)[:, 0]
+    mla.quantize_append(w.latent[old_slots], w.rope[old_slots], old_slots, cache)
+    mla.quantize_append(w.latent[w.append_slots], w.rope[w.append_slots], w.append_slots, cache)
+    out, lse = _run(w, cache)
+    _check(w, cache, out, lse, tokens=[0, 1023, 1024, 4095], what=f"prefill4k-{qdt}")
