@@ -121,11 +121,6 @@ int mla_sparse_decode(const void* q, int q_dtype, int64_t num_tokens, int32_t nu
       return MLA_ERR_INVALID_ARG;
   }
   const int S = num_splits ? num_splits : mla::decode_auto_splits(num_tokens, num_heads, topk);
-  if (S > 1) {
-    const int cap = mla::decode_resident_capacity();
-    if (cap <= 0) return MLA_ERR_HIP;
-    if (num_tokens * G * S > cap) return MLA_ERR_INVALID_ARG;  // the in-launch merge needs co-residency
-  }
   if (num_tokens * G * S > 0x7FFFFFFF) return MLA_ERR_INVALID_ARG;
   const size_t need = mla::decode_workspace_bytes(num_tokens, num_heads, S);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
@@ -153,11 +148,11 @@ int mla_sparse_decode(const void* q, int q_dtype, int64_t num_tokens, int32_t nu
   p.out = out;
   p.lse = lse;
   const int64_t tg = num_tokens * G;
-  size_t ctr = ((size_t)tg * 2 * sizeof(uint32_t) + 255) & ~(size_t)255;
+  size_t ctr = ((size_t)tg * sizeof(uint32_t) + 255) & ~(size_t)255;
   size_t pl = ((size_t)tg * S * 32 * sizeof(float) + 255) & ~(size_t)255;
   p.counters = reinterpret_cast<uint32_t*>(workspace);
   p.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ctr);
-  p.part_o = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ctr + pl);
+  p.part_o = reinterpret_cast<_Float16*>(reinterpret_cast<char*>(workspace) + ctr + pl);
   p.S = S;
   hipError_t e = mla::launch_decode(p, cache_fmt, q_dtype == MLA_BF16, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;

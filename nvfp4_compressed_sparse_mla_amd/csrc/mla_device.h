@@ -89,6 +89,34 @@ __device__ __forceinline__ half2_t e4m3_to_half2_splat(uint32_t b) {
   return e4m3_pair_to_half2((b & 0xFFu) * 0x00010001u);
 }
 
+// Hardware conversions (gfx950 v_cvt_scalef32_pk_f16_{fp4,fp8}).  These
+// instructions apply only the exponent of their float scale operand, so
+// they are used with scale 1.0 (an exact E2M1 / E4M3 -> FP16 conversion);
+// the E4M3 group scale is applied afterwards with one FP16 multiply, which
+// is exact because every code x scale product is an FP16 value.
+__device__ __forceinline__ half8_t e2m1x8_to_half8_hw(uint32_t w) {
+  const half2_t a = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0));
+  const half2_t b = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
+  const half2_t c = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
+  const half2_t d = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
+  return (half8_t){a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+__device__ __forceinline__ half8_t e4m3x8_to_half8_hw(uint32_t lo, uint32_t hi) {
+  const half2_t a = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false));
+  const half2_t b = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true));
+  const half2_t c = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false));
+  const half2_t d = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true));
+  return (half8_t){a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// Low byte of `b` (an E4M3 scale) as FP16, repeated eight times.
+__device__ __forceinline__ half8_t e4m3_splat8_hw(uint32_t b) {
+  const half2_t v = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b & 0xFFu, 1.0f, false));
+  const half_t s = v.x;
+  return (half8_t){s, s, s, s, s, s, s, s};
+}
+
 // ---------------------------------------------------------------- encode
 
 // E4M3 magnitude code (7 bits) of a >= 0, round to nearest even,

@@ -24,14 +24,12 @@ struct DecodeParams {
   float sm_log2;            // sm_scale * log2(e) * kv_scale
   void* out;
   float* lse;
-  uint32_t* counters;       // [T*G][2]
+  uint32_t* counters;       // [T*G] arrivals per (token, head group)
   float* part_lse;          // [T*G][S][32]
-  float* part_o;            // [T*G][S][32][512]
+  _Float16* part_o;         // [T*G][S][32][512]
   int S;                    // splits per (token, head group)
 };
 
-// capacity of co-resident decode workgroups on the current device
-int decode_resident_capacity();
 int decode_auto_splits(int64_t T, int H, int topk);
 size_t decode_workspace_bytes(int64_t T, int H, int S);
 

@@ -97,12 +97,13 @@ def test_decode_rejects_bad_arguments(lib):
 
 
 def test_workspace_size_arithmetic(lib):
-    # one split: only the counters (T*G*2 u32) rounded up to 256 bytes
+    # one split: only the arrival counters (T*G u32) rounded up to 256 bytes
     assert lib.mla_sparse_decode_workspace_size(15, 32, 2048, 1) == 256
-    # S splits add an lse block [T*G*S*32] f32 and an O block [T*G*S*32*512] f32
+    assert lib.mla_sparse_decode_workspace_size(100, 32, 2048, 1) == 512
+    # S splits add an lse block [T*G*S*32] f32 and an O block [T*G*S*32*512] fp16
     s = 4
     lse = 15 * s * 32 * 4
-    expect = 256 + ((lse + 255) // 256) * 256 + 15 * s * 32 * 512 * 4
+    expect = 256 + ((lse + 255) // 256) * 256 + 15 * s * 32 * 512 * 2
     assert lib.mla_sparse_decode_workspace_size(15, 32, 2048, s) == expect
     assert lib.mla_sparse_decode_workspace_size(15, 64, 2048, 1) == 256       # 2 head groups
     assert lib.mla_sparse_decode_workspace_size(15, 24, 2048, 1) == 0
