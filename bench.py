@@ -57,7 +57,23 @@ def _parse():
     ap.add_argument("--no-comparators", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
+
+
+def _copy_calibration(mib: int, reps: int = 10):
+    """A plain device-to-device copy of known size, for scaling HBM byte counters."""
+    import torch
+
+    n = mib * 1024 * 1024
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                      "launches": reps}), flush=True)
 
 
 class Timer:
@@ -250,6 +266,9 @@ def _cpu_baseline(w, seconds):
 
 def main():
     args = _parse()
+    if args.calibrate_copy:
+        _copy_calibration(args.calibrate_copy)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this implementation runs on one GPU only; the decode path shards "

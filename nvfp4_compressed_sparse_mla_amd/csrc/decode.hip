@@ -8,43 +8,47 @@
 // merged inside the same launch; the split count follows the token batch;
 // padded slots of the fixed-width list are masked and cost nothing.
 //
-// Workgroup = (token t, head group g of 32 heads, split s), 4 waves; wave
-// w = (rb, kh) with rb = w & 1 (which 16 rows of a 32-row tile) and
-// kh = w >> 1 (which half of the 576 key dimensions).  Two workgroups fit
-// on a CU (registers < 256 per lane, LDS < 80 KB), so one workgroup's
-// synchronisation stalls overlap the other's work.
+// Workgroup = (token t, head group g of 32 heads, split s), 4 waves, one
+// workgroup per CU.  Each wave is an independent attention stream over its
+// own 16-row tiles (tiles w, w+4, w+8, ... of the split) with its own DMA
+// ring, its own FP16 V buffer and its own online-softmax state for all 32
+// heads and all 512 output columns, held in accumulation registers.  The
+// tile loop has no barrier: a wave overlaps its own DMA (the next two
+// tiles in flight) with its own MFMA and conversion work.  The four streams
+// merge once, through LDS, at the end; splits merge through the workspace
+// (the split that finishes last merges).
 //
 //   prologue  load the token's index list, translate it through the block
 //             table, drop masked / out-of-range slots and compact the valid
 //             rows into LDS (padded slots are never fetched; split
-//             boundaries balance valid rows).  Load q into registers in the
-//             score MFMA's B-operand layout.
-//   raw ring  the selected rows of the next two 32-row tiles stream from
-//             HBM straight into a 3-slot LDS ring (global_load_lds_dwordx4,
-//             16 bytes per lane, consecutive lanes fill consecutive LDS
-//             bytes, so a tile lands as 32 contiguous rows).  Each wave
-//             counts its own DMA instructions and waits with an explicit
-//             vmcnt for the oldest tile only; ring reads are inline ds_read
-//             instructions so no compiler-inserted wait serialises the ring.
-//   per tile
-//     decode  lane (row, kh, kg) reads 44 bytes of its row from the ring:
-//             32 B of nibbles, 4 scales, 8 rope bytes -- the 8 key
-//             dimensions per K-step of the 16x16x32 MFMA's A operand (key
-//             dimensions are assigned to lanes so each lane's bytes are
-//             contiguous; q uses the same assignment).  Latent FP16 values
-//             also go to an LDS V tile for the values.
-//     scores  S^T[16 rows x 32 heads] over this wave's 288 dimensions;
-//             the two dimension halves are summed through LDS, leaving wave
-//             (rb, kh) with the full scores of rows rb x heads kh.
-//     softmax online, FP32, base 2; running max shared through LDS.
-//     values  O[32 heads x 128 cols of wave w] += P . V with 32x32x16
-//             MFMA; V's B operand comes from LDS with ds_read_b64_tr_b16
-//             (each lane gets 4 consecutive rows of one column per read).
-//   epilogue  S == 1: normalise and store.  S > 1: store the normalised
-//             partial (O/l as FP16, log2-sum-exp as FP32); the split that
-//             finishes last for (t, g) (an atomic count) merges all S
-//             partials.  Nothing waits on another workgroup, so no
-//             co-residency is needed.
+//             boundaries balance valid rows).  Each wave loads q for all 32
+//             heads into registers in the score MFMA's B-operand layout.
+//   per tile  (16 rows, one wave)
+//     ring    global_load_lds_dwordx4 streams the tile's rows into one of
+//             the wave's LDS slots two tiles ahead; the wave waits for its
+//             oldest tile with an explicit vmcnt and reads the slot with
+//             inline ds_read (no compiler-inserted drain).
+//     decode  lane (row r = lane & 15, kg = lane >> 4) reads 88 bytes of row
+//             r (NVFP4): 64 B of nibbles, their 8 scales and 16 rope bytes --
+//             key dimensions [128kg, +128) of the latent and [512 + 16kg,
+//             +16) of the rope, i.e. the lane's 8 dimensions of each of the
+//             18 K-steps of a 16x16x32 MFMA A operand (q uses the same
+//             assignment).  The latent FP16 values also go to the V buffer.
+//     scores  S^T[16 rows x 32 heads]: 36 MFMAs (16x16x32, FP16 -> FP32).
+//     softmax base 2 against a lazily raised reference max: the reference
+//             moves only when a score exceeds it by more than 8 (one ballot
+//             decides), so P = 2^(s - ref) <= 256 stays accurate in FP16 and
+//             the common tile needs no cross-lane max and no O rescale.  Row
+//             sums accumulate per lane and are reduced once at the end.
+//     values  O[32 heads x 512 cols] += P . V: 16 MFMAs (32x32x16).  Each
+//             lane's P operand is 8 rows of one head: 4 of its own scores
+//             and 4 from lane ^ 16.  V's B operand comes from the V buffer
+//             through ds_read_b64_tr_b16.
+//   epilogue  the four streams are weighted by 2^(m_w - M) / L and summed
+//             through LDS; S == 1 stores the output, S > 1 stores the
+//             normalised partial (FP16) and its log2-sum-exp, and the split
+//             that finishes last for (t, g) merges all S partials.  Nothing
+//             waits on another workgroup, so no co-residency is needed.
 #include "mla_device.h"
 #include "mla_launch.h"
 
@@ -52,46 +56,44 @@ namespace mla {
 
 namespace {
 
-constexpr int kTile = 32;             // valid rows per tile
+constexpr int kRowsT = 16;            // rows per tile (one wave)
 constexpr int kHG = 32;               // heads per workgroup
-constexpr int kThreads = 256;
-constexpr int kVRow = kLatent + 16;   // FP16 elements per LDS row of V (row stride = 8 banks mod 64)
-constexpr int kPRow = kTile + 8;      // FP16 elements per LDS row of P
-constexpr int kKSteps = 9;            // 288 dimensions per wave / 32
-constexpr int kRing = 3;              // raw-tile slots in LDS
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kVRow = kLatent + 16;   // FP16 elements per V-buffer row (stride = 8 banks mod 64)
+constexpr int kKSteps = 18;           // 576 key dimensions / 32
+constexpr float kLazy = 8.0f;         // the reference max may trail the running max by up to 2^8
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 enum { kFmtNvfp4 = 0, kFmtFp8 = 1 };
 
-template <int kFmt>
-struct Fmt {
-  static constexpr int kRowB = kFmt == kFmtNvfp4 ? kRowBytes : kFp8RowBytes;
-  static constexpr int kPieces = kRowB / 16;          // 16-byte pieces per row
-  static constexpr int kChunks = kTile * kPieces;     // per tile
-  static constexpr int kInstr = kChunks / 64;         // DMA instructions per tile
-  static_assert(kChunks % 64 == 0, "a tile must be whole DMA instructions");
-  static constexpr int kSlotBytes = kChunks * 16;
-};
-
-constexpr int ring_slot_bytes(int fmt) {
-  return kTile * (fmt == kFmtNvfp4 ? kRowBytes : kFp8RowBytes);
-}
-
-typedef __fp16 fp16x4_ld __attribute__((__vector_size__(4 * sizeof(__fp16))));
+constexpr int row_bytes(int fmt) { return fmt == kFmtNvfp4 ? kRowBytes : kFp8RowBytes; }
+// DMA instructions per tile: 16 rows in 16-byte pieces, 64 pieces per instruction
+constexpr int dma_instr(int fmt) { return (kRowsT * row_bytes(fmt) / 16 + 63) / 64; }
+constexpr int slot_bytes(int fmt) { return dma_instr(fmt) * 1024; }
+// NVFP4: 3 slots (two tiles in flight while one is decoded); FP8 rows are
+// larger, so 2 slots and the refill is issued once a slot is in registers
+constexpr int ring_depth(int fmt) { return fmt == kFmtNvfp4 ? 3 : 2; }
+constexpr int kWaveRing = 18432;      // bytes of ring per wave (both formats)
+static_assert(ring_depth(kFmtNvfp4) * slot_bytes(kFmtNvfp4) <= kWaveRing, "NVFP4 ring");
+static_assert(ring_depth(kFmtFp8) * slot_bytes(kFmtFp8) <= kWaveRing, "FP8 ring");
+constexpr int kWaveV = kRowsT * kVRow;          // FP16 elements of V buffer per wave
+constexpr int kMergeHalves = kHG * kLatent;     // one stream's O in FP16
+static_assert(2 * kMergeHalves * 2 <= kWaves * kWaveRing, "merge buffers of streams 0,1");
+static_assert(2 * kMergeHalves <= kWaves * kWaveV, "merge buffers of streams 2,3");
 
 __device__ __forceinline__ uint32_t lds_off(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
 }
 
-// ds_read of ring bytes written by the DMA; the compiler does not see these
-// as LDS reads, so it adds no vmcnt wait for the DMA (the kernel waits
-// itself).  The results are valid after the lgkmcnt wait in ring_read.
-// (Inline assembly with AMDGPU register constraints exists only in the
-// device compilation pass; the host pass never runs device functions.)
-// The same holds for the LDS DMA builtin, whose presence in a kernel
-// template's body would otherwise keep the host pass from emitting the
-// kernel's launch stub.
+// Ring reads are inline ds_read instructions: the compiler does not see them
+// as LDS reads, so it adds no wait for the DMA (the kernel waits itself with
+// vmcnt); their results are valid after the lgkmcnt wait in ring_read.
+// Inline assembly with AMDGPU register constraints and the LDS DMA builtin
+// exist only in the device compilation pass (the host pass never runs
+// device code; the DMA builtin in a kernel template's body would also keep
+// the host pass from emitting the kernel's launch stub).
 #if defined(__HIP_DEVICE_COMPILE__)
 #define MLA_DEVICE_ASM(...) asm volatile(__VA_ARGS__)
 #define MLA_DMA16(src, lds) __builtin_amdgcn_global_load_lds((src), (lds), 16, 0, 0)
@@ -110,56 +112,58 @@ __device__ __forceinline__ u32x2 ring_b64(uint32_t a) {
   MLA_DEVICE_ASM("ds_read_b64 %0, %1" : "=v"(v) : "v"(a));
   return v;
 }
-__device__ __forceinline__ uint32_t ring_b32(uint32_t a) {
-  uint32_t v;
-  MLA_DEVICE_ASM("ds_read_b32 %0, %1" : "=v"(v) : "v"(a));
-  return v;
-}
 
-// Raw bytes one lane reads from its row: the key dimensions
-// [256kh + 64kg, +64) of the latent and [512 + 32kh + 8kg, +8) of the rope.
+// The bytes lane (row, kg) reads from its row.
 template <int kFmt>
 struct Raw;
 template <>
 struct Raw<kFmtNvfp4> {
-  u32x4 l0, l1;   // 32 bytes of nibbles = 64 codes
-  uint32_t sc;    // the 4 group scales of those codes
-  u32x2 rp;       // 8 rope bytes
+  u32x4 l[4];     // 64 bytes of nibbles: latent dimensions [128kg, +128)
+  u32x2 sc;       // their 8 group scales
+  u32x4 rp;       // rope dimensions [16kg, +16)
 };
 template <>
 struct Raw<kFmtFp8> {
-  u32x4 l0, l1, l2, l3;  // 64 latent bytes
-  u32x2 rp;              // 8 rope bytes
+  u32x4 l[8];     // 128 latent bytes
+  u32x4 rp;       // 16 rope bytes
 };
 
 template <int kFmt>
-__device__ __forceinline__ void ring_read(Raw<kFmt>& r, uint32_t row_base, int kh, int kg) {
+__device__ __forceinline__ void ring_read(Raw<kFmt>& r, uint32_t row_base, int kg) {
   if constexpr (kFmt == kFmtNvfp4) {
-    r.l0 = ring_b128(row_base + 128 * kh + 32 * kg);
-    r.l1 = ring_b128(row_base + 128 * kh + 32 * kg + 16);
-    r.sc = ring_b32(row_base + kScaleOff + 16 * kh + 4 * kg);
-    r.rp = ring_b64(row_base + kRopeOff + 32 * kh + 8 * kg);
-    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(r.l0), "+v"(r.l1), "+v"(r.sc), "+v"(r.rp));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.l[i] = ring_b128(row_base + 64 * kg + 16 * i);
+    r.sc = ring_b64(row_base + kScaleOff + 8 * kg);
+    r.rp = ring_b128(row_base + kRopeOff + 16 * kg);
+    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)"
+                   : "+v"(r.l[0]), "+v"(r.l[1]), "+v"(r.l[2]), "+v"(r.l[3]), "+v"(r.sc), "+v"(r.rp));
   } else {
-    r.l0 = ring_b128(row_base + 256 * kh + 64 * kg);
-    r.l1 = ring_b128(row_base + 256 * kh + 64 * kg + 16);
-    r.l2 = ring_b128(row_base + 256 * kh + 64 * kg + 32);
-    r.l3 = ring_b128(row_base + 256 * kh + 64 * kg + 48);
-    r.rp = ring_b64(row_base + kLatent + 32 * kh + 8 * kg);
-    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(r.l0), "+v"(r.l1), "+v"(r.l2), "+v"(r.l3), "+v"(r.rp));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.l[i] = ring_b128(row_base + 128 * kg + 16 * i);
+    r.rp = ring_b128(row_base + kLatent + 16 * kg);
+    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)"
+                   : "+v"(r.l[0]), "+v"(r.l[1]), "+v"(r.l[2]), "+v"(r.l[3]), "+v"(r.l[4]),
+                     "+v"(r.l[5]), "+v"(r.l[6]), "+v"(r.l[7]), "+v"(r.rp));
   }
 }
 
-// Latent K-step ks (0..7) of the lane's 64 dimensions, as FP16.
+// A operand of K-step ks: the lane's 8 key dimensions of its row, FP16.
 template <int kFmt>
-__device__ __forceinline__ half8_t latent8(const Raw<kFmt>& r, int ks) {
+__device__ __forceinline__ half8_t kstep8(const Raw<kFmt>& r, int ks) {
   if constexpr (kFmt == kFmtNvfp4) {
-    const uint32_t w = ks < 4 ? r.l0[ks] : r.l1[ks - 4];
-    return e2m1x8_to_half8_hw(w) * e4m3_splat8_hw(r.sc >> (8 * (ks >> 1)));
+    if (ks < 16) {
+      const uint32_t w = r.l[ks >> 2][ks & 3];
+      return e2m1x8_to_half8_hw(w) * e4m3_splat8_hw(r.sc[ks >> 3] >> (8 * ((ks >> 1) & 3)));
+    }
+    const int o = 2 * (ks - 16);
+    return e4m3x8_to_half8_hw(r.rp[o], r.rp[o + 1]);
   } else {
-    const u32x4& v = ks < 2 ? r.l0 : ks < 4 ? r.l1 : ks < 6 ? r.l2 : r.l3;
-    const int o = 2 * (ks & 1);
-    return e4m3x8_to_half8_hw(v[o], v[o + 1]);
+    if (ks < 16) {
+      const int o = 2 * (ks & 1);
+      return e4m3x8_to_half8_hw(r.l[ks >> 1][o], r.l[ks >> 1][o + 1]);
+    }
+    const int o = 2 * (ks - 16);
+    return e4m3x8_to_half8_hw(r.rp[o], r.rp[o + 1]);
   }
 }
 
@@ -179,6 +183,17 @@ __device__ __forceinline__ half8_t load_q8(const uint16_t* p) {
   }
 }
 
+// two adjacent output elements
+template <bool kBf16>
+__device__ __forceinline__ void store_out2(void* out, int64_t i, float a, float b) {
+  if constexpr (kBf16) {
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + i) =
+        (uint32_t)float_to_bf16_rne(a) | ((uint32_t)float_to_bf16_rne(b) << 16);
+  } else {
+    *reinterpret_cast<half2_t*>(reinterpret_cast<half_t*>(out) + i) = (half2_t){(half_t)a, (half_t)b};
+  }
+}
+
 template <bool kBf16>
 __device__ __forceinline__ void store_out(void* out, int64_t i, float v) {
   if constexpr (kBf16) reinterpret_cast<uint16_t*>(out)[i] = float_to_bf16_rne(v);
@@ -186,21 +201,37 @@ __device__ __forceinline__ void store_out(void* out, int64_t i, float v) {
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
-
-__device__ __forceinline__ half4_t ds_read_tr16(const half_t* p) {
-  fp16x4_ld v = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-      (__attribute__((address_space(3))) fp16x4_ld*)(p));
-  return __builtin_bit_cast(half4_t, v);
+__device__ __forceinline__ uint32_t shfl_xor_u(uint32_t v, int m) {
+  return (uint32_t)__shfl_xor((int)v, m, 64);
 }
 
-// Workgroup barrier for the tile loop.  Inside the loop waves exchange data
-// only through LDS (and the DMA, which each wave waits for itself), so the
-// barrier waits for this wave's LDS operations only.  __syncthreads() would
-// also wait for every outstanding global/DMA operation (vmcnt(0)) and drain
-// the ring.  The memory clobber keeps the compiler from moving memory
-// accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// B operands of 4 value MFMAs (4 consecutive 32-column blocks starting at
+// `base`) from the V buffer: ds_read_b64_tr_b16 gives each lane 4
+// consecutive rows of one column; two reads (rows 0-3 and 4-7 of the lane's
+// 8) make one operand.  In assembly so that the compiler does not make them
+// wait for the ring's DMA.
+__device__ __forceinline__ void read_v4(u32x4 (&b)[4], uint32_t base) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x2 lo, hi;
+    MLA_DEVICE_ASM("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(base), "i"(64 * i));
+    MLA_DEVICE_ASM("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(base), "i"(64 * i + 8 * kVRow));
+    b[i] = (u32x4){lo.x, lo.y, hi.x, hi.y};
+  }
+}
+
+// Column block held by accumulator block i (0..15) of wave w.  The blocks
+// are rotated per wave so that the stream merge (a reduce-scatter between
+// waves w, w^1 and then w, w^2) always keeps blocks 0..7 and then 0..3:
+// block i of w and block 8+i of w^1 are the same columns, and so are block
+// i < 4 of w and block 4+i of w^2.  Each group of 4 blocks (4Q..4Q+3) is 4
+// consecutive column blocks starting at this value for i = 4Q.
+__device__ __forceinline__ int col_block(int w, int i) {
+  return 8 * (((i >> 3) + (w & 1)) & 1) + (((i & 7) + 4 * (w >> 1)) & 7);
+}
+
+__device__ __forceinline__ void lgkm_wait(u32x4 (&b)[4]) {
+  MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
 }
 
 // s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
@@ -211,43 +242,56 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
+// x * a for an accumulator element that lives in an AGPR.  Written in C++
+// the multiply makes the compiler move all 256 accumulators through VGPRs
+// (and spill); in assembly the element is read, scaled and written back in
+// place.
+__device__ __forceinline__ float scale_acc(float x, float a) {
+  float tmp;
+  MLA_DEVICE_ASM("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(x), "=&v"(tmp) : "v"(a));
+  (void)tmp;
+  return x;
+}
+
+// head of accumulator element j of `lane` in the 32x32 MFMA C layout
+__device__ __forceinline__ int c_head(int j, int lane) { return (j >> 2) * 8 + 4 * (lane >> 5) + (j & 3); }
+
 }  // namespace
 
 template <int kFmt, bool kBf16>
-__global__ __launch_bounds__(kThreads, 2) void sparse_decode_kernel(DecodeParams p) {
-  using F = Fmt<kFmt>;
-  __shared__ __align__(16) uint8_t ring[kRing][ring_slot_bytes(kFmt)];   // raw tiles (DMA target)
-  static_assert(ring_slot_bytes(kFmt) == F::kSlotBytes, "ring slot size");
-  __shared__ __align__(16) half_t vt[kTile * kVRow];              // V tile, FP16, row-major
-  // The score halves exchanged between kh waves (written before barrier B,
-  // read before barrier C) and P (written after barrier C, read after
-  // barrier D, dead before the next tile's exchange) share one buffer.
-  __shared__ __align__(16) uint8_t xbuf[2 * 2 * 64 * sizeof(float4_t)];
-  float4_t(*sx)[2][64] = reinterpret_cast<float4_t(*)[2][64]>(xbuf);     // [rb][kh][lane]
-  half_t* pt = reinterpret_cast<half_t*>(xbuf);                           // P, [head][row]
-  static_assert(kHG * kPRow * sizeof(half_t) <= sizeof(xbuf), "P must fit the exchange buffer");
+__global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams p) {
+  constexpr int kRB = row_bytes(kFmt);
+  constexpr int kInstr = dma_instr(kFmt);
+  constexpr int kSlot = slot_bytes(kFmt);
+  constexpr int kDepth = ring_depth(kFmt);
+  constexpr int kPieces = kRowsT * (kRB / 16);  // 16-byte pieces per tile
+
+  // The DMA target and the V buffers are separate arrays so that the
+  // compiler can tell V-buffer accesses from DMA writes.  After the tile
+  // loop both hold the streams' weighted outputs for the merge.
+  __shared__ __align__(16) uint8_t ring_all[kWaves * kWaveRing];
+  __shared__ __align__(16) half_t vbuf_all[kWaves * kWaveV];
   __shared__ int phys[kMaxTopk];
-  __shared__ float red_max[4][16];
-  __shared__ float red_sum[4][16];
-  __shared__ float m_run[2][kHG];
-  __shared__ float alpha_s[kHG];
-  __shared__ float l_s[kHG];
-  __shared__ int chg_s[2];
-  __shared__ int cnt_s[8][4];
+  __shared__ float wm_s[kWaves][kHG];     // per-stream reference max (base 2)
+  __shared__ float wl_s[kWaves][kHG];     // per-stream row sums
+  __shared__ float alpha_s[kWaves][kHG];  // O rescale factors, then stream weights
+  __shared__ int cnt_s[8][kWaves];
   __shared__ int last_s;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int S = p.S, G = p.G;
   const int s = (int)(blockIdx.x % (unsigned)S);
   const int64_t tg = blockIdx.x / (unsigned)S;
   const int g = (int)(tg % G);
   const int64_t t = tg / G;
-  const int rb = wave & 1, kh = wave >> 1;
   const int r16 = lane & 15, kg = lane >> 4;
+  uint8_t* ring = ring_all + wave * kWaveRing;
+  half_t* vbuf = vbuf_all + wave * kWaveV;
 
   // ---------------------------------------------------------------- q
-  // B operand of K-step ks for head block hb: q[head][d(ks)] with
-  // d(ks < 8) = 256kh + 64kg + 8ks + [0,8) and d(8) = 512 + 32kh + 8kg + [0,8)
+  // B operand of K-step ks for head block hb: q[head][d] with
+  // d(ks < 16) = 128kg + 8ks + [0,8) and d(16 + i) = 512 + 16kg + 8i + [0,8)
   half8_t qreg[2][kKSteps];
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
@@ -255,47 +299,57 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_decode_kernel(DecodeParams
     if (head < p.H) {
       const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + t * p.q_st + (int64_t)head * p.q_sh;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) qreg[hb][ks] = load_q8<kBf16>(qp + 256 * kh + 64 * kg + 8 * ks);
-      qreg[hb][8] = load_q8<kBf16>(qp + kLatent + 32 * kh + 8 * kg);
+      for (int ks = 0; ks < 16; ++ks) qreg[hb][ks] = load_q8<kBf16>(qp + 128 * kg + 8 * ks);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) qreg[hb][16 + i] = load_q8<kBf16>(qp + kLatent + 16 * kg + 8 * i);
     } else {
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) qreg[hb][ks] = (half8_t){0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
-  if (tid < kHG) {
-    m_run[0][tid] = kNegInf;
-    l_s[tid] = 0.0f;
-  }
 
   // ------------------------------------------------ compact the valid rows
+  // All index loads are issued before any is used, then all block-table
+  // loads: two dependent memory round trips (addresses of slots past topk
+  // or of masked entries are clamped to valid ones and the result dropped).
   int rows8[8], pre8[8];
   {
     const int32_t* ip = p.idx + t * p.idx_st;
-    const int64_t seq = p.bt ? (int64_t)p.tok_seq[t] : 0;
-    const bool seq_ok = !p.bt || (seq >= 0 && seq < p.bt_rows);
+    int v8[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int slot = i * kThreads + tid;
-      int r = -1;
-      if (slot < p.topk) {
-        const int v = ip[slot];
-        if (v >= 0 && seq_ok) {
-          if (p.bt) {
-            const int b = v / p.bs;
-            if (b < p.bt_cols) {
-              const int pb = p.bt[seq * p.bt_st + b];
-              if (pb >= 0) {
-                const int64_t pr = (int64_t)pb * p.bs + (v - b * p.bs);
-                r = pr < p.cache_rows ? (int)pr : -1;
-              }
-            }
-          } else {
-            r = v < p.cache_rows ? v : -1;
-          }
-        }
+      v8[i] = ip[slot < p.topk ? slot : p.topk - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i * kThreads + tid >= p.topk) v8[i] = -1;
+    if (p.bt) {
+      const int64_t seq = p.tok_seq[t];
+      const bool seq_ok = seq >= 0 && seq < p.bt_rows;
+      const int32_t* btr = p.bt + (seq_ok ? seq : 0) * p.bt_st;
+      int b8[8], pb8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        b8[i] = v8[i] >= 0 ? v8[i] / p.bs : 0;
+        pb8[i] = btr[b8[i] < p.bt_cols ? b8[i] : p.bt_cols - 1];
       }
-      rows8[i] = r;
-      const uint64_t m = __ballot(r >= 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int r = -1;
+        if (seq_ok && v8[i] >= 0 && b8[i] < p.bt_cols && pb8[i] >= 0) {
+          const int64_t pr = (int64_t)pb8[i] * p.bs + (v8[i] - b8[i] * p.bs);
+          r = pr < p.cache_rows ? (int)pr : -1;
+        }
+        rows8[i] = r;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rows8[i] = (v8[i] >= 0 && v8[i] < p.cache_rows) ? v8[i] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint64_t m = __ballot(rows8[i] >= 0);
       pre8[i] = __popcll(m & ((1ull << lane) - 1ull));
       if (lane == 0) cnt_s[i][wave] = __popcll(m);
     }
@@ -308,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_decode_kernel(DecodeParams
     for (int i = 0; i < 8; ++i) {
       base[i] = total;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < kWaves; ++w) {
         if (w < wave) base[i] += cnt_s[i][w];
         total += cnt_s[i][w];
       }
@@ -321,196 +375,280 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_decode_kernel(DecodeParams
 
   const int r0 = (int)((int64_t)total * s / S);
   const int n = (int)((int64_t)total * (s + 1) / S) - r0;
-  const int ntiles = (n + kTile - 1) / kTile;
+  const int ntiles = (n + kRowsT - 1) / kRowsT;
+  const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
 
-  float16_t acc_o[4];
+  // ---------------------------------------------------------------- stream state
+  float16_t acc_o[16];                    // O[32 heads x 32 cols] of column block col_block(wave, i), C layout
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+  for (int nb = 0; nb < 16; ++nb)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc_o[nb][j] = 0.0f;
+  // byte offset in a V-buffer row of accumulator blocks 4q..4q+3
+  uint32_t vq[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) vq[q] = 64 * col_block(wave, 4 * q);
+  float mref[2] = {kNegInf, kNegInf};     // reference max of head hb*16 + r16 (base 2)
+  float lsum[2] = {0.0f, 0.0f};           // this lane's share of that head's row sum
 
-  // ------------------------------------------------ raw ring (DMA)
-  // Wave w issues the tile's DMA instructions w, w+4, w+8, ...: `mine` of them.
-  constexpr int kMineHi = (F::kInstr + 3) / 4;
-  const int mine = (F::kInstr + 3 - wave) / 4;
-  // Issue tile `it` into ring slot `slot`: row indices past the split are
-  // clamped to its last row (a real row; those slots are never used).
-  auto issue = [&](int it, int slot) {
+  // DMA of this wave's k-th tile (split tile wave + 4k) into ring slot
+  // `slot`: instruction j moves pieces 64j + lane (piece = row * kRB/16 +
+  // 16-byte column), landing at slot + 16 * piece, so rows sit kRB apart.
+  // Pieces past the tile (padding of the last instruction) re-load piece 0
+  // into the slot's padding; rows past the split re-load the split's last
+  // row.  Both are real rows and are never used.
+  auto issue = [&](int k, int slot) {
+    const int tile = wave + kWaves * k;
 #pragma unroll
-    for (int j = 0; j < kMineHi; ++j) {
-      if (j < mine) {
-        const int c = 64 * (wave + 4 * j) + lane;            // chunk = row * pieces + piece
-        const int row = c / F::kPieces, piece = c - row * F::kPieces;
-        int i = it * kTile + row;
-        i = i < n ? i : n - 1;
-        const uint8_t* src = p.cache + (int64_t)phys[r0 + i] * F::kRowB + 16 * piece;
-        MLA_DMA16(src, &ring[slot][1024 * (wave + 4 * j)]);
-      }
-    }
-  };
-  // wait until this wave's DMA of the oldest of the three tiles in flight is done
-  auto wait_oldest = [&]() {
-    if (mine == kMineHi) wait_vmcnt<2 * kMineHi>();
-    else wait_vmcnt<2 * (kMineHi - 1)>();
-  };
-
-  auto process = [&](int it) {
-    const int slot = it % kRing;
-    // ---- decode each K-step's operand just before its two MFMAs (partial
-    // scores over this wave's 288 dimensions, both head blocks); the latent
-    // also goes to LDS as FP16 for the values
-    Raw<kFmt> raw;
-    ring_read<kFmt>(raw, lds_off(&ring[slot][(16 * rb + r16) * F::kRowB]), kh, kg);
-    half_t* vrow = vt + (16 * rb + r16) * kVRow + 256 * kh + 64 * kg;
-    float4_t acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      half8_t kop;
-      if (ks < 8) {
-        kop = latent8<kFmt>(raw, ks);
-        *reinterpret_cast<half8_t*>(vrow + 8 * ks) = kop;
-      } else {
-        kop = e4m3x8_to_half8_hw(raw.rp.x, raw.rp.y);
-      }
-      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qreg[0][ks], acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qreg[1][ks], acc[1], 0, 0, 0);
-    }
-    sx[rb][kh][lane] = kh ? acc[0] : acc[1];   // the partner's head block
-    lds_barrier();
-    const float4_t part = sx[rb][kh ^ 1][lane];
-    const float4_t sc = (kh ? acc[1] : acc[0]) + part;
-
-    // ---- scores of rows (rb) x heads (hb = kh): mask, scale, tile max
-    float sv[4];
-    float mx = kNegInf;
-    const int row0 = it * kTile + 16 * rb + 4 * kg;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sv[j] = (row0 + j < n) ? sc[j] * p.sm_log2 : kNegInf;
-      mx = __builtin_fmaxf(mx, sv[j]);
-    }
-    mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 32));
-    if (lane < 16) red_max[wave][lane] = mx;
-    lds_barrier();
-    {
-      const int hl = kh * 16 + r16;
-      const float m_old = m_run[it & 1][hl];
-      const float tmax = __builtin_fmaxf(red_max[2 * kh][r16], red_max[2 * kh + 1][r16]);
-      const float m_new = __builtin_fmaxf(m_old, tmax);
-      float pj[4], psum = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pj[j] = __builtin_amdgcn_exp2f(sv[j] - m_new);
-        psum += pj[j];
-      }
-      psum += shfl_xor_f(psum, 16);
-      psum += shfl_xor_f(psum, 32);
-      if (lane < 16) red_sum[wave][lane] = psum;
-      *reinterpret_cast<half4_t*>(pt + hl * kPRow + 16 * rb + 4 * kg) =
-          (half4_t){(half_t)pj[0], (half_t)pj[1], (half_t)pj[2], (half_t)pj[3]};
-      if (rb == 0) {
-        const bool changed = lane < 16 && m_new > m_old;
-        const uint64_t any = __ballot(changed);
-        if (lane < 16) {
-          m_run[(it + 1) & 1][hl] = m_new;
-          alpha_s[hl] = __builtin_amdgcn_exp2f(m_old - m_new);
-        }
-        if (lane == 0) chg_s[kh] = any != 0;
-      }
-    }
-    lds_barrier();
-
-    // ---- values: O[32 heads x 128 cols of this wave] += P . V
-    if (tid < kHG)
-      l_s[tid] = l_s[tid] * alpha_s[tid] + red_sum[2 * (tid >> 4)][tid & 15] +
-                 red_sum[2 * (tid >> 4) + 1][tid & 15];
-    if ((chg_s[0] | chg_s[1]) != 0) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float al = alpha_s[(j >> 2) * 8 + 4 * (lane >> 5) + (j & 3)];
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc_o[nb][j] *= al;
-      }
-    }
-    {
-      const int grp = lane >> 4, sl = lane & 15;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const half8_t a =
-            *reinterpret_cast<const half8_t*>(pt + (lane & 31) * kPRow + 16 * ks + 8 * (lane >> 5));
-        const int vr = 16 * ks + 8 * (grp >> 1) + (sl >> 2);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const half_t* vp = vt + vr * kVRow + 128 * wave + 32 * nb + 16 * (grp & 1) + 4 * (sl & 3);
-          const half4_t lo = ds_read_tr16(vp);
-          const half4_t hi = ds_read_tr16(vp + 4 * kVRow);
-          const half8_t b = (half8_t){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          acc_o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc_o[nb], 0, 0, 0);
-        }
-      }
+    for (int j = 0; j < kInstr; ++j) {
+      int c = 64 * j + lane;
+      c = c < kPieces ? c : 0;
+      const int row = c / (kRB / 16), piece = c - row * (kRB / 16);
+      int i = tile * kRowsT + row;
+      i = i < n ? i : n - 1;
+      const uint8_t* src = p.cache + (int64_t)phys[r0 + i] * kRB + 16 * piece;
+      MLA_DMA16(src, ring + slot * kSlot + 1024 * j);
     }
   };
 
-  // ------------------------------------------------ tiles, 2 ahead in flight
-  if (ntiles > 0) {
+  const float sm = p.sm_log2;
+  if (my_tiles > 0) {
     issue(0, 0);
-    issue(1, 1);
-    for (int it = 0; it < ntiles; ++it) {
-      // slot (it+2)%3 last held tile it-1, whose reads all precede the
-      // barriers of tile it-1
-      issue(it + 2, (it + 2) % kRing);
-      wait_oldest();
-      lds_barrier();   // tile `it` complete in LDS for every wave; V tile free
-      process(it);
+    if (my_tiles > 1) issue(1, 1);
+    for (int k = 0; k < my_tiles; ++k) {
+      const int slot = k % kDepth;
+      // wait until only this wave's later tiles are in flight
+      if constexpr (kDepth == 3) {
+        if (k + 2 < my_tiles) {
+          issue(k + 2, (k + 2) % 3);   // that slot held tile k - 1, already in registers
+          wait_vmcnt<2 * kInstr>();
+        } else if (k + 1 < my_tiles) {
+          wait_vmcnt<kInstr>();
+        } else {
+          wait_vmcnt<0>();
+        }
+      } else {
+        if (k + 1 < my_tiles) wait_vmcnt<kInstr>();
+        else wait_vmcnt<0>();
+      }
+      const int tile = wave + kWaves * k;
+
+      // ---- decode + scores: S^T[16 rows x 32 heads]
+      Raw<kFmt> raw;
+      ring_read<kFmt>(raw, lds_off(ring + slot * kSlot + r16 * kRB), kg);
+      if constexpr (kDepth == 2) {
+        if (k + 2 < my_tiles) issue(k + 2, slot);   // the slot's bytes are in registers
+      }
+      half_t* vrow = vbuf + r16 * kVRow + 128 * kg;
+      float4_t sacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        const half8_t kop = kstep8<kFmt>(raw, ks);
+        if (ks < 16) *reinterpret_cast<half8_t*>(vrow + 8 * ks) = kop;
+        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qreg[0][ks], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qreg[1][ks], sacc[1], 0, 0, 0);
+      }
+
+      // ---- softmax, base 2.  The lane holds rows 4kg + j (j = 0..3) of
+      // head hb*16 + r16.
+      const int row0 = tile * kRowsT + 4 * kg;
+      float sv[2][4], tmax[2];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        tmax[hb] = kNegInf;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sv[hb][j] = (row0 + j < n) ? sacc[hb][j] * sm : kNegInf;
+          tmax[hb] = __builtin_fmaxf(tmax[hb], sv[hb][j]);
+        }
+      }
+      const bool raise = tmax[0] > mref[0] + kLazy || tmax[1] > mref[1] + kLazy;
+      if (__ballot(raise) != 0) {
+        // reference := running max for every head; rescale O and the sums
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          float m = tmax[hb];
+          m = __builtin_fmaxf(m, shfl_xor_f(m, 16));
+          m = __builtin_fmaxf(m, shfl_xor_f(m, 32));
+          const float mnew = __builtin_fmaxf(mref[hb], m);
+          const float al = mref[hb] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mref[hb] - mnew);
+          lsum[hb] *= al;
+          mref[hb] = mnew;
+          if (kg == 0) alpha_s[wave][hb * 16 + r16] = al;
+        }
+        // written and read by this wave only: LDS keeps a wave's order
+        MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float al = alpha_s[wave][c_head(j, lane)];
+#pragma unroll
+          for (int nb = 0; nb < 16; ++nb) acc_o[nb][j] = scale_acc(acc_o[nb][j], al);
+        }
+      }
+      half_t ph[2][4];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float pv = __builtin_amdgcn_exp2f(sv[hb][j] - mref[hb]);
+          lsum[hb] += pv;
+          ph[hb][j] = (half_t)pv;
+        }
+      }
+      // A operand of the value MFMA: lane L = head (L & 31) x rows
+      // 8(L >> 5) + [0,8).  Lane (r16, kg) holds rows 4kg..4kg+3 of heads
+      // r16 and 16 + r16; it keeps the head block kg & 1 and swaps the other
+      // with lane ^ 16, which holds the neighbouring 4 rows.
+      const int keep = kg & 1;
+      const half4_t mine = keep ? (half4_t){ph[1][0], ph[1][1], ph[1][2], ph[1][3]}
+                                : (half4_t){ph[0][0], ph[0][1], ph[0][2], ph[0][3]};
+      const half4_t give = keep ? (half4_t){ph[0][0], ph[0][1], ph[0][2], ph[0][3]}
+                                : (half4_t){ph[1][0], ph[1][1], ph[1][2], ph[1][3]};
+      const u32x2 gv = __builtin_bit_cast(u32x2, give);
+      const u32x2 rv = {shfl_xor_u(gv.x, 16), shfl_xor_u(gv.y, 16)};
+      const half4_t other = __builtin_bit_cast(half4_t, rv);
+      const half8_t pa = keep ? (half8_t){other.x, other.y, other.z, other.w, mine.x, mine.y, mine.z, mine.w}
+                              : (half8_t){mine.x, mine.y, mine.z, mine.w, other.x, other.y, other.z, other.w};
+
+      // ---- values: O += P . V, V read in groups of 4 column blocks, the
+      // next group's reads in flight while this group's MFMAs run
+      MLA_DEVICE_ASM("" ::: "memory");   // the V-buffer writes stay above the reads
+      {
+        const int grp = lane >> 4, sl = lane & 15;
+        const uint32_t vb = lds_off(vbuf + (8 * (grp >> 1) + (sl >> 2)) * kVRow + 16 * (grp & 1) + 4 * (sl & 3));
+        u32x4 bv[2][4];
+        read_v4(bv[0], vb + vq[0]);
+        lgkm_wait(bv[0]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (q < 3) read_v4(bv[(q + 1) & 1], vb + vq[q + 1]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc_o[4 * q + i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                pa, __builtin_bit_cast(half8_t, bv[q & 1][i]), acc_o[4 * q + i], 0, 0, 0);
+          if (q < 3) lgkm_wait(bv[(q + 1) & 1]);
+        }
+      }
+      MLA_DEVICE_ASM("" ::: "memory");   // next tile's V-buffer writes stay below
     }
   }
-  wait_vmcnt<0>();       // no DMA may still be writing this workgroup's LDS at exit
-  __syncthreads();
+  wait_vmcnt<0>();   // no DMA may still be writing this workgroup's LDS
 
-  // ---------------------------------------------------------------- epilogue
+  // ---------------------------------------------------------------- merge the streams
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    lsum[hb] += shfl_xor_f(lsum[hb], 16);
+    lsum[hb] += shfl_xor_f(lsum[hb], 32);
+  }
+  if (kg == 0) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      wm_s[wave][hb * 16 + r16] = mref[hb];
+      wl_s[wave][hb * 16 + r16] = lsum[hb];
+    }
+  }
+  __syncthreads();   // every stream's state is visible and the rings are idle
+  // weight of stream w for head hd: 2^(m_w - M) / L with
+  // M = max_w m_w and L = sum_w 2^(m_w - M) l_w; log2-sum-exp = M + log2 L
+  if (tid < kWaves * kHG) {
+    const int w = tid >> 5, hd = tid & 31;
+    float M = kNegInf;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) M = __builtin_fmaxf(M, wm_s[v][hd]);
+    float L = 0.0f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v)
+        L += wm_s[v][hd] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(wm_s[v][hd] - M) * wl_s[v][hd];
+    }
+    const float mw = wm_s[w][hd];
+    alpha_s[w][hd] = (L > 0.0f && mw != kNegInf) ? __builtin_amdgcn_exp2f(mw - M) / L : 0.0f;
+    if (w == 0) {
+      const float lse2 = L > 0.0f ? M + __log2f(L) : kNegInf;
+      const int head = g * kHG + hd;
+      if (S > 1) p.part_lse[(tg * S + s) * kHG + hd] = lse2;
+      else if (head < p.H && p.lse) p.lse[t * p.H + head] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
+    }
+  }
+  __syncthreads();
+  // Reduce-scatter of the weighted streams in FP32 through LDS, in the MFMA
+  // C layout (lane-contiguous 16-byte pieces: no bank conflicts).  Round 1:
+  // waves w and w^1 swap blocks 8..15 and keep the sums of 0..7; round 2:
+  // waves w and w^2 swap blocks 4..7 and keep 0..3.  Exchange buffers: waves
+  // 0,1 in the ring area, 2,3 in the V area (32 KB each, the rings are idle).
+  auto xbuf = [&](int w) -> float4_t* {
+    return w < 2 ? reinterpret_cast<float4_t*>(ring_all) + w * 2048
+                 : reinterpret_cast<float4_t*>(vbuf_all) + (w - 2) * 2048;
+  };
+  float cw[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) cw[j] = alpha_s[wave][c_head(j, lane)];
+  {
+    float4_t* mine = xbuf(wave);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4)
+        mine[(i * 4 + j4) * 64 + lane] =
+            (float4_t){acc_o[8 + i][4 * j4] * cw[4 * j4], acc_o[8 + i][4 * j4 + 1] * cw[4 * j4 + 1],
+                       acc_o[8 + i][4 * j4 + 2] * cw[4 * j4 + 2], acc_o[8 + i][4 * j4 + 3] * cw[4 * j4 + 3]};
+  }
+  __syncthreads();
+  float res[8][16];
+  {
+    const float4_t* other = xbuf(wave ^ 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const float4_t v = other[(i * 4 + j4) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) res[i][4 * j4 + e] = acc_o[i][4 * j4 + e] * cw[4 * j4 + e] + v[e];
+      }
+  }
+  __syncthreads();   // wave ^ 1 has read this wave's buffer
+  {
+    float4_t* mine = xbuf(wave);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4)
+        mine[(i * 4 + j4) * 64 + lane] = (float4_t){res[4 + i][4 * j4], res[4 + i][4 * j4 + 1],
+                                                    res[4 + i][4 * j4 + 2], res[4 + i][4 * j4 + 3]};
+  }
+  __syncthreads();
+  {
+    const float4_t* other = xbuf(wave ^ 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const float4_t v = other[(i * 4 + j4) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) res[i][4 * j4 + e] += v[e];
+      }
+  }
+
+  // this wave now holds the full result for column blocks col_block(wave, 0..3)
   const float out_mul = p.kv_scale;  // FP8 rows: values carry kv_scale
   const int64_t H = p.H;
-  if (S == 1) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int hd = (j >> 2) * 8 + 4 * (lane >> 5) + (j & 3);
-      const int head = g * kHG + hd;
-      if (head >= p.H) continue;
-      const float l = l_s[hd];
-      const float inv = l > 0.0f ? out_mul / l : 0.0f;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int col = 128 * wave + 32 * nb + (lane & 31);
-        store_out<kBf16>(p.out, (t * H + head) * kLatent + col, acc_o[nb][j] * inv);
-      }
-      if (wave == 0 && (lane & 31) == 0 && p.lse) {
-        const float m = m_run[ntiles & 1][hd];
-        p.lse[t * H + head] = l > 0.0f ? (m + __log2f(l)) * kLn2 : kNegInf;
-      }
-    }
-    return;
-  }
-
-  // partial of this split: normalised O (FP16) and log2-sum-exp (FP32)
   {
-    half_t* po = p.part_o + ((tg * S + s) * kHG) * kLatent;
+    const int col0 = 32 * col_block(wave, 0) + (lane & 31);
+    half_t* po = S > 1 ? p.part_o + ((tg * S + s) * kHG) * kLatent : nullptr;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int hd = (j >> 2) * 8 + 4 * (lane >> 5) + (j & 3);
-      const float l = l_s[hd];
-      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      const int hd = c_head(j, lane);
+      const int head = g * kHG + hd;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int col = 128 * wave + 32 * nb + (lane & 31);
-        po[hd * kLatent + col] = (half_t)(acc_o[nb][j] * inv);
-      }
-      if (wave == 0 && (lane & 31) == 0) {
-        const float m = m_run[ntiles & 1][hd];
-        p.part_lse[(tg * S + s) * kHG + hd] = l > 0.0f ? m + __log2f(l) : kNegInf;
+      for (int i = 0; i < 4; ++i) {
+        const int col = col0 + 32 * i;
+        if (S > 1) po[hd * kLatent + col] = (half_t)res[i][j];
+        else if (head < p.H) store_out<kBf16>(p.out, (t * H + head) * kLatent + col, res[i][j] * out_mul);
       }
     }
   }
+  if (S == 1) return;
+
   // publish the partial (one release after the barrier has ordered every
   // wave's stores before it) and count arrivals; the last arrival merges
   __syncthreads();
@@ -528,8 +666,8 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_decode_kernel(DecodeParams
   __syncthreads();
   if (!last_s) return;
 
-  // merge weights per (split, head), in the V tile's LDS
-  float* wsh = reinterpret_cast<float*>(vt);
+  // merge weights per (split, head)
+  float* wsh = reinterpret_cast<float*>(ring_all);
   if (tid < kHG) {
     const float* pl = p.part_lse + tg * S * kHG + tid;
     float mx = kNegInf;
@@ -545,7 +683,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_decode_kernel(DecodeParams
   __syncthreads();
   {
     // 8 consecutive columns per work item: 32 heads x 64 chunks
-    const half_t* po = p.part_o + (tg * S) * kHG * kLatent;
+    const half_t* pp = p.part_o + (tg * S) * kHG * kLatent;
     for (int e = tid; e < kHG * (kLatent / 8); e += kThreads) {
       const int hd = e >> 6, c8 = 8 * (e & 63);
       const int head = g * kHG + hd;
@@ -553,12 +691,13 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_decode_kernel(DecodeParams
       float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int ss = 0; ss < S; ++ss) {
         const float w = wsh[ss * kHG + hd];
-        const half8_t v = *reinterpret_cast<const half8_t*>(po + (ss * kHG + hd) * kLatent + c8);
+        const half8_t v = *reinterpret_cast<const half8_t*>(pp + (ss * kHG + hd) * kLatent + c8);
 #pragma unroll
         for (int i = 0; i < 8; ++i) a[i] += w * (float)v[i];
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) store_out<kBf16>(p.out, (t * H + head) * kLatent + c8 + i, a[i] * out_mul);
+      for (int i = 0; i < 8; i += 2)
+        store_out2<kBf16>(p.out, (t * H + head) * kLatent + c8 + i, a[i] * out_mul, a[i + 1] * out_mul);
     }
   }
 }
@@ -586,11 +725,12 @@ int decode_auto_splits(int64_t T, int H, int topk) {
   const int64_t groups = T * G;
   if (groups <= 0) return 1;
   const int cus = device_cus() > 0 ? device_cus() : 256;
-  // two workgroups per CU is the target; a split keeps at least 256 valid
-  // rows (8 tiles) so its fixed costs (index compaction, q load, merge
-  // share) stay small next to its streaming work
-  int64_t s = (2 * cus + groups - 1) / groups;
-  int64_t max_by_rows = topk / 256;
+  // One workgroup per CU is resident at a time: fill the CUs once (more
+  // splits than that would start a second, mostly idle round).  A split
+  // keeps at least 128 valid rows (two tiles per stream) so its fixed
+  // costs (index compaction, q load, stream and split merges) stay small.
+  int64_t s = cus / groups;
+  int64_t max_by_rows = topk / 128;
   if (max_by_rows < 1) max_by_rows = 1;
   if (s > max_by_rows) s = max_by_rows;
   if (s > 64) s = 64;

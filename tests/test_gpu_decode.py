@@ -82,7 +82,12 @@ def test_split_count_invariance(splits):
     ref_out, ref_lse = _run(w, cache, num_splits=1)
     out, lse = _run(w, cache, num_splits=splits)
     _check(w, cache, out, lse, what=f"splits{splits}")
-    assert torch.allclose(out.float(), ref_out.float(), atol=2e-3, rtol=2e-3)
+    # Splitting changes only where FP16 partials are rounded, so the outputs
+    # agree to a small fraction of each token's largest output (the parity
+    # bar's metric, 5x tighter).
+    diff = (out.float() - ref_out.float()).abs().amax(dim=(1, 2))
+    scale = ref_out.float().abs().amax(dim=(1, 2))
+    assert torch.all(diff <= 2e-3 * scale), (diff / scale.clamp_min(1e-30)).tolist()
     fin = torch.isfinite(ref_lse)
     assert torch.equal(fin, torch.isfinite(lse))
     assert torch.allclose(lse[fin], ref_lse[fin], atol=1e-4)
