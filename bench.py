@@ -12,8 +12,12 @@ distinct picks from each sequence's 146,000 rows, 2.2M-row NVFP4 pool.
 Timing: W untimed warm-up steps, then K timed steps.  By default the caches
 are cold for every step: a 1 GiB read sweep runs between steps (outside the
 per-step events) so neither the 256 MB Infinity Cache nor L2 holds the
-gathered rows.  Every launch is bracketed by HIP events on the stream the
-kernels run on.  Prints one JSON line.
+gathered rows.  Every step is bracketed by HIP events on the stream the
+kernels run on; `value` and `us_per_step` come from that pass.  A second
+pass repeats the steps with the library's kernel timing on
+(hipExtLaunchKernel events at each kernel's own start and end): those
+durations give `decode_kernel_us`, the roofline figure and the comparators'
+`*_kernel_us`.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--warm] [--no-comparators] [--no-cpu-baseline]
@@ -138,6 +142,7 @@ def _gpu_run(args):
         do_flush()
         step()
     torch.cuda.synchronize()
+    # pass A, the timed region: K steps, each bracketed by HIP events, no instrumentation
     tm = Timer(torch, args.steps)
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -145,6 +150,21 @@ def _gpu_run(args):
         step(tm, i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # pass B: the same steps with the library's kernel timing on (each kernel's own
+    # start/end events), for the roofline and the per-kernel figures
+    kern_ms, app_kern_ms = [], []
+    mla.kernel_timing(True)
+    try:
+        for i in range(max(20, args.steps // 2)):
+            do_flush()
+            mla.quantize_append(app_lat, app_rope, app_slots, cache)
+            app_kern_ms.append(mla.last_kernel_ms())
+            mla.sparse_decode(w.q, cache, w.indices, w.sm_scale, block_table=w.block_table,
+                              token_seq=w.token_seq, block_size=w.block_size, workspace=ws,
+                              num_splits=splits, out=out, lse=lse)
+            kern_ms.append(mla.last_kernel_ms())
+    finally:
+        mla.kernel_timing(False)
     step_ms = tm.spans(0, 2)
     dec_ms = tm.spans(1, 2)
     app_ms = tm.spans(0, 1)
@@ -155,6 +175,8 @@ def _gpu_run(args):
         "decode_ms_p10": sorted(dec_ms)[len(dec_ms) // 10],
         "decode_ms_p90": sorted(dec_ms)[(9 * len(dec_ms)) // 10],
         "append_ms": statistics.mean(app_ms), "wall_ms_per_iter": 1e3 * wall / args.steps,
+        "kernel_ms": statistics.mean(kern_ms), "kernel_ms_median": statistics.median(kern_ms),
+        "append_kernel_ms": statistics.mean(app_kern_ms),
     }
 
     if not args.no_comparators:
@@ -210,6 +232,27 @@ def _comparators(args, torch, mla, w, cache, dev, splits, do_flush):
     r["staged_total_us"] = 1e3 * statistics.mean(tm.spans(0, 2))
     r["staged_gather_dequant_us"] = 1e3 * statistics.mean(tm.spans(0, 1))
     r["staged_fp8_decode_us"] = 1e3 * statistics.mean(tm.spans(1, 2))
+    # the same launches with kernel timing on: each kernel's own duration
+    k_fp8, k_gather, k_sfp8 = [], [], []
+    mla.kernel_timing(True)
+    try:
+        for i in range(n):
+            do_flush()
+            fp8_decode()
+            k_fp8.append(mla.last_kernel_ms())
+            do_flush()
+            mla.gather_dequant_fp8(cache, w.indices, 1.0, block_table=w.block_table, token_seq=w.token_seq,
+                                   block_size=w.block_size, rows=staged_rows, staged_indices=staged_idx)
+            k_gather.append(mla.last_kernel_ms())
+            mla.sparse_decode(w.q, staged_rows, staged_idx, w.sm_scale, fmt="fp8", workspace=ws,
+                              num_splits=splits, out=out, lse=lse)
+            k_sfp8.append(mla.last_kernel_ms())
+    finally:
+        mla.kernel_timing(False)
+    r["fp8_576_decode_kernel_us"] = 1e3 * statistics.mean(k_fp8)
+    r["staged_gather_dequant_kernel_us"] = 1e3 * statistics.mean(k_gather)
+    r["staged_fp8_decode_kernel_us"] = 1e3 * statistics.mean(k_sfp8)
+    r["staged_total_kernel_us"] = r["staged_gather_dequant_kernel_us"] + r["staged_fp8_decode_kernel_us"]
     return r
 
 
@@ -264,6 +307,40 @@ def _cpu_baseline(w, seconds):
     }
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_decode_nvfp4_hbm_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "nvfp4_compressed_sparse_mla_amd", "csrc", f)
+                  for f in ("decode.hip", "mla_device.h", "mla_launch.h")]
+
+
+def _kernel_sources_sha256() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _traffic(workload: str, splits: int):
+    """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, only if it was taken on the current kernel sources
+    and the same workload and split count; otherwise None."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    sha = next((l.split()[1] for l in lines if l.startswith("kernel_sources_sha256 ")), None)
+    if sha != _kernel_sources_sha256():
+        return None
+    for l in lines:
+        f = l.split()
+        if len(f) == 5 and f[0] == "traffic" and f[1] == workload and f[2] == f"splits={splits}":
+            r, wr = int(f[3].split("=")[1]), int(f[4].split("=")[1])
+            return {"read": r, "write": wr, "total": r + wr}
+    return None
+
+
 def main():
     args = _parse()
     if args.calibrate_copy:
@@ -276,8 +353,10 @@ def main():
                                    "figure is produced", "n_gpus": args.gpus}))
         sys.exit(2)
     res, w = _gpu_run(args)
-    dec_s = res["decode_ms"] * 1e-3
-    achieved = res["gathered"] / dec_s / 1e9
+    # roofline: algorithmic bytes of one launch over the kernel's own duration
+    # (HIP events recorded at kernel start and end by hipExtLaunchKernel)
+    achieved = res["gathered"] / (res["kernel_ms"] * 1e-3) / 1e9
+    traffic = None if (args.splits or args.warm) else _traffic(args.workload, res["splits"])
     line = {
         "metric": METRIC,
         "value": round(res["gathered"] / (res["step_ms"] * 1e-3) / 1e9, 2),
@@ -287,10 +366,13 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(res["step_ms"], 5),
         "us_per_step": round(1e3 * res["step_ms"], 3),
+        "decode_kernel_us": round(1e3 * res["kernel_ms"], 3),
+        "decode_kernel_us_median": round(1e3 * res["kernel_ms_median"], 3),
         "decode_us": round(1e3 * res["decode_ms"], 3),
         "decode_us_median": round(1e3 * res["decode_ms_median"], 3),
         "decode_us_p10_p90": [round(1e3 * res["decode_ms_p10"], 3), round(1e3 * res["decode_ms_p90"], 3)],
         "append_us": round(1e3 * res["append_ms"], 3),
+        "append_kernel_us": round(1e3 * res["append_kernel_ms"], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -302,8 +384,11 @@ def main():
                    "valid_slots": res["valid"], "gathered_bytes": res["gathered"],
                    "splits": res["splits"], "cache": "nvfp4-352"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "sparse_decode_kernel", "bytes_per_launch": res["gathered"]},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic["total"] if traffic else None,
+                     "traffic_read_write": [traffic["read"], traffic["write"]] if traffic else None,
+                     "kernel": "sparse_decode_kernel", "bytes_per_launch": res["gathered"],
+                     "kernel_us": round(1e3 * res["kernel_ms"], 3)},
     }
     if "comparators" in res:
         line["comparators"] = {k: round(v, 3) for k, v in res["comparators"].items()}

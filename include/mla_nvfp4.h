@@ -211,6 +211,26 @@ int mla_nvfp4_gather_dequant_fp8(const uint8_t* cache, int64_t cache_rows,
                                  float fp8_scale, uint8_t* fp8_rows,
                                  int32_t* staged_indices, void* stream);
 
+/*
+ * Kernel timing for benchmarks (instrumentation, not part of the method).
+ *
+ * mla_kernel_timing(1) makes every later launching call of this library
+ * (quantize-append, gather-dequant, sparse decode) made by this host thread
+ * on the current device launch its kernel with hipExtLaunchKernel and a
+ * pair of HIP events owned by the library, which the runtime records at
+ * the kernel's own start and end on the caller's stream.  Results are
+ * unchanged; each launch costs a little more host and queue time.
+ * mla_kernel_timing(0) stops that and releases the events.  Returns
+ * MLA_ERR_HIP if the events cannot be created.
+ *
+ * mla_last_kernel_ms waits for the last timed launch of this thread to
+ * finish and writes its kernel duration in milliseconds to *ms (host
+ * pointer).  Returns MLA_ERR_INVALID_ARG if ms is NULL or no launch has
+ * been timed since timing was enabled.
+ */
+int mla_kernel_timing(int enable);
+int mla_last_kernel_ms(float* ms);
+
 /* Human-readable name of a status code (static storage). */
 const char* mla_status_string(int status);
 

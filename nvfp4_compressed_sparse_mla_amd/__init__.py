@@ -167,3 +167,17 @@ def gather_dequant_fp8(cache: torch.Tensor, indices: torch.Tensor, fp8_scale: fl
         rows.data_ptr(), staged_indices.data_ptr(), _stream(cache))
     check(st, "mla_nvfp4_gather_dequant_fp8")
     return rows, staged_indices
+
+
+def kernel_timing(enable: bool) -> None:
+    """Benchmark instrumentation: time every later library kernel with HIP events."""
+    check(load().mla_kernel_timing(1 if enable else 0), "mla_kernel_timing")
+
+
+def last_kernel_ms() -> float:
+    """Kernel duration (ms) of the last timed library launch; waits for it to finish."""
+    import ctypes
+
+    ms = ctypes.c_float(0.0)
+    check(load().mla_last_kernel_ms(ctypes.byref(ms)), "mla_last_kernel_ms")
+    return float(ms.value)

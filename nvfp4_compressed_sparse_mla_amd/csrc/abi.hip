@@ -17,6 +17,32 @@ bool pow2_scale(float s) {
   return frexpf(s, &e) == 0.5f && e >= -20 && e <= 20;
 }
 
+// Benchmark timing state of one host thread (see mla_kernel_timing).
+struct Timing {
+  bool enabled = false, recorded = false;
+  int device = -1;
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+Timing& timing() {
+  static thread_local Timing tm;
+  return tm;
+}
+
+// Events for this launch if timing is on for the current device.
+mla::KernelEvents timing_events() {
+  Timing& tm = timing();
+  int dev = -1;
+  if (tm.enabled && hipGetDevice(&dev) == hipSuccess && dev == tm.device) return {tm.start, tm.stop};
+  return {};
+}
+
+int launched(hipError_t e, const mla::KernelEvents& ev) {
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  if (ev.start) timing().recorded = true;
+  return MLA_OK;
+}
+
 int head_groups(int32_t H) {
   if (H == 16 || H == 32) return 1;
   if (H == 64) return 2;
@@ -58,10 +84,11 @@ int mla_nvfp4_quantize_append(const void* latent, int64_t latent_row_stride, con
   int st = quantize_checks(latent, latent_row_stride, rope, rope_row_stride, dtype, n, slot_mapping,
                            cache, cache_rows);
   if (st != MLA_OK || n == 0) return st;
-  hipError_t e = mla::launch_nvfp4_quantize(latent, latent_row_stride, rope, rope_row_stride,
-                                            dtype == MLA_BF16, n, slot_mapping, cache, cache_rows,
-                                            (hipStream_t)stream);
-  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  const mla::KernelEvents ev = timing_events();
+  return launched(mla::launch_nvfp4_quantize(latent, latent_row_stride, rope, rope_row_stride,
+                                             dtype == MLA_BF16, n, slot_mapping, cache, cache_rows,
+                                             (hipStream_t)stream, ev),
+                  ev);
 }
 
 int mla_fp8_quantize_append(const void* latent, int64_t latent_row_stride, const void* rope,
@@ -73,10 +100,11 @@ int mla_fp8_quantize_append(const void* latent, int64_t latent_row_stride, const
   if (st != MLA_OK) return st;
   if (!pow2_scale(kv_scale)) return MLA_ERR_INVALID_ARG;
   if (n == 0) return MLA_OK;
-  hipError_t e = mla::launch_fp8_quantize(latent, latent_row_stride, rope, rope_row_stride,
-                                          dtype == MLA_BF16, n, slot_mapping, cache, cache_rows,
-                                          kv_scale, (hipStream_t)stream);
-  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  const mla::KernelEvents ev = timing_events();
+  return launched(mla::launch_fp8_quantize(latent, latent_row_stride, rope, rope_row_stride,
+                                           dtype == MLA_BF16, n, slot_mapping, cache, cache_rows,
+                                           kv_scale, (hipStream_t)stream, ev),
+                  ev);
 }
 
 int32_t mla_sparse_decode_num_splits(int64_t num_tokens, int32_t num_heads, int32_t topk) {
@@ -154,8 +182,34 @@ int mla_sparse_decode(const void* q, int q_dtype, int64_t num_tokens, int32_t nu
   p.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ctr);
   p.part_o = reinterpret_cast<_Float16*>(reinterpret_cast<char*>(workspace) + ctr + pl);
   p.S = S;
-  hipError_t e = mla::launch_decode(p, cache_fmt, q_dtype == MLA_BF16, (hipStream_t)stream);
-  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  const mla::KernelEvents ev = timing_events();
+  return launched(mla::launch_decode(p, cache_fmt, q_dtype == MLA_BF16, (hipStream_t)stream, ev), ev);
+}
+
+int mla_kernel_timing(int enable) {
+  Timing& tm = timing();
+  if (tm.enabled) {
+    (void)hipEventDestroy(tm.start);
+    (void)hipEventDestroy(tm.stop);
+    tm = Timing{};
+  }
+  if (!enable) return MLA_OK;
+  if (hipGetDevice(&tm.device) != hipSuccess) return MLA_ERR_HIP;
+  if (hipEventCreate(&tm.start) != hipSuccess) return MLA_ERR_HIP;
+  if (hipEventCreate(&tm.stop) != hipSuccess) {
+    (void)hipEventDestroy(tm.start);
+    tm = Timing{};
+    return MLA_ERR_HIP;
+  }
+  tm.enabled = true;
+  return MLA_OK;
+}
+
+int mla_last_kernel_ms(float* ms) {
+  Timing& tm = timing();
+  if (!ms || !tm.enabled || !tm.recorded) return MLA_ERR_INVALID_ARG;
+  if (hipEventSynchronize(tm.stop) != hipSuccess) return MLA_ERR_HIP;
+  return hipEventElapsedTime(ms, tm.start, tm.stop) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 int mla_nvfp4_gather_dequant_fp8(const uint8_t* cache, int64_t cache_rows, const int32_t* indices,
@@ -189,8 +243,8 @@ int mla_nvfp4_gather_dequant_fp8(const uint8_t* cache, int64_t cache_rows, const
   p.inv_scale = 1.0f / fp8_scale;
   p.rows = fp8_rows;
   p.sidx = staged_indices;
-  hipError_t e = mla::launch_gather_dequant_fp8(p, (hipStream_t)stream);
-  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  const mla::KernelEvents ev = timing_events();
+  return launched(mla::launch_gather_dequant_fp8(p, (hipStream_t)stream, ev), ev);
 }
 
 }  // extern "C"

@@ -727,10 +727,10 @@ int decode_auto_splits(int64_t T, int H, int topk) {
   const int cus = device_cus() > 0 ? device_cus() : 256;
   // One workgroup per CU is resident at a time: fill the CUs once (more
   // splits than that would start a second, mostly idle round).  A split
-  // keeps at least 128 valid rows (two tiles per stream) so its fixed
+  // keeps at least 256 valid rows (four tiles per stream) so its fixed
   // costs (index compaction, q load, stream and split merges) stay small.
   int64_t s = cus / groups;
-  int64_t max_by_rows = topk / 128;
+  int64_t max_by_rows = topk / 256;
   if (max_by_rows < 1) max_by_rows = 1;
   if (s > max_by_rows) s = max_by_rows;
   if (s > 64) s = 64;
@@ -750,7 +750,8 @@ size_t decode_workspace_bytes(int64_t T, int H, int S) {
   return ctr + pl + po;
 }
 
-hipError_t launch_decode(const DecodeParams& p, int fmt, bool bf16, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, int fmt, bool bf16, hipStream_t stream,
+                         const KernelEvents& ev) {
   const int64_t blocks = p.T * p.G * p.S;
   dim3 grid((unsigned)blocks), block(kThreads);
   void* args[] = {const_cast<DecodeParams*>(&p)};
@@ -761,7 +762,7 @@ hipError_t launch_decode(const DecodeParams& p, int fmt, bool bf16, hipStream_t 
   else
     fn = bf16 ? (const void*)sparse_decode_kernel<kFmtFp8, true>
               : (const void*)sparse_decode_kernel<kFmtFp8, false>;
-  return hipLaunchKernel(fn, grid, block, args, 0, stream);
+  return launch_kernel(fn, grid, block, args, stream, ev);
 }
 
 }  // namespace mla

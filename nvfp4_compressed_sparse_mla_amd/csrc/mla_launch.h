@@ -1,10 +1,24 @@
 // Host-side launch interface between the C ABI layer and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace mla {
+
+// Optional benchmark events: when `start` is set the kernel is launched with
+// hipExtLaunchKernel, which records start/stop at the kernel's own start and
+// end on the stream.
+struct KernelEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+inline hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, hipStream_t stream,
+                                const KernelEvents& ev) {
+  if (ev.start) return hipExtLaunchKernel(fn, grid, block, args, 0, stream, ev.start, ev.stop, 0);
+  return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
 
 struct DecodeParams {
   const void* q;
@@ -33,14 +47,16 @@ struct DecodeParams {
 int decode_auto_splits(int64_t T, int H, int topk);
 size_t decode_workspace_bytes(int64_t T, int H, int S);
 
-hipError_t launch_decode(const DecodeParams& p, int fmt, bool bf16, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int fmt, bool bf16, hipStream_t stream,
+                         const KernelEvents& ev);
 
 hipError_t launch_nvfp4_quantize(const void* latent, int64_t ls, const void* rope, int64_t rs,
                                  bool bf16, int64_t n, const int64_t* slots, uint8_t* cache,
-                                 int64_t cache_rows, hipStream_t stream);
+                                 int64_t cache_rows, hipStream_t stream, const KernelEvents& ev);
 hipError_t launch_fp8_quantize(const void* latent, int64_t ls, const void* rope, int64_t rs,
                                bool bf16, int64_t n, const int64_t* slots, uint8_t* cache,
-                               int64_t cache_rows, float kv_scale, hipStream_t stream);
+                               int64_t cache_rows, float kv_scale, hipStream_t stream,
+                               const KernelEvents& ev);
 
 struct StagedParams {
   const uint8_t* cache;
@@ -57,6 +73,6 @@ struct StagedParams {
   uint8_t* rows;
   int32_t* sidx;
 };
-hipError_t launch_gather_dequant_fp8(const StagedParams& p, hipStream_t stream);
+hipError_t launch_gather_dequant_fp8(const StagedParams& p, hipStream_t stream, const KernelEvents& ev);
 
 }  // namespace mla

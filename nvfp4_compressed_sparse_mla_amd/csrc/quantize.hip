@@ -108,33 +108,28 @@ __global__ __launch_bounds__(256) void fp8_quantize_append_kernel(
 
 hipError_t launch_nvfp4_quantize(const void* latent, int64_t ls, const void* rope, int64_t rs,
                                  bool bf16, int64_t n, const int64_t* slots, uint8_t* cache,
-                                 int64_t cache_rows, hipStream_t stream) {
+                                 int64_t cache_rows, hipStream_t stream, const KernelEvents& ev) {
   dim3 grid((unsigned)((n + 7) / 8)), block(256);
-  if (bf16)
-    hipLaunchKernelGGL(nvfp4_quantize_append_kernel<true>, grid, block, 0, stream,
-                       (const uint16_t*)latent, ls, (const uint16_t*)rope, rs, n, slots, cache,
-                       cache_rows);
-  else
-    hipLaunchKernelGGL(nvfp4_quantize_append_kernel<false>, grid, block, 0, stream,
-                       (const uint16_t*)latent, ls, (const uint16_t*)rope, rs, n, slots, cache,
-                       cache_rows);
-  return hipGetLastError();
+  const uint16_t* lat = (const uint16_t*)latent;
+  const uint16_t* rp = (const uint16_t*)rope;
+  void* args[] = {&lat, &ls, &rp, &rs, &n, &slots, &cache, &cache_rows};
+  const void* fn = bf16 ? (const void*)nvfp4_quantize_append_kernel<true>
+                        : (const void*)nvfp4_quantize_append_kernel<false>;
+  return launch_kernel(fn, grid, block, args, stream, ev);
 }
 
 hipError_t launch_fp8_quantize(const void* latent, int64_t ls, const void* rope, int64_t rs,
                                bool bf16, int64_t n, const int64_t* slots, uint8_t* cache,
-                               int64_t cache_rows, float kv_scale, hipStream_t stream) {
+                               int64_t cache_rows, float kv_scale, hipStream_t stream,
+                               const KernelEvents& ev) {
   dim3 grid((unsigned)((n + 7) / 8)), block(256);
-  const float inv = 1.0f / kv_scale;
-  if (bf16)
-    hipLaunchKernelGGL(fp8_quantize_append_kernel<true>, grid, block, 0, stream,
-                       (const uint16_t*)latent, ls, (const uint16_t*)rope, rs, n, slots, cache,
-                       cache_rows, inv);
-  else
-    hipLaunchKernelGGL(fp8_quantize_append_kernel<false>, grid, block, 0, stream,
-                       (const uint16_t*)latent, ls, (const uint16_t*)rope, rs, n, slots, cache,
-                       cache_rows, inv);
-  return hipGetLastError();
+  float inv = 1.0f / kv_scale;
+  const uint16_t* lat = (const uint16_t*)latent;
+  const uint16_t* rp = (const uint16_t*)rope;
+  void* args[] = {&lat, &ls, &rp, &rs, &n, &slots, &cache, &cache_rows, &inv};
+  const void* fn = bf16 ? (const void*)fp8_quantize_append_kernel<true>
+                        : (const void*)fp8_quantize_append_kernel<false>;
+  return launch_kernel(fn, grid, block, args, stream, ev);
 }
 
 }  // namespace mla

@@ -77,11 +77,11 @@ __global__ __launch_bounds__(256) void gather_dequant_fp8_kernel(StagedParams p)
   *reinterpret_cast<u32x2*>(dst + kLatent + 8 * part) = (u32x2){r0, r1};
 }
 
-hipError_t launch_gather_dequant_fp8(const StagedParams& p, hipStream_t stream) {
+hipError_t launch_gather_dequant_fp8(const StagedParams& p, hipStream_t stream, const KernelEvents& ev) {
   const int64_t total = p.T * p.topk;
   dim3 grid((unsigned)((total + 31) / 32)), block(256);
-  hipLaunchKernelGGL(gather_dequant_fp8_kernel, grid, block, 0, stream, p);
-  return hipGetLastError();
+  void* args[] = {const_cast<StagedParams*>(&p)};
+  return launch_kernel((const void*)gather_dequant_fp8_kernel, grid, block, args, stream, ev);
 }
 
 }  // namespace mla

@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 7, names
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -109,6 +109,13 @@ def test_workspace_size_arithmetic(lib):
     assert lib.mla_sparse_decode_workspace_size(15, 24, 2048, 1) == 0
     assert lib.mla_sparse_decode_workspace_size(15, 32, 0, 1) == 0
     assert lib.mla_sparse_decode_workspace_size(15, 32, 2048, 99) == 0
+
+
+def test_timing_query_without_a_timed_launch(lib):
+    ms = ctypes.c_float(0.0)
+    assert lib.mla_last_kernel_ms(None) == INVALID
+    assert lib.mla_last_kernel_ms(ctypes.byref(ms)) == INVALID   # timing never enabled
+    assert lib.mla_kernel_timing(0) == OK                         # disabling is always fine
 
 
 def test_gather_dequant_rejects_bad_arguments(lib):

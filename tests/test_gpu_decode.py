@@ -209,3 +209,18 @@ def test_prefill4k_full_size_sampled(qdt):
     mla.quantize_append(w.latent[w.append_slots], w.rope[w.append_slots], w.append_slots, cache)
     out, lse = _run(w, cache)
     _check(w, cache, out, lse, tokens=[0, 1023, 1024, 4095], what=f"prefill4k-{qdt}")
+
+
+def test_kernel_timing_hook():
+    """The benchmark timing hook records the kernel's own duration and leaves results unchanged."""
+    w = make_custom(3000, 2, 32, 512, seed=31, device=DEV)
+    cache = _fill(w)
+    plain = _run(w, cache)
+    mla.kernel_timing(True)
+    try:
+        timed = _run(w, cache)
+        ms = mla.last_kernel_ms()
+    finally:
+        mla.kernel_timing(False)
+    assert 0.0 < ms < 100.0
+    assert torch.equal(plain[0], timed[0]) and torch.equal(plain[1], timed[1])
