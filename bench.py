@@ -12,7 +12,9 @@ distinct picks from each sequence's 146,000 rows, 2.2M-row NVFP4 pool.
 Timing: W untimed warm-up steps, then K timed steps.  By default the caches
 are cold for every step: a 1 GiB read sweep runs between steps (outside the
 per-step events) so neither the 256 MB Infinity Cache nor L2 holds the
-gathered rows.  Every step is bracketed by HIP events on the stream the
+gathered rows; the step's small inputs (q, index lists, block table, new
+rows), which the kernels before attention have just written in a real decode
+step, are read once after the sweep (--cold-inputs leaves them cold).  Every step is bracketed by HIP events on the stream the
 kernels run on; `value` and `us_per_step` come from that pass.  A second
 pass repeats the steps with the library's kernel timing on
 (hipExtLaunchKernel events at each kernel's own start and end): those
@@ -57,6 +59,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode15")
     ap.add_argument("--warm", action="store_true", help="no cache flush between steps")
+    ap.add_argument("--cold-inputs", action="store_true",
+                    help="leave q, index lists and block table cold too (default: only the gathered rows)")
     ap.add_argument("--splits", type=int, default=0, help="force the split count (0 = launch sizer)")
     ap.add_argument("--no-comparators", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -122,9 +126,20 @@ def _gpu_run(args):
     valid = w.valid_slots()
     gathered = valid * ROW_BYTES
 
+    # The step's own small inputs (q, index lists, block table, the new rows)
+    # are written by the kernels that precede attention in a decode step, so
+    # after the sweep they are read once more to leave them in cache; only
+    # the gathered cache rows stay cold.  --cold-inputs skips that.
+    step_inputs = [w.q, w.indices, app_lat, app_rope, app_slots]
+    if w.block_table is not None:
+        step_inputs += [w.block_table, w.token_seq]
+
     def do_flush():
         if flush is not None:
             flush.sum()
+            if not args.cold_inputs:
+                for x in step_inputs:
+                    x.sum()
 
     def step(tm=None, i=0):
         if tm:
@@ -378,7 +393,9 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic",
-        "cache_state": "warm" if args.warm else "cold (1 GiB sweep between steps)",
+        "cache_state": "warm" if args.warm else (
+            "cold (1 GiB sweep between steps, inputs included)" if args.cold_inputs else
+            "cold rows (1 GiB sweep between steps; q, index lists, block table and new rows re-read after it)"),
         "config": {"workload": f"{args.workload}: {DESCRIPTIONS.get(args.workload, '')}",
                    "tokens": res["T"], "heads": res["H"], "topk": res["K"], "pool_rows": res["rows"],
                    "valid_slots": res["valid"], "gathered_bytes": res["gathered"],

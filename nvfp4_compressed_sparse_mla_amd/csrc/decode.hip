@@ -35,11 +35,12 @@
 //             18 K-steps of a 16x16x32 MFMA A operand (q uses the same
 //             assignment).  The latent FP16 values also go to the V buffer.
 //     scores  S^T[16 rows x 32 heads]: 36 MFMAs (16x16x32, FP16 -> FP32).
-//     softmax base 2 against a lazily raised reference max: the reference
-//             moves only when a score exceeds it by more than 8 (one ballot
-//             decides), so P = 2^(s - ref) <= 256 stays accurate in FP16 and
-//             the common tile needs no cross-lane max and no O rescale.  Row
-//             sums accumulate per lane and are reduced once at the end.
+//     softmax base 2 against a lazily raised reference max: the first tile
+//             sets the reference, which then moves only when a score exceeds
+//             it by more than 15 (one ballot decides), so P = 2^(s - ref) <=
+//             2^15 stays inside FP16 (with its full 11-bit precision) and the
+//             common tile needs no cross-lane max and no O rescale.  Row sums
+//             accumulate per lane and are reduced once at the end.
 //     values  O[32 heads x 512 cols] += P . V: 16 MFMAs (32x32x16).  Each
 //             lane's P operand is 8 rows of one head: 4 of its own scores
 //             and 4 from lane ^ 16.  V's B operand comes from the V buffer
@@ -52,6 +53,8 @@
 #include "mla_device.h"
 #include "mla_launch.h"
 
+#include <type_traits>
+
 namespace mla {
 
 namespace {
@@ -62,7 +65,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kVRow = kLatent + 16;   // FP16 elements per V-buffer row (stride = 8 banks mod 64)
 constexpr int kKSteps = 18;           // 576 key dimensions / 32
-constexpr float kLazy = 8.0f;         // the reference max may trail the running max by up to 2^8
+constexpr float kLazy = 15.0f;        // P = 2^(s - reference) <= 2^15 stays inside FP16
+constexpr float kMargin = 5.0f;       // a new reference sits 2^5 above the max that set it
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -128,22 +132,37 @@ struct Raw<kFmtFp8> {
   u32x4 rp;       // 16 rope bytes
 };
 
+// The row bytes are read in two parts so that the second half of the
+// latent (K-steps 8..15) occupies registers only from when it is decoded:
+// part A = latent K-steps 0..7, scales and rope; part B = latent K-steps
+// 8..15.  Each part waits for its own reads.
 template <int kFmt>
-__device__ __forceinline__ void ring_read(Raw<kFmt>& r, uint32_t row_base, int kg) {
+__device__ __forceinline__ void ring_read_a(Raw<kFmt>& r, uint32_t row_base, int kg) {
   if constexpr (kFmt == kFmtNvfp4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.l[i] = ring_b128(row_base + 64 * kg + 16 * i);
+    for (int i = 0; i < 2; ++i) r.l[i] = ring_b128(row_base + 64 * kg + 16 * i);
     r.sc = ring_b64(row_base + kScaleOff + 8 * kg);
     r.rp = ring_b128(row_base + kRopeOff + 16 * kg);
-    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)"
-                   : "+v"(r.l[0]), "+v"(r.l[1]), "+v"(r.l[2]), "+v"(r.l[3]), "+v"(r.sc), "+v"(r.rp));
+    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(r.l[0]), "+v"(r.l[1]), "+v"(r.sc), "+v"(r.rp));
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r.l[i] = ring_b128(row_base + 128 * kg + 16 * i);
+    for (int i = 0; i < 4; ++i) r.l[i] = ring_b128(row_base + 128 * kg + 16 * i);
     r.rp = ring_b128(row_base + kLatent + 16 * kg);
     MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)"
-                   : "+v"(r.l[0]), "+v"(r.l[1]), "+v"(r.l[2]), "+v"(r.l[3]), "+v"(r.l[4]),
-                     "+v"(r.l[5]), "+v"(r.l[6]), "+v"(r.l[7]), "+v"(r.rp));
+                   : "+v"(r.l[0]), "+v"(r.l[1]), "+v"(r.l[2]), "+v"(r.l[3]), "+v"(r.rp));
+  }
+}
+
+template <int kFmt>
+__device__ __forceinline__ void ring_read_b(Raw<kFmt>& r, uint32_t row_base, int kg) {
+  if constexpr (kFmt == kFmtNvfp4) {
+#pragma unroll
+    for (int i = 2; i < 4; ++i) r.l[i] = ring_b128(row_base + 64 * kg + 16 * i);
+    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(r.l[2]), "+v"(r.l[3]));
+  } else {
+#pragma unroll
+    for (int i = 4; i < 8; ++i) r.l[i] = ring_b128(row_base + 128 * kg + 16 * i);
+    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(r.l[4]), "+v"(r.l[5]), "+v"(r.l[6]), "+v"(r.l[7]));
   }
 }
 
@@ -183,21 +202,19 @@ __device__ __forceinline__ half8_t load_q8(const uint16_t* p) {
   }
 }
 
-// two adjacent output elements
-template <bool kBf16>
-__device__ __forceinline__ void store_out2(void* out, int64_t i, float a, float b) {
-  if constexpr (kBf16) {
-    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + i) =
-        (uint32_t)float_to_bf16_rne(a) | ((uint32_t)float_to_bf16_rne(b) << 16);
-  } else {
-    *reinterpret_cast<half2_t*>(reinterpret_cast<half_t*>(out) + i) = (half2_t){(half_t)a, (half_t)b};
+// eight consecutive output elements (16-byte aligned), fp16 or bf16
+template <bool kBf16, typename T>
+__device__ __forceinline__ void store8(T* dst, const float (&v)[8]) {
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (kBf16) {
+      w[i] = (uint32_t)float_to_bf16_rne(v[2 * i]) | ((uint32_t)float_to_bf16_rne(v[2 * i + 1]) << 16);
+    } else {
+      w[i] = as_u32((half2_t){(half_t)v[2 * i], (half_t)v[2 * i + 1]});
+    }
   }
-}
-
-template <bool kBf16>
-__device__ __forceinline__ void store_out(void* out, int64_t i, float v) {
-  if constexpr (kBf16) reinterpret_cast<uint16_t*>(out)[i] = float_to_bf16_rne(v);
-  else reinterpret_cast<half_t*>(out)[i] = (half_t)v;
+  *reinterpret_cast<u32x4*>(dst) = w;
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
@@ -205,33 +222,34 @@ __device__ __forceinline__ uint32_t shfl_xor_u(uint32_t v, int m) {
   return (uint32_t)__shfl_xor((int)v, m, 64);
 }
 
-// B operands of 4 value MFMAs (4 consecutive 32-column blocks starting at
-// `base`) from the V buffer: ds_read_b64_tr_b16 gives each lane 4
+// B operands of the 4 value MFMAs of column group q (32-column blocks q,
+// q+4, q+8, q+12) from the V buffer: ds_read_b64_tr_b16 gives each lane 4
 // consecutive rows of one column; two reads (rows 0-3 and 4-7 of the lane's
 // 8) make one operand.  In assembly so that the compiler does not make them
-// wait for the ring's DMA.
-__device__ __forceinline__ void read_v4(u32x4 (&b)[4], uint32_t base) {
+// wait for the ring's DMA; the memory clobber keeps the V-buffer writes that
+// follow in program order from moving above them.
+__device__ __forceinline__ void read_v4_group(u32x4 (&b)[4], uint32_t base, int q) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t a = base + 64 * (q + 4 * e);
+    (void)a;
     u32x2 lo, hi;
-    MLA_DEVICE_ASM("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(base), "i"(64 * i));
-    MLA_DEVICE_ASM("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(base), "i"(64 * i + 8 * kVRow));
-    b[i] = (u32x4){lo.x, lo.y, hi.x, hi.y};
+    MLA_DEVICE_ASM("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a) : "memory");
+    MLA_DEVICE_ASM("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(a), "i"(8 * kVRow) : "memory");
+    b[e] = (u32x4){lo.x, lo.y, hi.x, hi.y};
   }
-}
-
-// Column block held by accumulator block i (0..15) of wave w.  The blocks
-// are rotated per wave so that the stream merge (a reduce-scatter between
-// waves w, w^1 and then w, w^2) always keeps blocks 0..7 and then 0..3:
-// block i of w and block 8+i of w^1 are the same columns, and so are block
-// i < 4 of w and block 4+i of w^2.  Each group of 4 blocks (4Q..4Q+3) is 4
-// consecutive column blocks starting at this value for i = 4Q.
-__device__ __forceinline__ int col_block(int w, int i) {
-  return 8 * (((i >> 3) + (w & 1)) & 1) + (((i & 7) + 4 * (w >> 1)) & 7);
 }
 
 __device__ __forceinline__ void lgkm_wait(u32x4 (&b)[4]) {
   MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+}
+
+// Workgroup barrier for LDS data only: waits for this wave's LDS operations,
+// not for its outstanding global loads (__syncthreads() would also wait for
+// those, e.g. the q loads still in flight during the prologue).  The memory
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
@@ -289,33 +307,17 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   uint8_t* ring = ring_all + wave * kWaveRing;
   half_t* vbuf = vbuf_all + wave * kWaveV;
 
-  // ---------------------------------------------------------------- q
-  // B operand of K-step ks for head block hb: q[head][d] with
-  // d(ks < 16) = 128kg + 8ks + [0,8) and d(16 + i) = 512 + 16kg + 8i + [0,8)
-  half8_t qreg[2][kKSteps];
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const int head = g * kHG + hb * 16 + r16;
-    if (head < p.H) {
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + t * p.q_st + (int64_t)head * p.q_sh;
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) qreg[hb][ks] = load_q8<kBf16>(qp + 128 * kg + 8 * ks);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) qreg[hb][16 + i] = load_q8<kBf16>(qp + kLatent + 16 * kg + 8 * i);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) qreg[hb][ks] = (half8_t){0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  }
-
   // ------------------------------------------------ compact the valid rows
   // All index loads are issued before any is used, then all block-table
   // loads: two dependent memory round trips (addresses of slots past topk
   // or of masked entries are clamped to valid ones and the result dropped).
-  int rows8[8], pre8[8];
+  // The index loads head the longest dependent chain (index -> block table
+  // -> row DMA), so they and the block-table loads are issued before the q
+  // loads, which only the first score MFMA needs (vector loads complete in
+  // issue order, so anything issued after q would wait for it).
+  int v8[8];
   {
     const int32_t* ip = p.idx + t * p.idx_st;
-    int v8[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int slot = i * kThreads + tid;
@@ -324,16 +326,40 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (i * kThreads + tid >= p.topk) v8[i] = -1;
-    if (p.bt) {
-      const int64_t seq = p.tok_seq[t];
-      const bool seq_ok = seq >= 0 && seq < p.bt_rows;
-      const int32_t* btr = p.bt + (seq_ok ? seq : 0) * p.bt_st;
-      int b8[8], pb8[8];
+  }
+  int b8[8], pb8[8];
+  bool seq_ok = true;
+  if (p.bt) {
+    const int64_t seq = p.tok_seq[t];
+    seq_ok = seq >= 0 && seq < p.bt_rows;
+    const int32_t* btr = p.bt + (seq_ok ? seq : 0) * p.bt_st;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        b8[i] = v8[i] >= 0 ? v8[i] / p.bs : 0;
-        pb8[i] = btr[b8[i] < p.bt_cols ? b8[i] : p.bt_cols - 1];
-      }
+    for (int i = 0; i < 8; ++i) {
+      b8[i] = v8[i] >= 0 ? v8[i] / p.bs : 0;
+      pb8[i] = btr[b8[i] < p.bt_cols ? b8[i] : p.bt_cols - 1];
+    }
+  }
+
+  // ---------------------------------------------------------------- q
+  // B operand of K-step ks for head block hb: q[head][d] with
+  // d(ks < 16) = 128kg + 8ks + [0,8) and d(16 + i) = 512 + 16kg + 8i + [0,8)
+  // (With 16 heads the second head block repeats head 15: straight-line
+  // loads keep the compiler's load counting exact, and those lanes' results
+  // are never stored.)
+  half8_t qreg[2][kKSteps];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int head = min(g * kHG + hb * 16 + r16, p.H - 1);
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + t * p.q_st + (int64_t)head * p.q_sh;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qreg[hb][ks] = load_q8<kBf16>(qp + 128 * kg + 8 * ks);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) qreg[hb][16 + i] = load_q8<kBf16>(qp + kLatent + 16 * kg + 8 * i);
+  }
+
+  int rows8[8], pre8[8];
+  {
+    if (p.bt) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         int r = -1;
@@ -354,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
       if (lane == 0) cnt_s[i][wave] = __popcll(m);
     }
   }
-  __syncthreads();
+  lds_barrier();
   int total = 0;
   {
     int base[8];
@@ -371,7 +397,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     for (int i = 0; i < 8; ++i)
       if (rows8[i] >= 0) phys[base[i] + pre8[i]] = rows8[i];
   }
-  __syncthreads();
+  lds_barrier();
 
   const int r0 = (int)((int64_t)total * s / S);
   const int n = (int)((int64_t)total * (s + 1) / S) - r0;
@@ -379,17 +405,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
 
   // ---------------------------------------------------------------- stream state
-  float16_t acc_o[16];                    // O[32 heads x 32 cols] of column block col_block(wave, i), C layout
-#pragma unroll
-  for (int nb = 0; nb < 16; ++nb)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc_o[nb][j] = 0.0f;
-  // byte offset in a V-buffer row of accumulator blocks 4q..4q+3
-  uint32_t vq[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) vq[q] = 64 * col_block(wave, 4 * q);
-  float mref[2] = {kNegInf, kNegInf};     // reference max of head hb*16 + r16 (base 2)
-  float lsum[2] = {0.0f, 0.0f};           // this lane's share of that head's row sum
+  float16_t acc_o[16];                    // O[32 heads x 32 cols] of column block i, C layout
+  float mref[2];                          // reference of head hb*16 + r16 (base 2)
+  float lsum[2];                          // this lane's share of that head's row sum
 
   // DMA of this wave's k-th tile (split tile wave + 4k) into ring slot
   // `slot`: instruction j moves pieces 64j + lane (piece = row * kRB/16 +
@@ -397,11 +415,16 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   // Pieces past the tile (padding of the last instruction) re-load piece 0
   // into the slot's padding; rows past the split re-load the split's last
   // row.  Both are real rows and are never used.
+  // Each lane's (row, 16-byte piece) of DMA instruction j is recomputed
+  // from the lane index at every issue (an opaque copy keeps the compiler
+  // from hoisting per-instruction addresses into registers).
   auto issue = [&](int k, int slot) {
     const int tile = wave + kWaves * k;
+    int ln = lane;
+    MLA_DEVICE_ASM("" : "+v"(ln));
 #pragma unroll
     for (int j = 0; j < kInstr; ++j) {
-      int c = 64 * j + lane;
+      int c = 64 * j + ln;
       c = c < kPieces ? c : 0;
       const int row = c / (kRB / 16), piece = c - row * (kRB / 16);
       int i = tile * kRowsT + row;
@@ -411,72 +434,90 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     }
   };
 
+  // V-buffer addresses: this lane's ds_read_b64_tr_b16 base for column
+  // block 0 (block b is 64 bytes further) and its row for the V writes.
+  const int vgrp = lane >> 4, vsl = lane & 15;
+  const uint32_t vb = lds_off(vbuf + (8 * (vgrp >> 1) + (vsl >> 2)) * kVRow + 16 * (vgrp & 1) + 4 * (vsl & 3));
+  half_t* const vrow = vbuf + r16 * kVRow + 128 * kg;
+
+  // Per tile (16 rows, this wave): wait for the tile's DMA, read the row
+  // bytes from the ring, decode them (A operands of the score MFMAs, and the
+  // latent also into the V buffer), scores, softmax, then the values.  The
+  // next two tiles' DMA is in flight throughout.
+  //
+  // Softmax reference (base 2): the first tile sets it to its max + kMargin
+  // (P <= 2^-kMargin there); afterwards it moves only when a score exceeds
+  // it by more than kLazy (P would leave FP16), one ballot deciding; then O
+  // and the row sums are rescaled in place.
   const float sm = p.sm_log2;
+#pragma unroll
+  for (int nb = 0; nb < 16; ++nb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc_o[nb][j] = 0.0f;
+  mref[0] = mref[1] = kNegInf;
+  lsum[0] = lsum[1] = 0.0f;
   if (my_tiles > 0) {
     issue(0, 0);
-    if (my_tiles > 1) issue(1, 1);
-    for (int k = 0; k < my_tiles; ++k) {
-      const int slot = k % kDepth;
-      // wait until only this wave's later tiles are in flight
-      if constexpr (kDepth == 3) {
-        if (k + 2 < my_tiles) {
-          issue(k + 2, (k + 2) % 3);   // that slot held tile k - 1, already in registers
-          wait_vmcnt<2 * kInstr>();
-        } else if (k + 1 < my_tiles) {
-          wait_vmcnt<kInstr>();
-        } else {
-          wait_vmcnt<0>();
-        }
-      } else {
-        if (k + 1 < my_tiles) wait_vmcnt<kInstr>();
-        else wait_vmcnt<0>();
-      }
-      const int tile = wave + kWaves * k;
-
-      // ---- decode + scores: S^T[16 rows x 32 heads]
-      Raw<kFmt> raw;
-      ring_read<kFmt>(raw, lds_off(ring + slot * kSlot + r16 * kRB), kg);
-      if constexpr (kDepth == 2) {
-        if (k + 2 < my_tiles) issue(k + 2, slot);   // the slot's bytes are in registers
-      }
-      half_t* vrow = vbuf + r16 * kVRow + 128 * kg;
-      float4_t sacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+    if (my_tiles > 1) issue(1, 1 % kDepth);
+  }
+  for (int k = 0; k < my_tiles; ++k) {
+    const int slot = k % kDepth;
+    // wait until only this wave's later tiles are in flight
+    if (k + 1 < my_tiles) wait_vmcnt<kInstr>();
+    else wait_vmcnt<0>();
+    Raw<kFmt> raw;
+    ring_read_a<kFmt>(raw, lds_off(ring + slot * kSlot + r16 * kRB), kg);
+    float4_t sacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) {
-        const half8_t kop = kstep8<kFmt>(raw, ks);
-        if (ks < 16) *reinterpret_cast<half8_t*>(vrow + 8 * ks) = kop;
-        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qreg[0][ks], sacc[0], 0, 0, 0);
-        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qreg[1][ks], sacc[1], 0, 0, 0);
+    for (int ks = 16; ks < kKSteps; ++ks) {   // rope first: its bytes are then dead
+      const half8_t kop = kstep8<kFmt>(raw, ks);
+      sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qreg[0][ks], sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qreg[1][ks], sacc[1], 0, 0, 0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      if (ks == 8) {
+        ring_read_b<kFmt>(raw, lds_off(ring + slot * kSlot + r16 * kRB), kg);
+        // the slot of tile k + 2 held tile k - 1 (3 slots) or tile k (2
+        // slots), both now in registers
+        if (k + 2 < my_tiles) issue(k + 2, (k + 2) % kDepth);
       }
+      const half8_t kop = kstep8<kFmt>(raw, ks);
+      *reinterpret_cast<half8_t*>(vrow + 8 * ks) = kop;
+      sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qreg[0][ks], sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qreg[1][ks], sacc[1], 0, 0, 0);
+    }
 
-      // ---- softmax, base 2.  The lane holds rows 4kg + j (j = 0..3) of
-      // head hb*16 + r16.
-      const int row0 = tile * kRowsT + 4 * kg;
-      float sv[2][4], tmax[2];
+    // ---- softmax, base 2.  The lane holds rows 4kg + j (j = 0..3) of
+    // head hb*16 + r16.
+    const int row0 = (wave + kWaves * k) * kRowsT + 4 * kg;
+    float sv[2][4], tmax[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      tmax[hb] = kNegInf;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sv[hb][j] = (row0 + j < n) ? sacc[hb][j] * sm : kNegInf;
+        tmax[hb] = __builtin_fmaxf(tmax[hb], sv[hb][j]);
+      }
+    }
+    const bool first = k == 0;
+    const bool raise = tmax[0] > mref[0] + kLazy || tmax[1] > mref[1] + kLazy;
+    if (first || __ballot(raise) != 0) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        tmax[hb] = kNegInf;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sv[hb][j] = (row0 + j < n) ? sacc[hb][j] * sm : kNegInf;
-          tmax[hb] = __builtin_fmaxf(tmax[hb], sv[hb][j]);
-        }
+        float m = tmax[hb];
+        m = __builtin_fmaxf(m, shfl_xor_f(m, 16));
+        m = __builtin_fmaxf(m, shfl_xor_f(m, 32));
+        const float mnew = __builtin_fmaxf(mref[hb], m) + kMargin;
+        const float al = first ? 0.0f : __builtin_amdgcn_exp2f(mref[hb] - mnew);
+        lsum[hb] *= al;
+        mref[hb] = mnew;
+        if (kg == 0) alpha_s[wave][hb * 16 + r16] = al;
       }
-      const bool raise = tmax[0] > mref[0] + kLazy || tmax[1] > mref[1] + kLazy;
-      if (__ballot(raise) != 0) {
-        // reference := running max for every head; rescale O and the sums
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          float m = tmax[hb];
-          m = __builtin_fmaxf(m, shfl_xor_f(m, 16));
-          m = __builtin_fmaxf(m, shfl_xor_f(m, 32));
-          const float mnew = __builtin_fmaxf(mref[hb], m);
-          const float al = mref[hb] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mref[hb] - mnew);
-          lsum[hb] *= al;
-          mref[hb] = mnew;
-          if (kg == 0) alpha_s[wave][hb * 16 + r16] = al;
-        }
-        // written and read by this wave only: LDS keeps a wave's order
+      if (!first) {
+        // Rescale O in place (the value MFMAs of the previous tile issued
+        // long before; LDS keeps this wave's order for alpha_s).
         MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -485,52 +526,47 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
           for (int nb = 0; nb < 16; ++nb) acc_o[nb][j] = scale_acc(acc_o[nb][j], al);
         }
       }
-      half_t ph[2][4];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float pv = __builtin_amdgcn_exp2f(sv[hb][j] - mref[hb]);
-          lsum[hb] += pv;
-          ph[hb][j] = (half_t)pv;
-        }
-      }
-      // A operand of the value MFMA: lane L = head (L & 31) x rows
-      // 8(L >> 5) + [0,8).  Lane (r16, kg) holds rows 4kg..4kg+3 of heads
-      // r16 and 16 + r16; it keeps the head block kg & 1 and swaps the other
-      // with lane ^ 16, which holds the neighbouring 4 rows.
-      const int keep = kg & 1;
-      const half4_t mine = keep ? (half4_t){ph[1][0], ph[1][1], ph[1][2], ph[1][3]}
-                                : (half4_t){ph[0][0], ph[0][1], ph[0][2], ph[0][3]};
-      const half4_t give = keep ? (half4_t){ph[0][0], ph[0][1], ph[0][2], ph[0][3]}
-                                : (half4_t){ph[1][0], ph[1][1], ph[1][2], ph[1][3]};
-      const u32x2 gv = __builtin_bit_cast(u32x2, give);
-      const u32x2 rv = {shfl_xor_u(gv.x, 16), shfl_xor_u(gv.y, 16)};
-      const half4_t other = __builtin_bit_cast(half4_t, rv);
-      const half8_t pa = keep ? (half8_t){other.x, other.y, other.z, other.w, mine.x, mine.y, mine.z, mine.w}
-                              : (half8_t){mine.x, mine.y, mine.z, mine.w, other.x, other.y, other.z, other.w};
-
-      // ---- values: O += P . V, V read in groups of 4 column blocks, the
-      // next group's reads in flight while this group's MFMAs run
-      MLA_DEVICE_ASM("" ::: "memory");   // the V-buffer writes stay above the reads
-      {
-        const int grp = lane >> 4, sl = lane & 15;
-        const uint32_t vb = lds_off(vbuf + (8 * (grp >> 1) + (sl >> 2)) * kVRow + 16 * (grp & 1) + 4 * (sl & 3));
-        u32x4 bv[2][4];
-        read_v4(bv[0], vb + vq[0]);
-        lgkm_wait(bv[0]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (q < 3) read_v4(bv[(q + 1) & 1], vb + vq[q + 1]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc_o[4 * q + i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                pa, __builtin_bit_cast(half8_t, bv[q & 1][i]), acc_o[4 * q + i], 0, 0, 0);
-          if (q < 3) lgkm_wait(bv[(q + 1) & 1]);
-        }
-      }
-      MLA_DEVICE_ASM("" ::: "memory");   // next tile's V-buffer writes stay below
     }
+    half_t ph[2][4];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pv = __builtin_amdgcn_exp2f(sv[hb][j] - mref[hb]);
+        lsum[hb] += pv;
+        ph[hb][j] = (half_t)pv;
+      }
+    }
+    // A operand of the value MFMA: lane L = head (L & 31) x rows
+    // 8(L >> 5) + [0,8).  Lane (r16, kg) holds rows 4kg..4kg+3 of heads
+    // r16 and 16 + r16; it keeps the head block kg & 1 and swaps the other
+    // with lane ^ 16, which holds the neighbouring 4 rows.
+    const int keep = kg & 1;
+    const half4_t mine = keep ? (half4_t){ph[1][0], ph[1][1], ph[1][2], ph[1][3]}
+                              : (half4_t){ph[0][0], ph[0][1], ph[0][2], ph[0][3]};
+    const half4_t give = keep ? (half4_t){ph[0][0], ph[0][1], ph[0][2], ph[0][3]}
+                              : (half4_t){ph[1][0], ph[1][1], ph[1][2], ph[1][3]};
+    const u32x2 gv = __builtin_bit_cast(u32x2, give);
+    const u32x2 rv = {shfl_xor_u(gv.x, 16), shfl_xor_u(gv.y, 16)};
+    const half4_t other = __builtin_bit_cast(half4_t, rv);
+    const half8_t pa = keep ? (half8_t){other.x, other.y, other.z, other.w, mine.x, mine.y, mine.z, mine.w}
+                            : (half8_t){mine.x, mine.y, mine.z, mine.w, other.x, other.y, other.z, other.w};
+
+    // ---- values: O += P . V, V read in groups of 4 column blocks, the
+    // next group's reads in flight while this group's MFMAs run
+    u32x4 bv[2][4];
+    read_v4_group(bv[0], vb, 0);
+    lgkm_wait(bv[0]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q < 3) read_v4_group(bv[(q + 1) & 1], vb, q + 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc_o[q + 4 * e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            pa, __builtin_bit_cast(half8_t, bv[q & 1][e]), acc_o[q + 4 * e], 0, 0, 0);
+      if (q < 3) lgkm_wait(bv[(q + 1) & 1]);
+    }
+    MLA_DEVICE_ASM("" ::: "memory");   // the next tile's V-buffer writes stay below the reads
   }
   wait_vmcnt<0>();   // no DMA may still be writing this workgroup's LDS
 
@@ -573,78 +609,109 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   __syncthreads();
   // Reduce-scatter of the weighted streams in FP32 through LDS, in the MFMA
   // C layout (lane-contiguous 16-byte pieces: no bank conflicts).  Round 1:
-  // waves w and w^1 swap blocks 8..15 and keep the sums of 0..7; round 2:
-  // waves w and w^2 swap blocks 4..7 and keep 0..3.  Exchange buffers: waves
-  // 0,1 in the ring area, 2,3 in the V area (32 KB each, the rings are idle).
+  // waves w and w^1 swap column halves (wave w keeps half w & 1); round 2:
+  // waves w and w^2 swap quarters of that half (wave w keeps quarter w >> 1).
+  // Wave w ends with column blocks 4(2(w & 1) + (w >> 1)) .. +3.  Exchange
+  // buffers: waves 0,1 in the ring area, 2,3 in the V area (32 KB each; the
+  // rings are idle).  The code is specialised per wave so that every
+  // accumulator index is a compile-time constant.
   auto xbuf = [&](int w) -> float4_t* {
     return w < 2 ? reinterpret_cast<float4_t*>(ring_all) + w * 2048
                  : reinterpret_cast<float4_t*>(vbuf_all) + (w - 2) * 2048;
   };
-  float cw[16];
+  float res[4][16];
+  auto reduce = [&](auto W0, auto W1) {
+    constexpr int w0 = decltype(W0)::value, w1 = decltype(W1)::value;
+    float cw[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) cw[j] = alpha_s[wave][c_head(j, lane)];
-  {
-    float4_t* mine = xbuf(wave);
+    for (int j = 0; j < 16; ++j) cw[j] = alpha_s[wave][c_head(j, lane)];
+    constexpr int keep1 = 8 * w0, send1 = 8 * (1 - w0);
+    {
+      float4_t* mine = xbuf(wave);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4)
-        mine[(i * 4 + j4) * 64 + lane] =
-            (float4_t){acc_o[8 + i][4 * j4] * cw[4 * j4], acc_o[8 + i][4 * j4 + 1] * cw[4 * j4 + 1],
-                       acc_o[8 + i][4 * j4 + 2] * cw[4 * j4 + 2], acc_o[8 + i][4 * j4 + 3] * cw[4 * j4 + 3]};
-  }
-  __syncthreads();
-  float res[8][16];
-  {
-    const float4_t* other = xbuf(wave ^ 1);
+        for (int j4 = 0; j4 < 4; ++j4)
+          mine[(i * 4 + j4) * 64 + lane] = (float4_t){
+              acc_o[send1 + i][4 * j4] * cw[4 * j4], acc_o[send1 + i][4 * j4 + 1] * cw[4 * j4 + 1],
+              acc_o[send1 + i][4 * j4 + 2] * cw[4 * j4 + 2], acc_o[send1 + i][4 * j4 + 3] * cw[4 * j4 + 3]};
+    }
+    __syncthreads();
+    float half_sum[8][16];
+    {
+      const float4_t* other = xbuf(wave ^ 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const float4_t v = other[(i * 4 + j4) * 64 + lane];
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const float4_t v = other[(i * 4 + j4) * 64 + lane];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) res[i][4 * j4 + e] = acc_o[i][4 * j4 + e] * cw[4 * j4 + e] + v[e];
-      }
-  }
-  __syncthreads();   // wave ^ 1 has read this wave's buffer
-  {
-    float4_t* mine = xbuf(wave);
+          for (int e = 0; e < 4; ++e)
+            half_sum[i][4 * j4 + e] = acc_o[keep1 + i][4 * j4 + e] * cw[4 * j4 + e] + v[e];
+        }
+    }
+    __syncthreads();   // wave ^ 1 has read this wave's buffer
+    constexpr int keep2 = 4 * w1, send2 = 4 * (1 - w1);
+    {
+      float4_t* mine = xbuf(wave);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4)
-        mine[(i * 4 + j4) * 64 + lane] = (float4_t){res[4 + i][4 * j4], res[4 + i][4 * j4 + 1],
-                                                    res[4 + i][4 * j4 + 2], res[4 + i][4 * j4 + 3]};
-  }
-  __syncthreads();
-  {
-    const float4_t* other = xbuf(wave ^ 2);
+        for (int j4 = 0; j4 < 4; ++j4)
+          mine[(i * 4 + j4) * 64 + lane] = (float4_t){half_sum[send2 + i][4 * j4], half_sum[send2 + i][4 * j4 + 1],
+                                                      half_sum[send2 + i][4 * j4 + 2], half_sum[send2 + i][4 * j4 + 3]};
+    }
+    __syncthreads();
+    {
+      const float4_t* other = xbuf(wave ^ 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const float4_t v = other[(i * 4 + j4) * 64 + lane];
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const float4_t v = other[(i * 4 + j4) * 64 + lane];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) res[i][4 * j4 + e] += v[e];
-      }
+          for (int e = 0; e < 4; ++e) res[i][4 * j4 + e] = half_sum[keep2 + i][4 * j4 + e] + v[e];
+        }
+    }
+  };
+  switch (wave) {
+    case 0: reduce(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}); break;
+    case 1: reduce(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}); break;
+    case 2: reduce(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}); break;
+    default: reduce(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}); break;
   }
 
-  // this wave now holds the full result for column blocks col_block(wave, 0..3)
+  // this wave now holds the full result for column blocks colb/32 .. +3
+  const int colb = 128 * (2 * (wave & 1) + (wave >> 1));
   const float out_mul = p.kv_scale;  // FP8 rows: values carry kv_scale
   const int64_t H = p.H;
   {
-    const int col0 = 32 * col_block(wave, 0) + (lane & 31);
-    half_t* po = S > 1 ? p.part_o + ((tg * S + s) * kHG) * kLatent : nullptr;
+    // Stage the wave's [32 heads x 128 columns] in FP32 in the second half of
+    // its own exchange buffer (its partner read only the first half in round
+    // 2), then store 8 consecutive columns per lane (16-byte stores).  The
+    // column index is XOR-swizzled by bit 2 of the head so that the two head
+    // rows one store instruction writes fall in different banks.
+    float* stage = reinterpret_cast<float*>(xbuf(wave) + 1024);
+    const float mul = S > 1 ? 1.0f : out_mul;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int hd = c_head(j, lane);
-      const int head = g * kHG + hd;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int col = col0 + 32 * i;
-        if (S > 1) po[hd * kLatent + col] = (half_t)res[i][j];
-        else if (head < p.H) store_out<kBf16>(p.out, (t * H + head) * kLatent + col, res[i][j] * out_mul);
+      for (int j = 0; j < 16; ++j) {
+        const int hd = c_head(j, lane);
+        const int c = 32 * i + (lane & 31);
+        stage[hd * 128 + (c ^ (((hd >> 2) & 1) << 5))] = res[i][j] * mul;
       }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int e = lane + 64 * k, hd = e >> 4, cc = (e & 15) * 8;
+      const float* src = stage + hd * 128 + (cc ^ (((hd >> 2) & 1) << 5));
+      const float4_t a = *reinterpret_cast<const float4_t*>(src);
+      const float4_t b = *reinterpret_cast<const float4_t*>(src + 4);
+      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      const int head = g * kHG + hd;
+      if (S > 1) store8<false>(p.part_o + ((tg * S + s) * kHG + hd) * kLatent + colb + cc, v);
+      else if (head < p.H)
+        store8<kBf16>(reinterpret_cast<uint16_t*>(p.out) + (t * H + head) * kLatent + colb + cc, v);
     }
   }
   if (S == 1) return;
@@ -696,8 +763,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
         for (int i = 0; i < 8; ++i) a[i] += w * (float)v[i];
       }
 #pragma unroll
-      for (int i = 0; i < 8; i += 2)
-        store_out2<kBf16>(p.out, (t * H + head) * kLatent + c8 + i, a[i] * out_mul, a[i + 1] * out_mul);
+      for (int i = 0; i < 8; ++i) a[i] *= out_mul;
+      store8<kBf16>(reinterpret_cast<uint16_t*>(p.out) + (t * H + head) * kLatent + c8, a);
     }
   }
 }
