@@ -172,7 +172,8 @@ int mla_sparse_decode(const void* q, int q_dtype, int64_t num_tokens, int32_t nu
   p.bt_rows = block_table ? bt_rows : 0;
   p.bt_st = block_table ? bt_stride : 0;
   p.tok_seq = block_table ? token_seq : nullptr;
-  p.sm_log2 = sm_scale * 1.4426950408889634f * p.kv_scale;
+  p.sm_log2 = fabsf(sm_scale) * 1.4426950408889634f * p.kv_scale;
+  p.q_neg = sm_scale < 0.0f;
   p.out = out;
   p.lse = lse;
   const int64_t tg = num_tokens * G;

@@ -63,7 +63,9 @@ constexpr int kRowsT = 16;            // rows per tile (one wave)
 constexpr int kHG = 32;               // heads per workgroup
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kVRow = kLatent + 16;   // FP16 elements per V-buffer row (stride = 8 banks mod 64)
+// FP16 elements per V-buffer row: a 1072-byte stride puts the 16 rows one
+// row-wise 16-byte write instruction touches in distinct banks
+constexpr int kVRow = kLatent + 24;
 constexpr int kKSteps = 18;           // 576 key dimensions / 32
 constexpr float kLazy = 15.0f;        // P = 2^(s - reference) <= 2^15 stays inside FP16
 constexpr float kMargin = 5.0f;       // a new reference sits 2^5 above the max that set it
@@ -73,8 +75,8 @@ constexpr float kNegInf = -__builtin_huge_valf();
 enum { kFmtNvfp4 = 0, kFmtFp8 = 1 };
 
 constexpr int row_bytes(int fmt) { return fmt == kFmtNvfp4 ? kRowBytes : kFp8RowBytes; }
-// DMA instructions per tile: 16 rows in 16-byte pieces, 64 pieces per instruction
-constexpr int dma_instr(int fmt) { return (kRowsT * row_bytes(fmt) / 16 + 63) / 64; }
+// DMA instructions per tile: 4 pieces of 16 bytes of each of the 16 rows per instruction
+constexpr int dma_instr(int fmt) { return (row_bytes(fmt) / 16 + 3) / 4; }
 constexpr int slot_bytes(int fmt) { return dma_instr(fmt) * 1024; }
 // NVFP4: 3 slots (two tiles in flight while one is decoded); FP8 rows are
 // larger, so 2 slots and the refill is issued once a slot is in registers
@@ -100,15 +102,26 @@ __device__ __forceinline__ uint32_t lds_off(const void* p) {
 // the host pass from emitting the kernel's launch stub).
 #if defined(__HIP_DEVICE_COMPILE__)
 #define MLA_DEVICE_ASM(...) asm volatile(__VA_ARGS__)
-#define MLA_DMA16(src, lds) __builtin_amdgcn_global_load_lds((src), (lds), 16, 0, 0)
+// (the immediate offset is added to both the global and the LDS address)
+#define MLA_DMA16(src, lds, off) __builtin_amdgcn_global_load_lds((src), (lds), 16, (off), 0)
 #else
 #define MLA_DEVICE_ASM(...) __builtin_unreachable()
-#define MLA_DMA16(src, lds) ((void)(src), (void)(lds))
+#define MLA_DMA16(src, lds, off) ((void)(src), (void)(lds))
 #endif
 
+// f(integral_constant<int, J>) for J = I .. N-1
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <int kOff = 0>
 __device__ __forceinline__ u32x4 ring_b128(uint32_t a) {
   u32x4 v;
-  MLA_DEVICE_ASM("ds_read_b128 %0, %1" : "=v"(v) : "v"(a));
+  MLA_DEVICE_ASM("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(kOff));
   return v;
 }
 __device__ __forceinline__ u32x2 ring_b64(uint32_t a) {
@@ -116,52 +129,88 @@ __device__ __forceinline__ u32x2 ring_b64(uint32_t a) {
   MLA_DEVICE_ASM("ds_read_b64 %0, %1" : "=v"(v) : "v"(a));
   return v;
 }
+__device__ __forceinline__ uint32_t lds_b32(uint32_t a) {
+  uint32_t v;
+  MLA_DEVICE_ASM("ds_read_b32 %0, %1" : "=v"(v) : "v"(a));
+  return v;
+}
 
+// Ring slot layout (row-interleaved).  DMA instruction j of a tile moves
+// 16-byte piece 4j + c of tile row r from lane 16c + r, and an LDS-DMA
+// instruction writes its 64 lanes' pieces contiguously, so piece P of row r
+// sits at 1024 (P >> 2) + 256 (P & 3) + 16 r: the 16 rows' copies of one
+// piece are 256 contiguous bytes (no bank conflicts for the 16 lanes that
+// read them), and a lane's DMA source for every instruction is one row
+// address plus an immediate.
+//
 // The bytes lane (row, kg) reads from its row.
 template <int kFmt>
 struct Raw;
 template <>
 struct Raw<kFmtNvfp4> {
-  u32x4 l[4];     // 64 bytes of nibbles: latent dimensions [128kg, +128)
-  u32x2 sc;       // their 8 group scales
-  u32x4 rp;       // rope dimensions [16kg, +16)
+  u32x4 l[4];     // 64 bytes of nibbles: latent dimensions [128kg, +128) (pieces 4kg + c)
+  u32x2 sc;       // their 8 group scales (piece 16 + (kg >> 1), half kg & 1)
+  u32x4 rp;       // rope dimensions [16kg, +16) (piece 18 + kg)
 };
 template <>
 struct Raw<kFmtFp8> {
-  u32x4 l[8];     // 128 latent bytes
-  u32x4 rp;       // 16 rope bytes
+  u32x4 l[8];     // 128 latent bytes (pieces 8kg + c)
+  u32x4 rp;       // 16 rope bytes (piece 32 + kg)
+};
+
+// Per-lane ring offsets (within a slot) of the lane's pieces.
+template <int kFmt>
+struct RingOff {
+  uint32_t lat, sc, rope;
+  __device__ explicit RingOff(int r16, int kg) {
+    if constexpr (kFmt == kFmtNvfp4) {
+      lat = 1024 * kg + 16 * r16;
+      sc = 4096 + 256 * (kg >> 1) + 16 * r16 + 8 * (kg & 1);
+      rope = 4608 + 256 * kg + 16 * r16;
+    } else {
+      lat = 2048 * kg + 16 * r16;
+      sc = 0;
+      rope = 8192 + 256 * kg + 16 * r16;
+    }
+  }
 };
 
 // The row bytes are read in two parts so that the second half of the
 // latent (K-steps 8..15) occupies registers only from when it is decoded:
 // part A = latent K-steps 0..7, scales and rope; part B = latent K-steps
-// 8..15.  Each part waits for its own reads.
+// 8..15.  Each part waits for its own reads (and part A for `extra`, an LDS
+// read issued just before it).
 template <int kFmt>
-__device__ __forceinline__ void ring_read_a(Raw<kFmt>& r, uint32_t row_base, int kg) {
+__device__ __forceinline__ void ring_read_a(Raw<kFmt>& r, uint32_t slot, const RingOff<kFmt>& o,
+                                            uint32_t& extra) {
   if constexpr (kFmt == kFmtNvfp4) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) r.l[i] = ring_b128(row_base + 64 * kg + 16 * i);
-    r.sc = ring_b64(row_base + kScaleOff + 8 * kg);
-    r.rp = ring_b128(row_base + kRopeOff + 16 * kg);
-    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(r.l[0]), "+v"(r.l[1]), "+v"(r.sc), "+v"(r.rp));
+    r.l[0] = ring_b128<0>(slot + o.lat);
+    r.l[1] = ring_b128<256>(slot + o.lat);
+    r.sc = ring_b64(slot + o.sc);
+    r.rp = ring_b128(slot + o.rope);
+    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(r.l[0]), "+v"(r.l[1]), "+v"(r.sc), "+v"(r.rp), "+v"(extra));
   } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.l[i] = ring_b128(row_base + 128 * kg + 16 * i);
-    r.rp = ring_b128(row_base + kLatent + 16 * kg);
+    r.l[0] = ring_b128<0>(slot + o.lat);
+    r.l[1] = ring_b128<256>(slot + o.lat);
+    r.l[2] = ring_b128<512>(slot + o.lat);
+    r.l[3] = ring_b128<768>(slot + o.lat);
+    r.rp = ring_b128(slot + o.rope);
     MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)"
-                   : "+v"(r.l[0]), "+v"(r.l[1]), "+v"(r.l[2]), "+v"(r.l[3]), "+v"(r.rp));
+                   : "+v"(r.l[0]), "+v"(r.l[1]), "+v"(r.l[2]), "+v"(r.l[3]), "+v"(r.rp), "+v"(extra));
   }
 }
 
 template <int kFmt>
-__device__ __forceinline__ void ring_read_b(Raw<kFmt>& r, uint32_t row_base, int kg) {
+__device__ __forceinline__ void ring_read_b(Raw<kFmt>& r, uint32_t slot, const RingOff<kFmt>& o) {
   if constexpr (kFmt == kFmtNvfp4) {
-#pragma unroll
-    for (int i = 2; i < 4; ++i) r.l[i] = ring_b128(row_base + 64 * kg + 16 * i);
+    r.l[2] = ring_b128<512>(slot + o.lat);
+    r.l[3] = ring_b128<768>(slot + o.lat);
     MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(r.l[2]), "+v"(r.l[3]));
   } else {
-#pragma unroll
-    for (int i = 4; i < 8; ++i) r.l[i] = ring_b128(row_base + 128 * kg + 16 * i);
+    r.l[4] = ring_b128<1024>(slot + o.lat);
+    r.l[5] = ring_b128<1280>(slot + o.lat);
+    r.l[6] = ring_b128<1536>(slot + o.lat);
+    r.l[7] = ring_b128<1792>(slot + o.lat);
     MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(r.l[4]), "+v"(r.l[5]), "+v"(r.l[6]), "+v"(r.l[7]));
   }
 }
@@ -228,16 +277,16 @@ __device__ __forceinline__ uint32_t shfl_xor_u(uint32_t v, int m) {
 // 8) make one operand.  In assembly so that the compiler does not make them
 // wait for the ring's DMA; the memory clobber keeps the V-buffer writes that
 // follow in program order from moving above them.
-__device__ __forceinline__ void read_v4_group(u32x4 (&b)[4], uint32_t base, int q) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t a = base + 64 * (q + 4 * e);
-    (void)a;
+template <int kQ>
+__device__ __forceinline__ void read_v4_group(u32x4 (&b)[4], uint32_t base) {
+  static_for<0, 4>([&](auto E) {
+    constexpr int e = decltype(E)::value;
+    constexpr int off = 64 * (kQ + 4 * e);
     u32x2 lo, hi;
-    MLA_DEVICE_ASM("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a) : "memory");
-    MLA_DEVICE_ASM("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(a), "i"(8 * kVRow) : "memory");
+    MLA_DEVICE_ASM("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(base), "i"(off) : "memory");
+    MLA_DEVICE_ASM("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(base), "i"(off + 8 * kVRow) : "memory");
     b[e] = (u32x4){lo.x, lo.y, hi.x, hi.y};
-  }
+  });
 }
 
 __device__ __forceinline__ void lgkm_wait(u32x4 (&b)[4]) {
@@ -272,6 +321,35 @@ __device__ __forceinline__ float scale_acc(float x, float a) {
   return x;
 }
 
+// max of four MFMA results (v_max3; the compiler's fmaxf would first
+// canonicalise each input with another v_max)
+__device__ __forceinline__ float max4(float a, float b, float c, float d) {
+  float m;
+  MLA_DEVICE_ASM("v_max3_f32 %0, %1, %2, %3\n\tv_max_f32 %0, %0, %4" : "=&v"(m) : "v"(a), "v"(b), "v"(c), "v"(d));
+  return m;
+}
+
+// The two score MFMAs of a K-step (16x16x32, FP16 -> FP32), in assembly so
+// that their accumulators are VGPRs: the compiler gives every MFMA of the
+// kernel an AGPR accumulator, and the 256 AGPRs already hold O.  Hazards are
+// handled here: two wait states after the VALU write of the A operand
+// (the first instruction), accumulation chains back to back (the hardware
+// forwards a same-size accumulator), the first K-step of a tile starts from
+// the constant 0, and score_mfma_drain() waits out the MFMA latency before
+// VALU reads the scores.
+__device__ __forceinline__ void score_mfma2(float4_t (&acc)[2], const half8_t& a, const half8_t& b0,
+                                            const half8_t& b1, bool first) {
+  if (first)
+    MLA_DEVICE_ASM("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %2, %3, 0\n\tv_mfma_f32_16x16x32_f16 %1, %2, %4, 0"
+                   : "=&v"(acc[0]), "=&v"(acc[1]) : "v"(a), "v"(b0), "v"(b1));
+  else
+    MLA_DEVICE_ASM("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %2, %3, %0\n\tv_mfma_f32_16x16x32_f16 %1, %2, %4, %1"
+                   : "+v"(acc[0]), "+v"(acc[1]) : "v"(a), "v"(b0), "v"(b1));
+}
+__device__ __forceinline__ void score_mfma_drain(float4_t (&acc)[2]) {
+  MLA_DEVICE_ASM("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]));
+}
+
 // head of accumulator element j of `lane` in the 32x32 MFMA C layout
 __device__ __forceinline__ int c_head(int j, int lane) { return (j >> 2) * 8 + 4 * (lane >> 5) + (j & 3); }
 
@@ -283,7 +361,6 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   constexpr int kInstr = dma_instr(kFmt);
   constexpr int kSlot = slot_bytes(kFmt);
   constexpr int kDepth = ring_depth(kFmt);
-  constexpr int kPieces = kRowsT * (kRB / 16);  // 16-byte pieces per tile
 
   // The DMA target and the V buffers are separate arrays so that the
   // compiler can tell V-buffer accesses from DMA writes.  After the tile
@@ -356,6 +433,16 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
 #pragma unroll
     for (int i = 0; i < 2; ++i) qreg[hb][16 + i] = load_q8<kBf16>(qp + kLatent + 16 * kg + 8 * i);
   }
+  if (p.q_neg) {   // a negative softmax scale: flip q's signs (exact) so sm_log2 >= 0
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        u32x4 u = __builtin_bit_cast(u32x4, qreg[hb][ks]);
+        u ^= 0x80008000u;
+        qreg[hb][ks] = __builtin_bit_cast(half8_t, u);
+      }
+  }
 
   int rows8[8], pre8[8];
   {
@@ -409,30 +496,34 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   float mref[2];                          // reference of head hb*16 + r16 (base 2)
   float lsum[2];                          // this lane's share of that head's row sum
 
-  // DMA of this wave's k-th tile (split tile wave + 4k) into ring slot
-  // `slot`: instruction j moves pieces 64j + lane (piece = row * kRB/16 +
-  // 16-byte column), landing at slot + 16 * piece, so rows sit kRB apart.
-  // Pieces past the tile (padding of the last instruction) re-load piece 0
-  // into the slot's padding; rows past the split re-load the split's last
-  // row.  Both are real rows and are never used.
-  // Each lane's (row, 16-byte piece) of DMA instruction j is recomputed
-  // from the lane index at every issue (an opaque copy keeps the compiler
-  // from hoisting per-instruction addresses into registers).
-  auto issue = [&](int k, int slot) {
-    const int tile = wave + kWaves * k;
-    int ln = lane;
-    MLA_DEVICE_ASM("" : "+v"(ln));
-#pragma unroll
-    for (int j = 0; j < kInstr; ++j) {
-      int c = 64 * j + ln;
-      c = c < kPieces ? c : 0;
-      const int row = c / (kRB / 16), piece = c - row * (kRB / 16);
-      int i = tile * kRowsT + row;
-      i = i < n ? i : n - 1;
-      const uint8_t* src = p.cache + (int64_t)phys[r0 + i] * kRB + 16 * piece;
-      MLA_DMA16(src, ring + slot * kSlot + 1024 * j);
-    }
+  // DMA of one tile into ring slot `slot` (row-interleaved layout above):
+  // lane l moves pieces 4j + (l >> 4), j = 0 .. kInstr - 1, of the tile row
+  // l & 15 (= r16), whose cache row is `row`, so every source address is the
+  // lane's row address plus an immediate.  Rows past the split repeat the
+  // split's last row.  NVFP4 rows have 22 pieces: in the last instruction
+  // lanes 32..63 (pieces 22, 23) repeat pieces 20 and 21 of their row into
+  // positions that are never read.
+  const uint8_t* const lane_src = p.cache + 16 * kg;
+  const uint8_t* const lane_src_last = p.cache + 16 * (20 + (kg & 1));
+  auto issue = [&](uint32_t row, int slot) {
+    const uint8_t* const a = lane_src + (uint64_t)row * kRB;
+    uint8_t* const dst = ring + slot * kSlot;
+    // instruction j: source a + 64j, LDS dst + 1024j (the immediate 64j
+    // applies to both)
+    auto one = [&](auto J) {
+      constexpr int j = decltype(J)::value;
+      if constexpr (kFmt == kFmtNvfp4 && j == 5) MLA_DMA16(lane_src_last + (uint64_t)row * kRB, dst + 1024 * j, 0);
+      else MLA_DMA16(a, dst + (1024 - 64) * j, 64 * j);
+    };
+    static_for<0, kInstr>(one);
   };
+  // cache row of this lane's DMA row in the wave's k-th tile
+  auto tile_row_addr = [&](int k) -> uint32_t {
+    int i = (wave + kWaves * k) * kRowsT + r16;
+    i = i < n ? i : n - 1;
+    return lds_off(&phys[r0 + i]);
+  };
+  const RingOff<kFmt> ro(r16, kg);
 
   // V-buffer addresses: this lane's ds_read_b64_tr_b16 base for column
   // block 0 (block b is 64 bytes further) and its row for the V writes.
@@ -445,6 +536,13 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   // latent also into the V buffer), scores, softmax, then the values.  The
   // next two tiles' DMA is in flight throughout.
   //
+  // Software pipeline: the value MFMAs of tile k-1 run interleaved with the
+  // decode and score MFMAs of tile k, so the conversion work issues while
+  // the matrix core is busy.  Both use the one V buffer: value group j
+  // (column blocks j, j+4, j+8, j+12) reads tile k-1's V before latent
+  // K-steps 4j..4j+3 of tile k overwrite exactly those columns, and a wave's
+  // LDS operations execute in issue order.
+  //
   // Softmax reference (base 2): the first tile sets it to its max + kMargin
   // (P <= 2^-kMargin there); afterwards it moves only when a score exceeds
   // it by more than kLazy (P would leave FP16), one ballot deciding; then O
@@ -456,50 +554,61 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     for (int j = 0; j < 16; ++j) acc_o[nb][j] = 0.0f;
   mref[0] = mref[1] = kNegInf;
   lsum[0] = lsum[1] = 0.0f;
-  if (my_tiles > 0) {
-    issue(0, 0);
-    if (my_tiles > 1) issue(1, 1 % kDepth);
-  }
-  for (int k = 0; k < my_tiles; ++k) {
-    const int slot = k % kDepth;
-    // wait until only this wave's later tiles are in flight
+
+  Raw<kFmt> raw;
+  float4_t sacc[2];
+  uint32_t next_row = 0;
+  // wait for tile k's DMA and read part A of its rows (and the cache row of
+  // this lane's DMA row two tiles ahead)
+  auto tile_start = [&](int k) -> uint32_t {
     if (k + 1 < my_tiles) wait_vmcnt<kInstr>();
     else wait_vmcnt<0>();
-    Raw<kFmt> raw;
-    ring_read_a<kFmt>(raw, lds_off(ring + slot * kSlot + r16 * kRB), kg);
-    float4_t sacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-    for (int ks = 16; ks < kKSteps; ++ks) {   // rope first: its bytes are then dead
-      const half8_t kop = kstep8<kFmt>(raw, ks);
-      sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qreg[0][ks], sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qreg[1][ks], sacc[1], 0, 0, 0);
+    const uint32_t slot = lds_off(ring + (k % kDepth) * kSlot);
+    next_row = lds_b32(tile_row_addr(k + 2));
+    ring_read_a<kFmt>(raw, slot, ro, next_row);
+    return slot;
+  };
+  // one K-step of tile k's scores (latent K-steps also go to the V buffer)
+  auto score_step = [&](int k, int ks, uint32_t slot) {
+    if (ks == 8) {
+      ring_read_b<kFmt>(raw, slot, ro);
+      // the slot of tile k + 2 held tile k - 1 (3 slots) or tile k (2
+      // slots), both now in registers
+      if (k + 2 < my_tiles) issue(next_row, (k + 2) % kDepth);
     }
+    const half8_t kop = kstep8<kFmt>(raw, ks);
+    if (ks < 16) *reinterpret_cast<half8_t*>(vrow + 8 * ks) = kop;
+    score_mfma2(sacc, kop, qreg[0][ks], qreg[1][ks], ks == 16);
+  };
+  // value group j of the tile whose P is `pa` (its V is in the V buffer)
+  auto value_group = [&](const u32x4 (&bv)[4], const half8_t& pa, auto J) {
+    constexpr int j = decltype(J)::value;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      if (ks == 8) {
-        ring_read_b<kFmt>(raw, lds_off(ring + slot * kSlot + r16 * kRB), kg);
-        // the slot of tile k + 2 held tile k - 1 (3 slots) or tile k (2
-        // slots), both now in registers
-        if (k + 2 < my_tiles) issue(k + 2, (k + 2) % kDepth);
-      }
-      const half8_t kop = kstep8<kFmt>(raw, ks);
-      *reinterpret_cast<half8_t*>(vrow + 8 * ks) = kop;
-      sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qreg[0][ks], sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qreg[1][ks], sacc[1], 0, 0, 0);
-    }
-
-    // ---- softmax, base 2.  The lane holds rows 4kg + j (j = 0..3) of
-    // head hb*16 + r16.
+    for (int e = 0; e < 4; ++e)
+      acc_o[j + 4 * e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+          pa, __builtin_bit_cast(half8_t, bv[e]), acc_o[j + 4 * e], 0, 0, 0);
+  };
+  // Softmax of tile k (scores in sacc), first part: the reference.  Returns
+  // whether O must be rescaled by alpha_s before tile k's values are added.
+  // The lane holds rows 4kg + j (j = 0..3) of head hb*16 + r16; sm >= 0,
+  // so the scaled max is the max scaled.  Only the split's last tile can
+  // hold rows past its end; they get P = 0.
+  auto softmax_ref = [&](int k) -> bool {
     const int row0 = (wave + kWaves * k) * kRowsT + 4 * kg;
-    float sv[2][4], tmax[2];
+    const bool ragged = (wave + kWaves * k + 1) * kRowsT > n;
+    score_mfma_drain(sacc);
+    float tmax[2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      tmax[hb] = kNegInf;
+      float m = max4(sacc[hb][0], sacc[hb][1], sacc[hb][2], sacc[hb][3]);
+      if (ragged) {
+        m = kNegInf;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sv[hb][j] = (row0 + j < n) ? sacc[hb][j] * sm : kNegInf;
-        tmax[hb] = __builtin_fmaxf(tmax[hb], sv[hb][j]);
+        for (int j = 0; j < 4; ++j)
+          if (row0 + j < n) m = __builtin_fmaxf(m, sacc[hb][j]);
       }
+      // (-inf * 0 is NaN; the max with -inf maps it back to -inf)
+      tmax[hb] = __builtin_fmaxf(m * sm, kNegInf);
     }
     const bool first = k == 0;
     const bool raise = tmax[0] > mref[0] + kLazy || tmax[1] > mref[1] + kLazy;
@@ -515,58 +624,119 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
         mref[hb] = mnew;
         if (kg == 0) alpha_s[wave][hb * 16 + r16] = al;
       }
-      if (!first) {
-        // Rescale O in place (the value MFMAs of the previous tile issued
-        // long before; LDS keeps this wave's order for alpha_s).
-        MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float al = alpha_s[wave][c_head(j, lane)];
-#pragma unroll
-          for (int nb = 0; nb < 16; ++nb) acc_o[nb][j] = scale_acc(acc_o[nb][j], al);
-        }
-      }
+      return !first;
     }
-    half_t ph[2][4];
+    return false;
+  };
+  // second part: P of tile k against the reference, as the value MFMA's A
+  // operand
+  auto softmax_p = [&](int k) -> half8_t {
+    const int row0 = (wave + kWaves * k) * kRowsT + 4 * kg;
+    const bool ragged = (wave + kWaves * k + 1) * kRowsT > n;
+    float pv[2][4];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
+      const float nm = -mref[hb];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float pv = __builtin_amdgcn_exp2f(sv[hb][j] - mref[hb]);
-        lsum[hb] += pv;
-        ph[hb][j] = (half_t)pv;
+      for (int j = 0; j < 4; ++j) pv[hb][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[hb][j], sm, nm));
+      if (ragged) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (row0 + j >= n) pv[hb][j] = 0.0f;
       }
-    }
-    // A operand of the value MFMA: lane L = head (L & 31) x rows
-    // 8(L >> 5) + [0,8).  Lane (r16, kg) holds rows 4kg..4kg+3 of heads
-    // r16 and 16 + r16; it keeps the head block kg & 1 and swaps the other
-    // with lane ^ 16, which holds the neighbouring 4 rows.
-    const int keep = kg & 1;
-    const half4_t mine = keep ? (half4_t){ph[1][0], ph[1][1], ph[1][2], ph[1][3]}
-                              : (half4_t){ph[0][0], ph[0][1], ph[0][2], ph[0][3]};
-    const half4_t give = keep ? (half4_t){ph[0][0], ph[0][1], ph[0][2], ph[0][3]}
-                              : (half4_t){ph[1][0], ph[1][1], ph[1][2], ph[1][3]};
-    const u32x2 gv = __builtin_bit_cast(u32x2, give);
-    const u32x2 rv = {shfl_xor_u(gv.x, 16), shfl_xor_u(gv.y, 16)};
-    const half4_t other = __builtin_bit_cast(half4_t, rv);
-    const half8_t pa = keep ? (half8_t){other.x, other.y, other.z, other.w, mine.x, mine.y, mine.z, mine.w}
-                            : (half8_t){mine.x, mine.y, mine.z, mine.w, other.x, other.y, other.z, other.w};
-
-    // ---- values: O += P . V, V read in groups of 4 column blocks, the
-    // next group's reads in flight while this group's MFMAs run
-    u32x4 bv[2][4];
-    read_v4_group(bv[0], vb, 0);
-    lgkm_wait(bv[0]);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (q < 3) read_v4_group(bv[(q + 1) & 1], vb, q + 1);
+      for (int j = 0; j < 4; ++j) lsum[hb] += pv[hb][j];
+    }
+    // A operand of the value MFMA: lane L = head block (L >> 4) & 1, head
+    // L & 15, rows 8(L >> 5) + [0,8).  d[hb][x] = P of head hb*16 + r16,
+    // rows 4kg + 2x, +1 (FP16 pair).  permlane16_swap exchanges the odd
+    // 16-lane rows of its first operand with the even rows of its second;
+    // afterwards d[0] holds rows 8(kg >> 1) + [0,4) and d[1] rows + [4,8) of
+    // head block kg & 1 (the lane ^ 16 neighbour holds the other 4 rows).
+    uint32_t d[2][2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        d[hb][x] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                                    (float2_t){pv[hb][2 * x], pv[hb][2 * x + 1]}, half2_t));
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const auto sw = __builtin_amdgcn_permlane16_swap(d[0][x], d[1][x], false, false);
+      d[0][x] = sw[0];
+      d[1][x] = sw[1];
+    }
+    return __builtin_bit_cast(half8_t, (u32x4){d[0][0], d[0][1], d[1][0], d[1][1]});
+  };
+
+  if (my_tiles > 0) {
+    issue((uint32_t)phys[r0 + min(wave * kRowsT + r16, n - 1)], 0);
+    if (my_tiles > 1) issue((uint32_t)phys[r0 + min((wave + kWaves) * kRowsT + r16, n - 1)], 1 % kDepth);
+
+    // tile 0: scores only
+    {
+      const uint32_t slot = tile_start(0);
+#pragma unroll
+      for (int ks = 16; ks < kKSteps; ++ks) score_step(0, ks, slot);   // rope first: its bytes are then dead
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) score_step(0, ks, slot);
+    }
+    (void)softmax_ref(0);
+    half8_t pa = softmax_p(0);
+
+    // tiles 1 .. my_tiles-1: values of tile k-1 with the scores of tile k.
+    // A raised reference rescales O lazily: each value group first scales
+    // its four column blocks (the register allocator keeps O in place only
+    // when every rescale sits next to the MFMAs that consume it).
+    bool pending = false;   // O is still to be rescaled by alv before its next value MFMA
+    float16_t alv = {};     // the rescale factors of this lane's 16 accumulator rows
+    auto rescale_group = [&](auto J) {
+      constexpr int j = decltype(J)::value;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        acc_o[q + 4 * e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            pa, __builtin_bit_cast(half8_t, bv[q & 1][e]), acc_o[q + 4 * e], 0, 0, 0);
-      if (q < 3) lgkm_wait(bv[(q + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc_o[j + 4 * e][i] = scale_acc(acc_o[j + 4 * e][i], alv[i]);
+    };
+    for (int k = 1; k < my_tiles; ++k) {
+      const uint32_t slot = tile_start(k);
+#pragma unroll
+      for (int ks = 16; ks < kKSteps; ++ks) score_step(k, ks, slot);
+      static_for<0, 4>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        u32x4 bv[4];
+        read_v4_group<j>(bv, vb);   // tile k-1's V, read before K-steps 4j.. overwrite it
+        score_step(k, 4 * j, slot);
+        if (pending) rescale_group(J);
+        lgkm_wait(bv);
+        // one value MFMA (32 cycles) per K-step: the next K-step's
+        // conversions issue while it runs
+        static_for<0, 4>([&](auto E) {
+          constexpr int e = decltype(E)::value;
+          __builtin_amdgcn_sched_barrier(0);
+          acc_o[j + 4 * e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              pa, __builtin_bit_cast(half8_t, bv[e]), acc_o[j + 4 * e], 0, 0, 0);
+          if constexpr (e < 3) score_step(k, 4 * j + e + 1, slot);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      pending = softmax_ref(k);
+      if (pending) {   // (LDS keeps this wave's order for alpha_s)
+        MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < 16; ++i) alv[i] = alpha_s[wave][c_head(i, lane)];
+      }
+      pa = softmax_p(k);
     }
-    MLA_DEVICE_ASM("" ::: "memory");   // the next tile's V-buffer writes stay below the reads
+
+    // values of the last tile
+    static_for<0, 4>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      u32x4 bv[4];
+      read_v4_group<j>(bv, vb);
+      if (pending) rescale_group(J);
+      lgkm_wait(bv);
+      value_group(bv, pa, J);
+    });
   }
   wait_vmcnt<0>();   // no DMA may still be writing this workgroup's LDS
 

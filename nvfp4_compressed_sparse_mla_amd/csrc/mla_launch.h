@@ -35,7 +35,8 @@ struct DecodeParams {
   int bs, bt_rows, bt_cols;
   int64_t bt_st;
   const int32_t* tok_seq;
-  float sm_log2;            // sm_scale * log2(e) * kv_scale
+  float sm_log2;            // |sm_scale| * log2(e) * kv_scale (>= 0)
+  int q_neg;                // sm_scale < 0: q is negated on load (exact), so sm_log2 >= 0
   void* out;
   float* lse;
   uint32_t* counters;       // [T*G] arrivals per (token, head group)

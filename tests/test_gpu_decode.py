@@ -75,6 +75,17 @@ def test_ragged_tiles_and_tails(topk, valid):
     _check(w, cache, out, lse, what=f"topk{topk}")
 
 
+@pytest.mark.parametrize("scale", [-1.0 / 24.0, 0.0, 0.2])
+def test_softmax_scale_sign_and_zero(scale):
+    # a negative scale is handled by flipping q's signs; zero gives uniform
+    # weights over the valid rows (also in a ragged last tile)
+    w = make_custom(3000, 3, 32, 300, seed=5, device=DEV, valid_per_token=[300, 77, 1])
+    w.sm_scale = scale
+    cache = _fill(w)
+    out, lse = _run(w, cache)
+    _check(w, cache, out, lse, what=f"scale{scale:+.3f}")
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 16, 64])
 def test_split_count_invariance(splits):
     w = make_custom(5000, 4, 32, 2048, seed=11, device=DEV, valid_per_token=[2048, 1500, 90, 0])
