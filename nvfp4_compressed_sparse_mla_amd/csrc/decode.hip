@@ -200,6 +200,29 @@ __device__ __forceinline__ void ring_read_a(Raw<kFmt>& r, uint32_t slot, const R
   }
 }
 
+// part B issued without a wait (the caller's next lgkmcnt(0) wait covers it
+// and names these registers)
+template <int kFmt>
+__device__ __forceinline__ void ring_issue_b(Raw<kFmt>& r, uint32_t slot, const RingOff<kFmt>& o) {
+  if constexpr (kFmt == kFmtNvfp4) {
+    r.l[2] = ring_b128<512>(slot + o.lat);
+    r.l[3] = ring_b128<768>(slot + o.lat);
+  } else {
+    r.l[4] = ring_b128<1024>(slot + o.lat);
+    r.l[5] = ring_b128<1280>(slot + o.lat);
+    r.l[6] = ring_b128<1536>(slot + o.lat);
+    r.l[7] = ring_b128<1792>(slot + o.lat);
+  }
+}
+template <int kFmt>
+__device__ __forceinline__ void lgkm_wait_b(u32x4 (&b)[4], Raw<kFmt>& r) {
+  if constexpr (kFmt == kFmtNvfp4)
+    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(r.l[2]), "+v"(r.l[3]));
+  else
+    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)"
+                   : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(r.l[4]), "+v"(r.l[5]), "+v"(r.l[6]), "+v"(r.l[7]));
+}
+
 template <int kFmt>
 __device__ __forceinline__ void ring_read_b(Raw<kFmt>& r, uint32_t slot, const RingOff<kFmt>& o) {
   if constexpr (kFmt == kFmtNvfp4) {
@@ -233,6 +256,55 @@ __device__ __forceinline__ half8_t kstep8(const Raw<kFmt>& r, int ks) {
     const int o = 2 * (ks - 16);
     return e4m3x8_to_half8_hw(r.rp[o], r.rp[o + 1]);
   }
+}
+
+// A latent K-step's A operand decoded in two parts so that the conversion
+// work can be placed between MFMAs: part 1 = the conversions and half of
+// the scale multiplies, part 2 = the rest.  `sh` holds the lane's 8 group
+// scales as FP16 (group g = half g & 1 of sh[g >> 1]).
+struct KDec {
+  half2_t c[4];
+};
+template <int kFmt>
+__device__ __forceinline__ void kdec_part1(KDec& d, const Raw<kFmt>& r, const half2_t (&sh)[4], int ks) {
+  if constexpr (kFmt == kFmtNvfp4) {
+    const uint32_t w = r.l[ks >> 2][ks & 3];
+    const half2_t s2 = sh[ks >> 2];
+    const half_t sv = ((ks >> 1) & 1) ? s2.y : s2.x;
+    const half2_t s = {sv, sv};
+    d.c[0] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0));
+    d.c[1] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
+    d.c[2] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
+    d.c[3] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
+    d.c[0] *= s;
+    d.c[1] *= s;
+  } else {
+    const uint32_t w = r.l[ks >> 1][2 * (ks & 1)];
+    d.c[0] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+    d.c[1] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+  }
+}
+template <int kFmt>
+__device__ __forceinline__ half8_t kdec_part2(KDec& d, const Raw<kFmt>& r, const half2_t (&sh)[4], int ks) {
+  if constexpr (kFmt == kFmtNvfp4) {
+    const half2_t s2 = sh[ks >> 2];
+    const half_t sv = ((ks >> 1) & 1) ? s2.y : s2.x;
+    const half2_t s = {sv, sv};
+    d.c[2] *= s;
+    d.c[3] *= s;
+  } else {
+    const uint32_t w = r.l[ks >> 1][2 * (ks & 1) + 1];
+    d.c[2] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+    d.c[3] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+  }
+  return (half8_t){d.c[0].x, d.c[0].y, d.c[1].x, d.c[1].y, d.c[2].x, d.c[2].y, d.c[3].x, d.c[3].y};
+}
+// the lane's 8 NVFP4 group scales as FP16 pairs
+__device__ __forceinline__ void group_scales(half2_t (&sh)[4], const u32x2& sc) {
+  sh[0] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[0], 1.0f, false));
+  sh[1] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[0], 1.0f, true));
+  sh[2] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[1], 1.0f, false));
+  sh[3] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[1], 1.0f, true));
 }
 
 template <bool kBf16>
@@ -345,6 +417,11 @@ __device__ __forceinline__ void score_mfma2(float4_t (&acc)[2], const half8_t& a
   else
     MLA_DEVICE_ASM("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %2, %3, %0\n\tv_mfma_f32_16x16x32_f16 %1, %2, %4, %1"
                    : "+v"(acc[0]), "+v"(acc[1]) : "v"(a), "v"(b0), "v"(b1));
+}
+// one score MFMA of the software-pipelined loop (its A operand was written
+// at least a slot earlier, so no wait states are needed)
+__device__ __forceinline__ void score_mfma1(float4_t& acc, const half8_t& a, const half8_t& b) {
+  MLA_DEVICE_ASM("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void score_mfma_drain(float4_t (&acc)[2]) {
   MLA_DEVICE_ASM("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]));
@@ -699,23 +776,61 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     };
     for (int k = 1; k < my_tiles; ++k) {
       const uint32_t slot = tile_start(k);
+      half2_t sh[4];
+      if constexpr (kFmt == kFmtNvfp4) group_scales(sh, raw.sc);
 #pragma unroll
-      for (int ks = 16; ks < kKSteps; ++ks) score_step(k, ks, slot);
+      for (int ks = 16; ks < kKSteps; ++ks) {   // rope
+        const half8_t kop = kstep8<kFmt>(raw, ks);
+        score_mfma2(sacc, kop, qreg[0][ks], qreg[1][ks], ks == 16);
+      }
+      // Slot t (latent K-step t): the value MFMA of one column block of
+      // tile k-1, the conversions of K-step t+1 split around the two score
+      // MFMAs of K-step t, then the V write of K-step t+1.  The order is
+      // pinned (sched_barrier) so that every conversion issues while an MFMA
+      // runs.
+      half8_t kop;
+      {
+        KDec d;
+        kdec_part1<kFmt>(d, raw, sh, 0);
+        kop = kdec_part2<kFmt>(d, raw, sh, 0);
+      }
+      // value groups read one unit ahead (two buffers): group j + 1 is read
+      // during unit j, before K-step 4(j+1) overwrites it at unit j + 1
+      u32x4 bvb[2][4];
+      read_v4_group<0>(bvb[0], vb);
+      ring_issue_b<kFmt>(raw, slot, ro);   // latent K-steps 8..15, waited for with group 1
+      // the slot of tile k + 2 held tile k - 1 (3 slots) or tile k (2 slots),
+      // both now in registers
+      if (k + 2 < my_tiles) issue(next_row, (k + 2) % kDepth);
       static_for<0, 4>([&](auto J) {
         constexpr int j = decltype(J)::value;
-        u32x4 bv[4];
-        read_v4_group<j>(bv, vb);   // tile k-1's V, read before K-steps 4j.. overwrite it
-        score_step(k, 4 * j, slot);
+        u32x4 (&bv)[4] = bvb[j & 1];
+        if constexpr (j == 1) lgkm_wait_b<kFmt>(bv, raw);
+        else lgkm_wait(bv);
+        if constexpr (j < 3) read_v4_group<j + 1>(bvb[(j + 1) & 1], vb);
+        *reinterpret_cast<half8_t*>(vrow + 8 * (4 * j)) = kop;   // after group j's reads
         if (pending) rescale_group(J);
-        lgkm_wait(bv);
-        // one value MFMA (32 cycles) per K-step: the next K-step's
-        // conversions issue while it runs
         static_for<0, 4>([&](auto E) {
           constexpr int e = decltype(E)::value;
+          constexpr int t = 4 * j + e;
+          KDec d;
           __builtin_amdgcn_sched_barrier(0);
           acc_o[j + 4 * e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
               pa, __builtin_bit_cast(half8_t, bv[e]), acc_o[j + 4 * e], 0, 0, 0);
-          if constexpr (e < 3) score_step(k, 4 * j + e + 1, slot);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (t < 15) kdec_part1<kFmt>(d, raw, sh, t + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          score_mfma1(sacc[0], kop, qreg[0][t]);
+          __builtin_amdgcn_sched_barrier(0);
+          half8_t nx;
+          if constexpr (t < 15) nx = kdec_part2<kFmt>(d, raw, sh, t + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          score_mfma1(sacc[1], kop, qreg[1][t]);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (t < 15) {
+            kop = nx;
+            if constexpr ((t + 1) % 4 != 0) *reinterpret_cast<half8_t*>(vrow + 8 * (t + 1)) = kop;
+          }
         });
         __builtin_amdgcn_sched_barrier(0);
       });
