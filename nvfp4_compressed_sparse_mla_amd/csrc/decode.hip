@@ -338,6 +338,18 @@ __device__ __forceinline__ void store8(T* dst, const float (&v)[8]) {
   *reinterpret_cast<u32x4*>(dst) = w;
 }
 
+// Split partials cross workgroups (and L2 caches): they are written with
+// agent-scope atomic stores, which write through this XCD's L2, so the
+// writer needs no L2-wide writeback before counting its arrival.
+__device__ __forceinline__ void store8_agent(half_t* dst, const float (&v)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = as_u32((half2_t){(half_t)v[2 * i], (half_t)v[2 * i + 1]});
+  uint64_t* d = reinterpret_cast<uint64_t*>(dst);
+  __hip_atomic_store(d, (uint64_t)w[0] | ((uint64_t)w[1] << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(d + 1, (uint64_t)w[2] | ((uint64_t)w[3] << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ __forceinline__ uint32_t shfl_xor_u(uint32_t v, int m) {
   return (uint32_t)__shfl_xor((int)v, m, 64);
@@ -887,7 +899,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     if (w == 0) {
       const float lse2 = L > 0.0f ? M + __log2f(L) : kNegInf;
       const int head = g * kHG + hd;
-      if (S > 1) p.part_lse[(tg * S + s) * kHG + hd] = lse2;
+      if (S > 1) __hip_atomic_store(p.part_lse + (tg * S + s) * kHG + hd, lse2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else if (head < p.H && p.lse) p.lse[t * p.H + head] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
     }
   }
@@ -994,22 +1006,25 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
       const float4_t b = *reinterpret_cast<const float4_t*>(src + 4);
       const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
       const int head = g * kHG + hd;
-      if (S > 1) store8<false>(p.part_o + ((tg * S + s) * kHG + hd) * kLatent + colb + cc, v);
+      if (S > 1) store8_agent(p.part_o + ((tg * S + s) * kHG + hd) * kLatent + colb + cc, v);
       else if (head < p.H)
         store8<kBf16>(reinterpret_cast<uint16_t*>(p.out) + (t * H + head) * kLatent + colb + cc, v);
     }
   }
   if (S == 1) return;
 
-  // publish the partial (one release after the barrier has ordered every
-  // wave's stores before it) and count arrivals; the last arrival merges
+  // Count arrivals once every wave's partial stores are complete (each wave
+  // waits for its own; the barrier orders them before the count); the last
+  // arrival merges.
+  MLA_DEVICE_ASM("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   uint32_t* ctr = p.counters + tg;
   if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int last = old == (uint32_t)S - 1u;
     if (last) {
+      // the partials were written through (agent-scope stores) before their
+      // counts; invalidate this XCD's caches so that plain loads see them
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
     }
@@ -1018,38 +1033,60 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   __syncthreads();
   if (!last_s) return;
 
-  // merge weights per (split, head)
-  float* wsh = reinterpret_cast<float*>(ring_all);
+  // merge weights per (split, head): every split's log2-sum-exp into LDS
+  // first (one round of loads), then one thread per head
+  float* lse_sh = reinterpret_cast<float*>(ring_all);   // [S][32]
+  float* wsh = lse_sh + 64 * kHG;                        // [S][32]
+  for (int i = tid; i < S * kHG; i += kThreads)
+    lse_sh[i] = p.part_lse[tg * S * kHG + i];
+  __syncthreads();
   if (tid < kHG) {
-    const float* pl = p.part_lse + tg * S * kHG + tid;
     float mx = kNegInf;
-    for (int ss = 0; ss < S; ++ss) mx = __builtin_fmaxf(mx, pl[ss * kHG]);
+    for (int ss = 0; ss < S; ++ss) mx = __builtin_fmaxf(mx, lse_sh[ss * kHG + tid]);
     float sum = 0.0f;
     if (mx != kNegInf)
-      for (int ss = 0; ss < S; ++ss) sum += __builtin_amdgcn_exp2f(pl[ss * kHG] - mx);
+      for (int ss = 0; ss < S; ++ss) sum += __builtin_amdgcn_exp2f(lse_sh[ss * kHG + tid] - mx);
+    const float inv = mx != kNegInf ? 1.0f / sum : 0.0f;
     for (int ss = 0; ss < S; ++ss)
-      wsh[ss * kHG + tid] = mx != kNegInf ? __builtin_amdgcn_exp2f(pl[ss * kHG] - mx) / sum : 0.0f;
+      wsh[ss * kHG + tid] = mx != kNegInf ? __builtin_amdgcn_exp2f(lse_sh[ss * kHG + tid] - mx) * inv : 0.0f;
     const int head = g * kHG + tid;
     if (head < p.H && p.lse) p.lse[t * H + head] = mx != kNegInf ? (mx + __log2f(sum)) * kLn2 : kNegInf;
   }
   __syncthreads();
   {
-    // 8 consecutive columns per work item: 32 heads x 64 chunks
-    const half_t* pp = p.part_o + (tg * S) * kHG * kLatent;
-    for (int e = tid; e < kHG * (kLatent / 8); e += kThreads) {
-      const int hd = e >> 6, c8 = 8 * (e & 63);
-      const int head = g * kHG + hd;
-      if (head >= p.H) continue;
-      float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int ss = 0; ss < S; ++ss) {
-        const float w = wsh[ss * kHG + hd];
-        const half8_t v = *reinterpret_cast<const half8_t*>(pp + (ss * kHG + hd) * kLatent + c8);
+    // 8 consecutive columns per chunk, 32 heads x 64 chunks: chunk
+    // tid + 256 m (m = 0..7) is head (tid >> 6) + 4 m, columns 8 (tid & 63).
+    // Two splits' 16-byte loads (16 per thread) are in flight together; an
+    // odd S re-loads split 0 with weight 0.
+    const half_t* pp = p.part_o + (tg * S) * kHG * kLatent + (tid >> 6) * kLatent + 8 * (tid & 63);
+    float a[8][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] += w * (float)v[i];
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[m][i] = 0.0f;
+    for (int s0 = 0; s0 < S; s0 += 2) {
+      const int s1 = s0 + 1 < S ? s0 + 1 : 0;
+      half8_t v0[8], v1[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        v0[m] = *reinterpret_cast<const half8_t*>(pp + (s0 * kHG + 4 * m) * kLatent);
+        v1[m] = *reinterpret_cast<const half8_t*>(pp + (s1 * kHG + 4 * m) * kLatent);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a[i] *= out_mul;
-      store8<kBf16>(reinterpret_cast<uint16_t*>(p.out) + (t * H + head) * kLatent + c8, a);
+      for (int m = 0; m < 8; ++m) {
+        const float w0 = wsh[s0 * kHG + (tid >> 6) + 4 * m];
+        const float w1 = s0 + 1 < S ? wsh[s1 * kHG + (tid >> 6) + 4 * m] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[m][i] += w0 * (float)v0[m][i] + w1 * (float)v1[m][i];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int hd = (tid >> 6) + 4 * m, head = g * kHG + hd;
+      if (head >= p.H) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[m][i] *= out_mul;
+      store8<kBf16>(reinterpret_cast<uint16_t*>(p.out) + (t * H + head) * kLatent + 8 * (tid & 63), a[m]);
     }
   }
 }
