@@ -507,30 +507,21 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   }
 
   // ---------------------------------------------------------------- q
-  // B operand of K-step ks for head block hb: q[head][d] with
-  // d(ks < 16) = 128kg + 8ks + [0,8) and d(16 + i) = 512 + 16kg + 8i + [0,8)
-  // (With 16 heads the second head block repeats head 15: straight-line
-  // loads keep the compiler's load counting exact, and those lanes' results
-  // are never stored.)
-  half8_t qreg[2][kKSteps];
+  // q of the workgroup's 32 heads is loaded once, 9 coalesced 16-byte chunks
+  // per thread (chunk c: head c / 72, dimensions 8 (c % 72) + [0,8); heads
+  // past H repeat the last one), and later staged through the still idle V
+  // buffer, from where each wave reads the B operands of its score MFMAs.
+  constexpr int kQChunks = kHG * (kQK / 8) / kThreads;   // 9
+  half8_t qstage[kQChunks];
+  half8_t qreg[2][kKSteps];   // filled once the rows' DMA is issued (see below)
+  {
+    const uint16_t* qt = reinterpret_cast<const uint16_t*>(p.q) + t * p.q_st;
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const int head = min(g * kHG + hb * 16 + r16, p.H - 1);
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + t * p.q_st + (int64_t)head * p.q_sh;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qreg[hb][ks] = load_q8<kBf16>(qp + 128 * kg + 8 * ks);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) qreg[hb][16 + i] = load_q8<kBf16>(qp + kLatent + 16 * kg + 8 * i);
-  }
-  if (p.q_neg) {   // a negative softmax scale: flip q's signs (exact) so sm_log2 >= 0
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) {
-        u32x4 u = __builtin_bit_cast(u32x4, qreg[hb][ks]);
-        u ^= 0x80008000u;
-        qreg[hb][ks] = __builtin_bit_cast(half8_t, u);
-      }
+    for (int m = 0; m < kQChunks; ++m) {
+      const int c = tid + kThreads * m, h = c / (kQK / 8), dc = c - h * (kQK / 8);
+      const int head = min(g * kHG + h, p.H - 1);
+      qstage[m] = load_q8<kBf16>(qt + (int64_t)head * p.q_sh + 8 * dc);
+    }
   }
 
   int rows8[8], pre8[8];
@@ -761,6 +752,38 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   if (my_tiles > 0) {
     issue((uint32_t)phys[r0 + min(wave * kRowsT + r16, n - 1)], 0);
     if (my_tiles > 1) issue((uint32_t)phys[r0 + min((wave + kWaves) * kRowsT + r16, n - 1)], 1 % kDepth);
+  }
+  // q into LDS in B-operand order, then into registers (while the first
+  // tiles' DMA is in flight).  B operand of K-step ks for head block hb,
+  // lane (r16, kg): q[hb*16 + r16][d] with d(ks < 16) = 128kg + 8ks + [0,8)
+  // and d(16 + i) = 512 + 16kg + 8i + [0,8), at 16-byte slot
+  // (hb * 18 + ks) * 64 + 16kg + r16.  A negative softmax scale flips q's
+  // signs here (exact), so sm_log2 >= 0.
+  {
+    u32x4* qs = reinterpret_cast<u32x4*>(vbuf_all);
+#pragma unroll
+    for (int m = 0; m < kQChunks; ++m) {
+      const int c = tid + kThreads * m, h = c / (kQK / 8), d = 8 * (c - h * (kQK / 8));
+      int kgq, ks;
+      if (d < kLatent) {
+        kgq = d >> 7;
+        ks = (d >> 3) & 15;
+      } else {
+        kgq = (d - kLatent) >> 4;
+        ks = 16 + (((d - kLatent) >> 3) & 1);
+      }
+      u32x4 u = __builtin_bit_cast(u32x4, qstage[m]);
+      if (p.q_neg) u ^= 0x80008000u;
+      qs[((h >> 4) * kKSteps + ks) * 64 + 16 * kgq + (h & 15)] = u;
+    }
+    lds_barrier();   // (not __syncthreads: that would also wait for the tiles' DMA)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) qreg[hb][ks] = __builtin_bit_cast(half8_t, qs[(hb * kKSteps + ks) * 64 + lane]);
+    lds_barrier();   // every wave has its q before the V buffer is written
+  }
+  if (my_tiles > 0) {
 
     // tile 0: scores only
     {
