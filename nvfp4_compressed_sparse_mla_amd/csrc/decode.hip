@@ -1056,12 +1056,51 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   __syncthreads();
   if (!last_s) return;
 
-  // merge weights per (split, head): every split's log2-sum-exp into LDS
-  // first (one round of loads), then one thread per head
+  // Chunks of 8 consecutive columns, 32 heads x 64 chunks: chunk tid + 256 m
+  // (m = 0..7) is head (tid >> 6) + 4 m, columns 8 (tid & 63).  Splits are
+  // summed in index order, two per round, and the next round's 16-byte
+  // loads are in flight while a round is summed (an odd count adds split s0
+  // again with weight 0).  The log2-sum-exps are loaded first (lane x of
+  // wave 0 reads split x's), then the first round's partials, so that the
+  // merge weights wait only for the former.
   float* lse_sh = reinterpret_cast<float*>(ring_all);   // [S][32]
   float* wsh = lse_sh + 64 * kHG;                        // [S][32]
-  for (int i = tid; i < S * kHG; i += kThreads)
-    lse_sh[i] = p.part_lse[tg * S * kHG + i];
+  const int cc = 8 * (tid & 63);
+  const half_t* pp = p.part_o + (tg * S) * kHG * kLatent + (tid >> 6) * kLatent + cc;
+  auto load_split = [&](int x, half8_t (&v)[8]) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) v[m] = *reinterpret_cast<const half8_t*>(pp + (x * kHG + 4 * m) * kLatent);
+  };
+  float a[8][8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[m][i] = 0.0f;
+  auto add_pair = [&](const half8_t (&v0)[8], const half8_t (&v1)[8], int s0) {
+    const bool has1 = s0 + 1 < S;
+    const int s1 = has1 ? s0 + 1 : s0;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const float w0 = wsh[s0 * kHG + (tid >> 6) + 4 * m];
+      const float w1 = has1 ? wsh[s1 * kHG + (tid >> 6) + 4 * m] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[m][i] += w0 * (float)v0[m][i] + w1 * (float)v1[m][i];
+    }
+  };
+  half8_t A0[8], A1[8], B0[8], B1[8];
+  float4_t lx[8];
+  if (wave == 0) {
+    const float4_t* src = reinterpret_cast<const float4_t*>(p.part_lse + (tg * S + (lane < S ? lane : 0)) * kHG);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lx[i] = src[i];
+  }
+  load_split(0, A0);
+  load_split(1 < S ? 1 : 0, A1);
+  if (wave == 0 && lane < S) {
+    float4_t* dst = reinterpret_cast<float4_t*>(lse_sh + lane * kHG);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = lx[i];
+  }
   __syncthreads();
   if (tid < kHG) {
     float mx = kNegInf;
@@ -1076,41 +1115,29 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     if (head < p.H && p.lse) p.lse[t * H + head] = mx != kNegInf ? (mx + __log2f(sum)) * kLn2 : kNegInf;
   }
   __syncthreads();
-  {
-    // 8 consecutive columns per chunk, 32 heads x 64 chunks: chunk
-    // tid + 256 m (m = 0..7) is head (tid >> 6) + 4 m, columns 8 (tid & 63).
-    // Two splits' 16-byte loads (16 per thread) are in flight together; an
-    // odd S re-loads split 0 with weight 0.
-    const half_t* pp = p.part_o + (tg * S) * kHG * kLatent + (tid >> 6) * kLatent + 8 * (tid & 63);
-    float a[8][8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) a[m][i] = 0.0f;
-    for (int s0 = 0; s0 < S; s0 += 2) {
-      const int s1 = s0 + 1 < S ? s0 + 1 : 0;
-      half8_t v0[8], v1[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        v0[m] = *reinterpret_cast<const half8_t*>(pp + (s0 * kHG + 4 * m) * kLatent);
-        v1[m] = *reinterpret_cast<const half8_t*>(pp + (s1 * kHG + 4 * m) * kLatent);
-      }
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float w0 = wsh[s0 * kHG + (tid >> 6) + 4 * m];
-        const float w1 = s0 + 1 < S ? wsh[s1 * kHG + (tid >> 6) + 4 * m] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[m][i] += w0 * (float)v0[m][i] + w1 * (float)v1[m][i];
-      }
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    const bool more = s0 + 2 < S;
+    if (more) {
+      load_split(s0 + 2, B0);
+      load_split(s0 + 3 < S ? s0 + 3 : s0 + 2, B1);
     }
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int hd = (tid >> 6) + 4 * m, head = g * kHG + hd;
-      if (head >= p.H) continue;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) a[m][i] *= out_mul;
-      store8<kBf16>(reinterpret_cast<uint16_t*>(p.out) + (t * H + head) * kLatent + 8 * (tid & 63), a[m]);
+    add_pair(A0, A1, s0);
+    if (!more) break;
+    const bool more2 = s0 + 4 < S;
+    if (more2) {
+      load_split(s0 + 4, A0);
+      load_split(s0 + 5 < S ? s0 + 5 : s0 + 4, A1);
     }
+    add_pair(B0, B1, s0 + 2);
+    if (!more2) break;
+  }
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int hd = (tid >> 6) + 4 * m, head = g * kHG + hd;
+    if (head >= p.H) continue;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[m][i] *= out_mul;
+    store8<kBf16>(reinterpret_cast<uint16_t*>(p.out) + (t * H + head) * kLatent + cc, a[m]);
   }
 }
 
