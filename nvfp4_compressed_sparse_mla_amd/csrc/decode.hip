@@ -339,15 +339,16 @@ __device__ __forceinline__ void store8(T* dst, const float (&v)[8]) {
 }
 
 // Split partials cross workgroups (and L2 caches): they are written with
-// agent-scope atomic stores, which write through this XCD's L2, so the
-// writer needs no L2-wide writeback before counting its arrival.
+// the agent-scope cache policy (sc1, what an agent-scope atomic store
+// uses), which writes through this XCD's L2, so the writer needs no
+// L2-wide writeback before counting its arrival.  One 16-byte store; in
+// assembly, so the caller waits for it itself (s_waitcnt vmcnt(0) right
+// after its last store).
 __device__ __forceinline__ void store8_agent(half_t* dst, const float (&v)[8]) {
-  uint32_t w[4];
+  u32x4 w;
 #pragma unroll
   for (int i = 0; i < 4; ++i) w[i] = as_u32((half2_t){(half_t)v[2 * i], (half_t)v[2 * i + 1]});
-  uint64_t* d = reinterpret_cast<uint64_t*>(dst);
-  __hip_atomic_store(d, (uint64_t)w[0] | ((uint64_t)w[1] << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(d + 1, (uint64_t)w[2] | ((uint64_t)w[3] << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  MLA_DEVICE_ASM("global_store_dwordx4 %0, %1, off sc1" :: "v"(dst), "v"(w) : "memory");
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
@@ -583,20 +584,19 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   // split's last row.  NVFP4 rows have 22 pieces: in the last instruction
   // lanes 32..63 (pieces 22, 23) repeat pieces 20 and 21 of their row into
   // positions that are never read.
-  const uint8_t* const lane_src = p.cache + 16 * kg;
-  const uint8_t* const lane_src_last = p.cache + 16 * (20 + (kg & 1));
-  auto issue = [&](uint32_t row, int slot) {
-    const uint8_t* const a = lane_src + (uint64_t)row * kRB;
+  auto issue_from = [&](const uint8_t* row_base, int slot) {
+    const uint8_t* const a = row_base + 16 * kg;
     uint8_t* const dst = ring + slot * kSlot;
     // instruction j: source a + 64j, LDS dst + 1024j (the immediate 64j
     // applies to both)
     auto one = [&](auto J) {
       constexpr int j = decltype(J)::value;
-      if constexpr (kFmt == kFmtNvfp4 && j == 5) MLA_DMA16(lane_src_last + (uint64_t)row * kRB, dst + 1024 * j, 0);
+      if constexpr (kFmt == kFmtNvfp4 && j == 5) MLA_DMA16(row_base + 16 * (20 + (kg & 1)), dst + 1024 * j, 0);
       else MLA_DMA16(a, dst + (1024 - 64) * j, 64 * j);
     };
     static_for<0, kInstr>(one);
   };
+  auto issue = [&](uint32_t row, int slot) { issue_from(p.cache + (uint64_t)row * kRB, slot); };
   // cache row of this lane's DMA row in the wave's k-th tile
   auto tile_row_addr = [&](int k) -> uint32_t {
     int i = (wave + kWaves * k) * kRowsT + r16;
@@ -749,9 +749,20 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     return __builtin_bit_cast(half8_t, (u32x4){d[0][0], d[0][1], d[1][0], d[1][1]});
   };
 
-  if (my_tiles > 0) {
-    issue((uint32_t)phys[r0 + min(wave * kRowsT + r16, n - 1)], 0);
-    if (my_tiles > 1) issue((uint32_t)phys[r0 + min((wave + kWaves) * kRowsT + r16, n - 1)], 1 % kDepth);
+  // The first two tiles' DMA.  Missing tiles re-read a valid row (or q,
+  // with an empty cache) into slots that are never read.
+  // q's loads (issued before the compaction) are complete by now; waiting
+  // for them here, where nothing else is in flight, keeps the compiler from
+  // waiting for the tiles' DMA before q is staged
+  wait_vmcnt<0>();
+  {
+    const uint8_t* const spare = p.cache_rows > 0 ? p.cache : static_cast<const uint8_t*>(p.q);
+    const uint8_t* b0 = spare;
+    const uint8_t* b1 = spare;
+    if (my_tiles > 0) b0 = p.cache + (uint64_t)(uint32_t)phys[r0 + min(wave * kRowsT + r16, n - 1)] * kRB;
+    if (my_tiles > 1) b1 = p.cache + (uint64_t)(uint32_t)phys[r0 + min((wave + kWaves) * kRowsT + r16, n - 1)] * kRB;
+    issue_from(b0, 0);
+    issue_from(b1, 1 % kDepth);
   }
   // q into LDS in B-operand order, then into registers (while the first
   // tiles' DMA is in flight).  B operand of K-step ks for head block hb,
@@ -760,7 +771,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   // (hb * 18 + ks) * 64 + 16kg + r16.  A negative softmax scale flips q's
   // signs here (exact), so sm_log2 >= 0.
   {
-    u32x4* qs = reinterpret_cast<u32x4*>(vbuf_all);
+    // LDS accesses in assembly: the compiler would make them wait for the
+    // tiles' DMA (it cannot tell the V buffer from the ring)
+    const uint32_t qs = lds_off(vbuf_all);
 #pragma unroll
     for (int m = 0; m < kQChunks; ++m) {
       const int c = tid + kThreads * m, h = c / (kQK / 8), d = 8 * (c - h * (kQK / 8));
@@ -774,13 +787,20 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
       }
       u32x4 u = __builtin_bit_cast(u32x4, qstage[m]);
       if (p.q_neg) u ^= 0x80008000u;
-      qs[((h >> 4) * kKSteps + ks) * 64 + 16 * kgq + (h & 15)] = u;
+      const uint32_t a = qs + 16 * (((h >> 4) * kKSteps + ks) * 64 + 16 * kgq + (h & 15));
+      MLA_DEVICE_ASM("ds_write_b128 %0, %1" :: "v"(a), "v"(u) : "memory");
     }
     lds_barrier();   // (not __syncthreads: that would also wait for the tiles' DMA)
+    const uint32_t qa = qs + 16 * lane;
+    static_for<0, 2 * kKSteps>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      qreg[i / kKSteps][i % kKSteps] = __builtin_bit_cast(half8_t, ring_b128<1024 * i>(qa));
+    });
+    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) qreg[hb][ks] = __builtin_bit_cast(half8_t, qs[(hb * kKSteps + ks) * 64 + lane]);
+      for (int ks = 0; ks < kKSteps; ++ks) MLA_DEVICE_ASM("" : "+v"(qreg[hb][ks]));
     lds_barrier();   // every wave has its q before the V buffer is written
   }
   if (my_tiles > 0) {
