@@ -479,9 +479,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   // loads: two dependent memory round trips (addresses of slots past topk
   // or of masked entries are clamped to valid ones and the result dropped).
   // The index loads head the longest dependent chain (index -> block table
-  // -> row DMA), so they and the block-table loads are issued before the q
-  // loads, which only the first score MFMA needs (vector loads complete in
-  // issue order, so anything issued after q would wait for it).
+  // -> row DMA), so they are issued first; q's loads follow while they are
+  // in flight, then the block-table loads (vector loads complete in issue
+  // order: waiting for the block-table entries also waits for q, which by
+  // then has had a round trip's head start).
   int v8[8];
   {
     const int32_t* ip = p.idx + t * p.idx_st;
@@ -494,19 +495,6 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     for (int i = 0; i < 8; ++i)
       if (i * kThreads + tid >= p.topk) v8[i] = -1;
   }
-  int b8[8], pb8[8];
-  bool seq_ok = true;
-  if (p.bt) {
-    const int64_t seq = p.tok_seq[t];
-    seq_ok = seq >= 0 && seq < p.bt_rows;
-    const int32_t* btr = p.bt + (seq_ok ? seq : 0) * p.bt_st;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      b8[i] = v8[i] >= 0 ? v8[i] / p.bs : 0;
-      pb8[i] = btr[b8[i] < p.bt_cols ? b8[i] : p.bt_cols - 1];
-    }
-  }
-
   // ---------------------------------------------------------------- q
   // q of the workgroup's 32 heads is loaded once, 9 coalesced 16-byte chunks
   // per thread (chunk c: head c / 72, dimensions 8 (c % 72) + [0,8); heads
@@ -522,6 +510,19 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
       const int c = tid + kThreads * m, h = c / (kQK / 8), dc = c - h * (kQK / 8);
       const int head = min(g * kHG + h, p.H - 1);
       qstage[m] = load_q8<kBf16>(qt + (int64_t)head * p.q_sh + 8 * dc);
+    }
+  }
+
+  int b8[8], pb8[8];
+  bool seq_ok = true;
+  if (p.bt) {
+    const int64_t seq = p.tok_seq[t];
+    seq_ok = seq >= 0 && seq < p.bt_rows;
+    const int32_t* btr = p.bt + (seq_ok ? seq : 0) * p.bt_st;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      b8[i] = v8[i] >= 0 ? v8[i] / p.bs : 0;
+      pb8[i] = btr[b8[i] < p.bt_cols ? b8[i] : p.bt_cols - 1];
     }
   }
 
