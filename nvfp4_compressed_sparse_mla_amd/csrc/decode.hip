@@ -1115,8 +1115,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
 #pragma unroll
     for (int i = 0; i < 8; ++i) lx[i] = src[i];
   }
-  load_split(0, A0);
-  load_split(1 < S ? 1 : 0, A1);
+  // With two splits only the other one's partial is loaded; this split's
+  // own comes from its staging buffers (rounded to FP16 as stored, so the
+  // result does not depend on which split merges).
+  if (S == 2) {
+    load_split(1 - s, A1);
+  } else {
+    load_split(0, A0);
+    load_split(1 < S ? 1 : 0, A1);
+  }
   if (wave == 0 && lane < S) {
     float4_t* dst = reinterpret_cast<float4_t*>(lse_sh + lane * kHG);
 #pragma unroll
@@ -1136,21 +1143,37 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     if (head < p.H && p.lse) p.lse[t * H + head] = mx != kNegInf ? (mx + __log2f(sum)) * kLn2 : kNegInf;
   }
   __syncthreads();
-  for (int s0 = 0; s0 < S; s0 += 4) {
-    const bool more = s0 + 2 < S;
-    if (more) {
-      load_split(s0 + 2, B0);
-      load_split(s0 + 3 < S ? s0 + 3 : s0 + 2, B1);
+  if (S == 2) {
+    const int blk = cc >> 7;   // column block of 128, held by wave ((blk & 1) << 1) | (blk >> 1)
+    const float* own = reinterpret_cast<const float*>(xbuf(((blk & 1) << 1) | (blk >> 1)) + 1024);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int hd = (tid >> 6) + 4 * m;
+      const float* src = own + hd * 128 + ((cc & 127) ^ (((hd >> 2) & 1) << 5));
+      const float4_t x = *reinterpret_cast<const float4_t*>(src);
+      const float4_t y = *reinterpret_cast<const float4_t*>(src + 4);
+      A0[m] = (half8_t){(half_t)x.x, (half_t)x.y, (half_t)x.z, (half_t)x.w,
+                        (half_t)y.x, (half_t)y.y, (half_t)y.z, (half_t)y.w};
     }
-    add_pair(A0, A1, s0);
-    if (!more) break;
-    const bool more2 = s0 + 4 < S;
-    if (more2) {
-      load_split(s0 + 4, A0);
-      load_split(s0 + 5 < S ? s0 + 5 : s0 + 4, A1);
+    if (s == 0) add_pair(A0, A1, 0);
+    else add_pair(A1, A0, 0);
+  } else {
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      const bool more = s0 + 2 < S;
+      if (more) {
+        load_split(s0 + 2, B0);
+        load_split(s0 + 3 < S ? s0 + 3 : s0 + 2, B1);
+      }
+      add_pair(A0, A1, s0);
+      if (!more) break;
+      const bool more2 = s0 + 4 < S;
+      if (more2) {
+        load_split(s0 + 4, A0);
+        load_split(s0 + 5 < S ? s0 + 5 : s0 + 4, A1);
+      }
+      add_pair(B0, B1, s0 + 2);
+      if (!more2) break;
     }
-    add_pair(B0, B1, s0 + 2);
-    if (!more2) break;
   }
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
