@@ -1104,8 +1104,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     for (int m = 0; m < 8; ++m) {
       const float w0 = wsh[s0 * kHG + (tid >> 6) + 4 * m];
       const float w1 = has1 ? wsh[s1 * kHG + (tid >> 6) + 4 * m] : 0.0f;
+      // (two fused multiply-adds per element, each taking its FP16 operand
+      // as is: v_fma_mix)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a[m][i] += w0 * (float)v0[m][i] + w1 * (float)v1[m][i];
+      for (int i = 0; i < 8; ++i) a[m][i] = __builtin_fmaf(w1, (float)v1[m][i], __builtin_fmaf(w0, (float)v0[m][i], a[m][i]));
     }
   };
   half8_t A0[8], A1[8], B0[8], B1[8];
