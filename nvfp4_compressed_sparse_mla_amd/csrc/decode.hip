@@ -84,7 +84,9 @@ constexpr int ring_depth(int fmt) { return fmt == kFmtNvfp4 ? 3 : 2; }
 constexpr int kWaveRing = 18432;      // bytes of ring per wave (both formats)
 static_assert(ring_depth(kFmtNvfp4) * slot_bytes(kFmtNvfp4) <= kWaveRing, "NVFP4 ring");
 static_assert(ring_depth(kFmtFp8) * slot_bytes(kFmtFp8) <= kWaveRing, "FP8 ring");
-constexpr int kWaveV = kRowsT * kVRow;          // FP16 elements of V buffer per wave
+// FP16 elements of V buffer per wave; the stream merge's exchange regions
+// (36,352 bytes per stream) reuse two waves' buffers, hence the padding
+constexpr int kWaveV = kRowsT * kVRow + 512;
 constexpr int kMergeHalves = kHG * kLatent;     // one stream's O in FP16
 static_assert(2 * kMergeHalves * 2 <= kWaves * kWaveRing, "merge buffers of streams 0,1");
 static_assert(2 * kMergeHalves <= kWaves * kWaveV, "merge buffers of streams 2,3");
@@ -465,11 +467,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   __shared__ int last_s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Block index arithmetic in 32 bits (a 64-bit division is a long chain
+  // of dependent scalar instructions ahead of the first memory access).
   const int S = p.S, G = p.G;
-  const int s = (int)(blockIdx.x % (unsigned)S);
-  const int64_t tg = blockIdx.x / (unsigned)S;
-  const int g = (int)(tg % G);
-  const int64_t t = tg / G;
+  const uint32_t tg32 = S == 1 ? blockIdx.x : blockIdx.x / (uint32_t)S;
+  const int s = (int)(blockIdx.x - tg32 * (uint32_t)S);
+  const uint32_t t32 = G == 1 ? tg32 : tg32 / (uint32_t)G;
+  const int g = (int)(tg32 - t32 * (uint32_t)G);
+  const int64_t tg = tg32, t = t32;
   const int r16 = lane & 15, kg = lane >> 4;
   uint8_t* ring = ring_all + wave * kWaveRing;
   half_t* vbuf = vbuf_all + wave * kWaveV;
@@ -568,8 +573,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   }
   lds_barrier();
 
-  const int r0 = (int)((int64_t)total * s / S);
-  const int n = (int)((int64_t)total * (s + 1) / S) - r0;
+  // (total <= 2048 and S <= 64: the products fit in 32 bits)
+  const int r0 = S == 1 ? 0 : (int)((uint32_t)(total * s) / (uint32_t)S);
+  const int n = (S == 1 ? total : (int)((uint32_t)(total * (s + 1)) / (uint32_t)S)) - r0;
   const int ntiles = (n + kRowsT - 1) / kRowsT;
   const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
 
@@ -948,111 +954,69 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     }
   }
   __syncthreads();
-  // Reduce-scatter of the weighted streams in FP32 through LDS, in the MFMA
-  // C layout (lane-contiguous 16-byte pieces: no bank conflicts).  Round 1:
-  // waves w and w^1 swap column halves (wave w keeps half w & 1); round 2:
-  // waves w and w^2 swap quarters of that half (wave w keeps quarter w >> 1).
-  // Wave w ends with column blocks 4(2(w & 1) + (w >> 1)) .. +3.  Exchange
-  // buffers: waves 0,1 in the ring area, 2,3 in the V area (32 KB each; the
-  // rings are idle).  The code is specialised per wave so that every
-  // accumulator index is a compile-time constant.
-  auto xbuf = [&](int w) -> float4_t* {
-    return w < 2 ? reinterpret_cast<float4_t*>(ring_all) + w * 2048
-                 : reinterpret_cast<float4_t*>(vbuf_all) + (w - 2) * 2048;
-  };
-  float res[4][16];
-  auto reduce = [&](auto W0, auto W1) {
-    constexpr int w0 = decltype(W0)::value, w1 = decltype(W1)::value;
-    float cw[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) cw[j] = alpha_s[wave][c_head(j, lane)];
-    constexpr int keep1 = 8 * w0, send1 = 8 * (1 - w0);
-    {
-      float4_t* mine = xbuf(wave);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4)
-          mine[(i * 4 + j4) * 64 + lane] = (float4_t){
-              acc_o[send1 + i][4 * j4] * cw[4 * j4], acc_o[send1 + i][4 * j4 + 1] * cw[4 * j4 + 1],
-              acc_o[send1 + i][4 * j4 + 2] * cw[4 * j4 + 2], acc_o[send1 + i][4 * j4 + 3] * cw[4 * j4 + 3]};
-    }
-    __syncthreads();
-    float half_sum[8][16];
-    {
-      const float4_t* other = xbuf(wave ^ 1);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-          const float4_t v = other[(i * 4 + j4) * 64 + lane];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            half_sum[i][4 * j4 + e] = acc_o[keep1 + i][4 * j4 + e] * cw[4 * j4 + e] + v[e];
-        }
-    }
-    __syncthreads();   // wave ^ 1 has read this wave's buffer
-    constexpr int keep2 = 4 * w1, send2 = 4 * (1 - w1);
-    {
-      float4_t* mine = xbuf(wave);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4)
-          mine[(i * 4 + j4) * 64 + lane] = (float4_t){half_sum[send2 + i][4 * j4], half_sum[send2 + i][4 * j4 + 1],
-                                                      half_sum[send2 + i][4 * j4 + 2], half_sum[send2 + i][4 * j4 + 3]};
-    }
-    __syncthreads();
-    {
-      const float4_t* other = xbuf(wave ^ 2);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-          const float4_t v = other[(i * 4 + j4) * 64 + lane];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) res[i][4 * j4 + e] = half_sum[keep2 + i][4 * j4 + e] + v[e];
-        }
-    }
-  };
-  switch (wave) {
-    case 0: reduce(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}); break;
-    case 1: reduce(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}); break;
-    case 2: reduce(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}); break;
-    default: reduce(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}); break;
-  }
-
-  // this wave now holds the full result for column blocks colb/32 .. +3
-  const int colb = 128 * (2 * (wave & 1) + (wave >> 1));
+  // Stream merge in two rounds of 256 columns.  Each wave writes its FP32
+  // O for 8 column blocks straight from the accumulation registers into its
+  // exchange region (waves 0, 1 in the ring area, 2, 3 in the V area; the
+  // rings are idle), then every thread sums the four streams for 4 heads x 8
+  // columns with the stream weights and stores them (16-byte stores).
+  // Exchange layout: 16-byte slot s (the lane of the MFMA C layout) of block
+  // b (column block within the round x 4 + element quad) sits at byte
+  // 1136 b + 16 s + 32 (s >> 4): the writers' 64 lanes and the readers' 8
+  // consecutive slots (8 columns of 4 heads) are both free of bank conflicts.
   const float out_mul = p.kv_scale;  // FP8 rows: values carry kv_scale
   const int64_t H = p.H;
   {
-    // Stage the wave's [32 heads x 128 columns] in FP32 in the second half of
-    // its own exchange buffer (its partner read only the first half in round
-    // 2), then store 8 consecutive columns per lane (16-byte stores).  The
-    // column index is XOR-swizzled by bit 2 of the head so that the two head
-    // rows one store instruction writes fall in different banks.
-    float* stage = reinterpret_cast<float*>(xbuf(wave) + 1024);
+    constexpr uint32_t kXBlock = 1136, kXRegion = 32 * kXBlock;
+    static_assert(2 * kXRegion <= kWaves * kWaveRing && 2 * kXRegion <= kWaves * kWaveV * 2, "exchange regions");
+    uint8_t* const x01 = ring_all;
+    uint8_t* const x23 = reinterpret_cast<uint8_t*>(vbuf_all);
+    uint8_t* const xw = (wave < 2 ? x01 : x23) + (wave & 1) * kXRegion + 16 * lane + 32 * (lane >> 4);
+    // reader: heads 4 hq + [0,4), columns 256 hh + 8 co + [0,8)
+    const int hq = tid & 7, co = tid >> 3;
+    const uint32_t rslot = 32 * (hq & 1) + 8 * (co & 3);
+    const uint32_t rofs = ((co >> 2) * 4 + (hq >> 1)) * kXBlock + 16 * rslot + 32 * (rslot >> 4);
+    const uint8_t* const r01 = x01 + rofs;
+    const uint8_t* const r23 = x23 + rofs;
     const float mul = S > 1 ? 1.0f : out_mul;
+    float wgt[kWaves][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int w = 0; w < kWaves; ++w)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int hd = c_head(j, lane);
-        const int c = 32 * i + (lane & 31);
-        stage[hd * 128 + (c ^ (((hd >> 2) & 1) << 5))] = res[i][j] * mul;
+      for (int h = 0; h < 4; ++h) wgt[w][h] = alpha_s[w][4 * hq + h] * mul;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (hh == 1) __syncthreads();   // the first round's reads are done
+#pragma unroll
+      for (int nbl = 0; nbl < 8; ++nbl)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4_t*>(xw + (nbl * 4 + q) * kXBlock) =
+              (float4_t){acc_o[8 * hh + nbl][4 * q], acc_o[8 * hh + nbl][4 * q + 1], acc_o[8 * hh + nbl][4 * q + 2],
+                         acc_o[8 * hh + nbl][4 * q + 3]};
+      __syncthreads();
+      float o[4][8];
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int x = 0; x < 8; ++x) o[h][x] = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const uint8_t* const src = (w < 2 ? r01 : r23) + (w & 1) * kXRegion;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const float4_t v = *reinterpret_cast<const float4_t*>(src + 16 * x);
+#pragma unroll
+          for (int h = 0; h < 4; ++h) o[h][x] = __builtin_fmaf(wgt[w][h], v[h], o[h][x]);
+        }
       }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int e = lane + 64 * k, hd = e >> 4, cc = (e & 15) * 8;
-      const float* src = stage + hd * 128 + (cc ^ (((hd >> 2) & 1) << 5));
-      const float4_t a = *reinterpret_cast<const float4_t*>(src);
-      const float4_t b = *reinterpret_cast<const float4_t*>(src + 4);
-      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      const int head = g * kHG + hd;
-      if (S > 1) store8_agent(p.part_o + ((tg * S + s) * kHG + hd) * kLatent + colb + cc, v);
-      else if (head < p.H)
-        store8<kBf16>(reinterpret_cast<uint16_t*>(p.out) + (t * H + head) * kLatent + colb + cc, v);
+      for (int h = 0; h < 4; ++h) {
+        const int hd = 4 * hq + h, head = g * kHG + hd;
+        const int col = 256 * hh + 8 * co;
+        if (S > 1) store8_agent(p.part_o + ((tg * S + s) * kHG + hd) * kLatent + col, o[h]);
+        else if (head < p.H)
+          store8<kBf16>(reinterpret_cast<uint16_t*>(p.out) + (t * H + head) * kLatent + col, o[h]);
+      }
     }
   }
   if (S == 1) return;
@@ -1117,15 +1081,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
 #pragma unroll
     for (int i = 0; i < 8; ++i) lx[i] = src[i];
   }
-  // With two splits only the other one's partial is loaded; this split's
-  // own comes from its staging buffers (rounded to FP16 as stored, so the
-  // result does not depend on which split merges).
-  if (S == 2) {
-    load_split(1 - s, A1);
-  } else {
-    load_split(0, A0);
-    load_split(1 < S ? 1 : 0, A1);
-  }
+  load_split(0, A0);
+  load_split(1 < S ? 1 : 0, A1);
   if (wave == 0 && lane < S) {
     float4_t* dst = reinterpret_cast<float4_t*>(lse_sh + lane * kHG);
 #pragma unroll
@@ -1145,21 +1102,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     if (head < p.H && p.lse) p.lse[t * H + head] = mx != kNegInf ? (mx + __log2f(sum)) * kLn2 : kNegInf;
   }
   __syncthreads();
-  if (S == 2) {
-    const int blk = cc >> 7;   // column block of 128, held by wave ((blk & 1) << 1) | (blk >> 1)
-    const float* own = reinterpret_cast<const float*>(xbuf(((blk & 1) << 1) | (blk >> 1)) + 1024);
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int hd = (tid >> 6) + 4 * m;
-      const float* src = own + hd * 128 + ((cc & 127) ^ (((hd >> 2) & 1) << 5));
-      const float4_t x = *reinterpret_cast<const float4_t*>(src);
-      const float4_t y = *reinterpret_cast<const float4_t*>(src + 4);
-      A0[m] = (half8_t){(half_t)x.x, (half_t)x.y, (half_t)x.z, (half_t)x.w,
-                        (half_t)y.x, (half_t)y.y, (half_t)y.z, (half_t)y.w};
-    }
-    if (s == 0) add_pair(A0, A1, 0);
-    else add_pair(A1, A0, 0);
-  } else {
+  {
     for (int s0 = 0; s0 < S; s0 += 4) {
       const bool more = s0 + 2 < S;
       if (more) {
