@@ -219,9 +219,9 @@ __device__ __forceinline__ void ring_issue_b(Raw<kFmt>& r, uint32_t slot, const 
 template <int kFmt>
 __device__ __forceinline__ void lgkm_wait_b(u32x4 (&b)[4], Raw<kFmt>& r) {
   if constexpr (kFmt == kFmtNvfp4)
-    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(r.l[2]), "+v"(r.l[3]));
+    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(r.l[2]), "+v"(r.l[3]));
   else
-    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)"
+    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(4)"
                    : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(r.l[4]), "+v"(r.l[5]), "+v"(r.l[6]), "+v"(r.l[7]));
 }
 
@@ -378,6 +378,12 @@ __device__ __forceinline__ void read_v4_group(u32x4 (&b)[4], uint32_t base) {
 
 __device__ __forceinline__ void lgkm_wait(u32x4 (&b)[4]) {
   MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+}
+// the same, leaving the wave's last four LDS operations (V-buffer writes
+// issued after these reads) in flight: a wave's LDS operations complete in
+// issue order
+__device__ __forceinline__ void lgkm_wait4(u32x4 (&b)[4]) {
+  MLA_DEVICE_ASM("s_waitcnt lgkmcnt(4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
 }
 
 // Workgroup barrier for LDS data only: waits for this wave's LDS operations,
@@ -867,8 +873,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
       static_for<0, 4>([&](auto J) {
         constexpr int j = decltype(J)::value;
         u32x4 (&bv)[4] = bvb[j & 1];
-        if constexpr (j == 1) lgkm_wait_b<kFmt>(bv, raw);
-        else lgkm_wait(bv);
+        // group j's reads were issued one unit earlier, followed by that
+        // unit's four V-buffer writes (unit 0: by the ring's part B reads,
+        // which it waits for as well)
+        if constexpr (j == 0) lgkm_wait(bv);
+        else if constexpr (j == 1) lgkm_wait_b<kFmt>(bv, raw);
+        else lgkm_wait4(bv);
         if constexpr (j < 3) read_v4_group<j + 1>(bvb[(j + 1) & 1], vb);
         *reinterpret_cast<half8_t*>(vrow + 8 * (4 * j)) = kop;   // after group j's reads
         if (pending) rescale_group(J);
