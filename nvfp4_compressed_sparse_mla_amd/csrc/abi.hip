@@ -168,6 +168,7 @@ int mla_sparse_decode(const void* q, int q_dtype, int64_t num_tokens, int32_t nu
   p.idx_st = idx_stride_t;
   p.bt = block_table;
   p.bs = block_table ? block_size : 1;
+  p.bs_log2 = (p.bs & (p.bs - 1)) == 0 ? __builtin_ctz((unsigned)p.bs) : -1;
   p.bt_cols = block_table ? bt_cols : 0;
   p.bt_rows = block_table ? bt_rows : 0;
   p.bt_st = block_table ? bt_stride : 0;
@@ -237,6 +238,7 @@ int mla_nvfp4_gather_dequant_fp8(const uint8_t* cache, int64_t cache_rows, const
   p.idx_st = idx_stride_t;
   p.bt = block_table;
   p.bs = block_table ? block_size : 1;
+  p.bs_log2 = (p.bs & (p.bs - 1)) == 0 ? __builtin_ctz((unsigned)p.bs) : -1;
   p.bt_cols = block_table ? bt_cols : 0;
   p.bt_rows = block_table ? bt_rows : 0;
   p.bt_st = block_table ? bt_stride : 0;

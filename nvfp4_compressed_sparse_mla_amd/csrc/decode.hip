@@ -475,10 +475,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Block index arithmetic in 32 bits (a 64-bit division is a long chain
   // of dependent scalar instructions ahead of the first memory access).
+  // No branch here either: the kernel's argument loads can then all be
+  // issued at once, ahead of the first global load.
   const int S = p.S, G = p.G;
-  const uint32_t tg32 = S == 1 ? blockIdx.x : blockIdx.x / (uint32_t)S;
+  const uint32_t tg32 = blockIdx.x / (uint32_t)S;
   const int s = (int)(blockIdx.x - tg32 * (uint32_t)S);
-  const uint32_t t32 = G == 1 ? tg32 : tg32 / (uint32_t)G;
+  const uint32_t t32 = tg32 / (uint32_t)G;
   const int g = (int)(tg32 - t32 * (uint32_t)G);
   const int64_t tg = tg32, t = t32;
   const int r16 = lane & 15, kg = lane >> 4;
@@ -532,7 +534,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     const int32_t* btr = p.bt + (seq_ok ? seq : 0) * p.bt_st;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      b8[i] = v8[i] >= 0 ? v8[i] / p.bs : 0;
+      // (a power-of-two block size, the usual case, divides by a shift)
+      const int v = v8[i] >= 0 ? v8[i] : 0;
+      b8[i] = p.bs_log2 >= 0 ? v >> p.bs_log2 : v / p.bs;
       pb8[i] = btr[b8[i] < p.bt_cols ? b8[i] : p.bt_cols - 1];
     }
   }

@@ -33,6 +33,7 @@ struct DecodeParams {
   int64_t idx_st;
   const int32_t* bt;        // optional block table
   int bs, bt_rows, bt_cols;
+  int bs_log2;              // log2(bs) if bs is a power of two, else -1
   int64_t bt_st;
   const int32_t* tok_seq;
   float sm_log2;            // |sm_scale| * log2(e) * kv_scale (>= 0)
@@ -68,6 +69,7 @@ struct StagedParams {
   int64_t idx_st;
   const int32_t* bt;
   int bs, bt_rows, bt_cols;
+  int bs_log2;              // log2(bs) if bs is a power of two, else -1
   int64_t bt_st;
   const int32_t* tok_seq;
   float inv_scale;

@@ -148,21 +148,24 @@ def test_duplicates_and_out_of_range_indices():
     _check(w, cache, out, lse, what="dups")
 
 
-def test_block_table_small():
-    w = make_custom(64 * 40, 3, 32, 200, seed=15, device=DEV)
+@pytest.mark.parametrize("bs", [64, 48, 16])
+def test_block_table_small(bs):
+    # power-of-two block sizes take the shift path, others the division
+    w = make_custom(bs * 40, 3, 32, 200, seed=15, device=DEV)
     rng = np.random.default_rng(15)
     bt = np.stack([rng.permutation(40)[:30] for _ in range(2)]).astype(np.int32)
     bt[1, 25:] = -1                                 # unassigned blocks
     seq = np.array([0, 1, 0], dtype=np.int32)
-    idx = np.stack([rng.choice(30 * 64, 200, replace=False) for _ in range(3)]).astype(np.int32)
-    idx[1] = rng.choice(25 * 64, 200, replace=False)
+    idx = np.stack([rng.choice(30 * bs, 200, replace=False) for _ in range(3)]).astype(np.int32)
+    idx[1] = rng.choice(25 * bs, 200, replace=False)
     idx[2, 150:] = -1
     w.indices = torch.from_numpy(idx).to(DEV)
     w.block_table = torch.from_numpy(bt).to(DEV)
     w.token_seq = torch.from_numpy(seq).to(DEV)
+    w.block_size = bs
     cache = _fill(w)
     out, lse = _run(w, cache)
-    _check(w, cache, out, lse, what="blocktable")
+    _check(w, cache, out, lse, what=f"blocktable-bs{bs}")
 
 
 def test_fp8_rows_path():
