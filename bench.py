@@ -15,8 +15,10 @@ per-step events) so neither the 256 MB Infinity Cache nor L2 holds the
 gathered rows; the step's small inputs (q, index lists, block table, new
 rows), which the kernels before attention have just written in a real decode
 step, are read once after the sweep (--cold-inputs leaves them cold).  Every step is bracketed by HIP events on the stream the
-kernels run on; `value` and `us_per_step` come from that pass.  A second
-pass repeats the steps with the library's kernel timing on
+kernels run on, with no event inside a step; `value` and `us_per_step`
+come from that pass.  A second pass puts an event between the append and
+the decode (`append_us`, `decode_us`).  A third pass repeats the steps with
+the library's kernel timing on
 (hipExtLaunchKernel events at each kernel's own start and end): those
 durations give `decode_kernel_us`, the roofline figure and the comparators'
 `*_kernel_us`.  Prints one JSON line.
@@ -141,11 +143,11 @@ def _gpu_run(args):
                 for x in step_inputs:
                     x.sum()
 
-    def step(tm=None, i=0):
+    def step(tm=None, i=0, split=False):
         if tm:
             tm.mark(i, 0)
         mla.quantize_append(app_lat, app_rope, app_slots, cache)
-        if tm:
+        if tm and split:
             tm.mark(i, 1)
         mla.sparse_decode(w.q, cache, w.indices, w.sm_scale, block_table=w.block_table,
                           token_seq=w.token_seq, block_size=w.block_size, workspace=ws,
@@ -157,7 +159,8 @@ def _gpu_run(args):
         do_flush()
         step()
     torch.cuda.synchronize()
-    # pass A, the timed region: K steps, each bracketed by HIP events, no instrumentation
+    # pass A, the timed region: K steps, each bracketed by HIP events, no
+    # instrumentation inside a step
     tm = Timer(torch, args.steps)
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -165,6 +168,13 @@ def _gpu_run(args):
         step(tm, i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # pass A2: the same steps with an event between the append and the decode
+    # (the split into append_us and decode_us; that event costs the step time)
+    tm2 = Timer(torch, max(20, args.steps // 2))
+    for i in range(len(tm2.ev)):
+        do_flush()
+        step(tm2, i, split=True)
+    torch.cuda.synchronize()
     # pass B: the same steps with the library's kernel timing on (each kernel's own
     # start/end events), for the roofline and the per-kernel figures
     # (the decode follows its append on the GPU with no host round trip in
@@ -187,14 +197,17 @@ def _gpu_run(args):
     finally:
         mla.kernel_timing(False)
     step_ms = tm.spans(0, 2)
-    dec_ms = tm.spans(1, 2)
-    app_ms = tm.spans(0, 1)
+    dec_ms = tm2.spans(1, 2)
+    app_ms = tm2.spans(0, 1)
     res = {
         "T": T, "H": H, "K": K, "rows": rows, "splits": splits, "valid": valid, "gathered": gathered,
         "step_ms": statistics.mean(step_ms), "decode_ms": statistics.mean(dec_ms),
         "decode_ms_median": statistics.median(dec_ms),
         "decode_ms_p10": sorted(dec_ms)[len(dec_ms) // 10],
         "decode_ms_p90": sorted(dec_ms)[(9 * len(dec_ms)) // 10],
+        "step_ms_median": statistics.median(step_ms),
+        "step_ms_p10": sorted(step_ms)[len(step_ms) // 10],
+        "step_ms_p90": sorted(step_ms)[(9 * len(step_ms)) // 10],
         "append_ms": statistics.mean(app_ms), "wall_ms_per_iter": 1e3 * wall / args.steps,
         "kernel_ms": statistics.mean(kern_ms), "kernel_ms_median": statistics.median(kern_ms),
         "append_kernel_ms": statistics.mean(app_kern_ms),
@@ -387,6 +400,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(res["step_ms"], 5),
         "us_per_step": round(1e3 * res["step_ms"], 3),
+        "us_per_step_median": round(1e3 * res["step_ms_median"], 3),
+        "us_per_step_p10_p90": [round(1e3 * res["step_ms_p10"], 3), round(1e3 * res["step_ms_p90"], 3)],
         "decode_kernel_us": round(1e3 * res["kernel_ms"], 3),
         "decode_kernel_us_median": round(1e3 * res["kernel_ms_median"], 3),
         "decode_us": round(1e3 * res["decode_ms"], 3),
