@@ -42,6 +42,7 @@ if ROOT not in sys.path:
 
 METRIC = "sparse-MLA decode µs/step + gathered HBM GB/s (NVFP4 KV, top-2048)"
 HBM_PEAK_GBS = 8000.0
+MFMA_FP16_PEAK_TFLOPS = 2500.0
 ROW_BYTES = 352
 FP8_ROW_BYTES = 576
 
@@ -57,7 +58,7 @@ DESCRIPTIONS = {
 def _parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode15")
     ap.add_argument("--warm", action="store_true", help="no cache flush between steps")
@@ -84,6 +85,25 @@ def _copy_calibration(mib: int, reps: int = 10):
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
                       "launches": reps}), flush=True)
+
+
+def _copy_peak(torch, dev, mib: int = 512, reps: int = 5) -> float:
+    """Device-to-device copy bandwidth on this machine (GB/s of bytes read + written)."""
+    n = mib * 1024 * 1024
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    return round(2 * n / (best * 1e-3) / 1e9, 1)
 
 
 class Timer:
@@ -127,6 +147,7 @@ def _gpu_run(args):
         flush.fill_(1.0)
     valid = w.valid_slots()
     gathered = valid * ROW_BYTES
+    copy_gbs = _copy_peak(torch, dev)
 
     # The step's own small inputs (q, index lists, block table, the new rows)
     # are written by the kernels that precede attention in a decode step, so
@@ -211,6 +232,9 @@ def _gpu_run(args):
         "append_ms": statistics.mean(app_ms), "wall_ms_per_iter": 1e3 * wall / args.steps,
         "kernel_ms": statistics.mean(kern_ms), "kernel_ms_median": statistics.median(kern_ms),
         "append_kernel_ms": statistics.mean(app_kern_ms),
+        "copy_gbs": copy_gbs,
+        "append_bytes": int(app_lat.numel() * app_lat.element_size() + app_rope.numel() * app_rope.element_size()
+                            + app_slots.numel() * 8 + int((app_slots >= 0).sum()) * ROW_BYTES),
     }
 
     if not args.no_comparators:
@@ -317,28 +341,43 @@ def _cpu_baseline(w, seconds):
         lat16 = w.latent.index_select(0, sel).cpu().numpy().astype(np.float64)
         rope16 = w.rope.index_select(0, sel).cpu().numpy().astype(np.float64)
         per_tok.append(codec.nvfp4_encode_rows(lat16, rope16))
-    done_bytes = 0
-    n_tok = 0
-    t0 = time.perf_counter()
-    while True:
-        for t in tokens:
-            enc = per_tok[t]
-            lat, rope = codec.nvfp4_decode_rows(enc)
-            attention.sparse_mla_token(q[t], lat, rope, w.sm_scale)
-            done_bytes += enc.shape[0] * ROW_BYTES
-            n_tok += 1
-            if time.perf_counter() - t0 > seconds:
+    def run(limit):
+        done_bytes = 0
+        n_tok = 0
+        t0 = time.perf_counter()
+        while True:
+            for t in tokens:
+                enc = per_tok[t]
+                lat, rope = codec.nvfp4_decode_rows(enc)
+                attention.sparse_mla_token(q[t], lat, rope, w.sm_scale)
+                done_bytes += enc.shape[0] * ROW_BYTES
+                n_tok += 1
+                if time.perf_counter() - t0 > limit:
+                    break
+            if time.perf_counter() - t0 > limit:
                 break
-        if time.perf_counter() - t0 > seconds:
-            break
-    el = time.perf_counter() - t0
-    return {
+        return done_bytes, n_tok, time.perf_counter() - t0
+
+    done_bytes, n_tok, el = run(seconds)
+    out = {
         "value": done_bytes / el / 1e9, "unit": "GB/s", "cores": blas_threads,
         "kind": "oracle",
         "sample": f"{n_tok} token-passes of the {w.name} workload ({n_tok / max(1, len(tokens)):.1f} steps), "
-                  f"NVFP4 row decode + FP64 attention, {el:.1f} s; host os.cpu_count()={os.cpu_count()}",
+                  f"NVFP4 row decode + FP64 attention, {el:.1f} s; host os.cpu_count()={os.cpu_count()}, "
+                  f"affinity {len(os.sched_getaffinity(0))} cores",
         "us_per_step": 1e6 * el * len(tokens) / max(1, n_tok),
     }
+    # the same with the BLAS pool limited to one thread (half the time budget)
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            b1, n1, e1 = run(seconds / 2)
+        out["single_thread"] = {"value": b1 / e1 / 1e9, "unit": "GB/s", "cores": 1,
+                                "us_per_step": 1e6 * e1 * len(tokens) / max(1, n1),
+                                "sample": f"{n1} token-passes, {e1:.1f} s"}
+    except Exception:  # pragma: no cover
+        pass
+    return out
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_decode_nvfp4_hbm_traffic.txt")
@@ -390,6 +429,8 @@ def main():
     # roofline: algorithmic bytes of one launch over the kernel's own duration
     # (HIP events recorded at kernel start and end by hipExtLaunchKernel)
     achieved = res["gathered"] / (res["kernel_ms"] * 1e-3) / 1e9
+    # scores (576) and values (512) per valid slot and head, 2 flops per multiply-add
+    mfma_flops = 2.0 * res["H"] * (576 + 512) * res["valid"]
     traffic = None if (args.splits or args.warm) else _traffic(args.workload, res["splits"])
     line = {
         "metric": METRIC,
@@ -409,6 +450,9 @@ def main():
         "decode_us_p10_p90": [round(1e3 * res["decode_ms_p10"], 3), round(1e3 * res["decode_ms_p90"], 3)],
         "append_us": round(1e3 * res["append_ms"], 3),
         "append_kernel_us": round(1e3 * res["append_kernel_ms"], 3),
+        "append_kernel_gbs": round(res["append_bytes"] / (res["append_kernel_ms"] * 1e-3) / 1e9, 2),
+        "mfma_tflops": round(mfma_flops / (res["kernel_ms"] * 1e-3) / 1e12, 2),
+        "mfma_frac_of_fp16_peak": round(mfma_flops / (res["kernel_ms"] * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -423,6 +467,8 @@ def main():
                    "splits": res["splits"], "cache": "nvfp4-352"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "copy_peak_measured": res["copy_gbs"],
+                     "frac_of_copy_peak": round(achieved / res["copy_gbs"], 4),
                      "traffic": traffic["total"] if traffic else None,
                      "traffic_read_write": [traffic["read"], traffic["write"]] if traffic else None,
                      "kernel": "sparse_decode_kernel", "bytes_per_launch": res["gathered"],
