@@ -11,7 +11,7 @@ runs on FP16 operands with FP32 accumulation.  The 2048-position selection
 list has its empty slots padded (wireai.ir, 4-bit-caches section, third
 decision).
 
-Readings taken where the pages are silent (listed in the design doc):
+Readings taken where the pages are silent:
 
 * A1  Absorbed-MLA decode: the key of a row is its 576 values [latent(512);
       rope(64)] and its value is the latent alone, so scores contract over

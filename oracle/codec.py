@@ -13,7 +13,7 @@ wireai.ir article, 4-bit-caches section):
 * with the scales included a row shrinks from 576 bytes to 352 bytes
   (256 B of nibbles + 32 B of scales + 64 B of rope).
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * R1  The four-bit element is E2M1 (sign, 2 exponent bits with bias 1,
       1 mantissa bit; magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; no Inf/NaN),
