@@ -87,9 +87,8 @@ static_assert(ring_depth(kFmtFp8) * slot_bytes(kFmtFp8) <= kWaveRing, "FP8 ring"
 // FP16 elements of V buffer per wave; the stream merge's exchange regions
 // (36,352 bytes per stream) reuse two waves' buffers, hence the padding
 constexpr int kWaveV = kRowsT * kVRow + 512;
-constexpr int kMergeHalves = kHG * kLatent;     // one stream's O in FP16
-static_assert(2 * kMergeHalves * 2 <= kWaves * kWaveRing, "merge buffers of streams 0,1");
-static_assert(2 * kMergeHalves <= kWaves * kWaveV, "merge buffers of streams 2,3");
+// q of the workgroup's 32 heads is staged through the V buffers before the loop
+static_assert(kHG * kQK * 2 <= kWaves * kWaveV * 2, "q staging area");
 
 __device__ __forceinline__ uint32_t lds_off(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
