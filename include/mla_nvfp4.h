@@ -168,7 +168,9 @@ size_t mla_sparse_decode_workspace_size(int64_t num_tokens, int32_t num_heads,
  *   lse               device, [T, H] float, contiguous; may be NULL.
  *   workspace         device, workspace_bytes >= the size query's answer for
  *                     (T, H, topk, num_splits); zero-filled before first use.
- *   num_splits        0 = launch sizer's choice; otherwise 1..64.
+ *   num_splits        0 = launch sizer's choice; otherwise 1..64.  The call
+ *                     returns MLA_ERR_INVALID_ARG when the launch would need
+ *                     2^24 or more workgroups (ceil(T*H/32 / 8) * 8 * S).
  * Calls that overlap in time must not share a workspace.
  */
 int mla_sparse_decode(const void* q, int q_dtype, int64_t num_tokens,

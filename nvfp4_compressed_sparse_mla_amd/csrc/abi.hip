@@ -149,7 +149,9 @@ int mla_sparse_decode(const void* q, int q_dtype, int64_t num_tokens, int32_t nu
       return MLA_ERR_INVALID_ARG;
   }
   const int S = num_splits ? num_splits : mla::decode_auto_splits(num_tokens, num_heads, topk);
-  if (num_tokens * G * S > 0x7FFFFFFF) return MLA_ERR_INVALID_ARG;
+  // the grid (units rounded up to 8, times S workgroups of 256 threads)
+  // must hold fewer than 2^32 work-items
+  if ((num_tokens * G + 7) / 8 * 8 * S >= (int64_t)1 << 24) return MLA_ERR_INVALID_ARG;
   const size_t need = mla::decode_workspace_bytes(num_tokens, num_heads, S);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
 

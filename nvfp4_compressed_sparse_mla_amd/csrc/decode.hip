@@ -474,11 +474,18 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Block index arithmetic in 32 bits (a 64-bit division is a long chain
   // of dependent scalar instructions ahead of the first memory access).
-  // No branch here either: the kernel's argument loads can then all be
-  // issued at once, ahead of the first global load.
+  // Workgroups are dealt to the 8 XCDs in turn (workgroup b runs on XCD
+  // b mod 8).  With xcd_shift = 3 the S splits of (token, head group)
+  // 8 k + x are workgroups b = 8 (S k + s) + x, all on XCD x, where the
+  // merging split reads the others' partials (and all read the same q and
+  // index list) through one L2; the grid is then rounded up to a multiple
+  // of 8 S.  With xcd_shift = 0 split s of unit k is workgroup S k + s.
   const int S = p.S, G = p.G;
-  const uint32_t tg32 = blockIdx.x / (uint32_t)S;
-  const int s = (int)(blockIdx.x - tg32 * (uint32_t)S);
+  const uint32_t xsh = (uint32_t)p.xcd_shift;
+  const uint32_t slot = blockIdx.x >> xsh, kx = slot / (uint32_t)S;
+  const int s = (int)(slot - kx * (uint32_t)S);
+  const uint32_t tg32 = (kx << xsh) + (blockIdx.x & ((1u << xsh) - 1u));
+  if (tg32 >= (uint32_t)(p.T * G)) return;   // padding of the rounded-up grid
   const uint32_t t32 = tg32 / (uint32_t)G;
   const int g = (int)(tg32 - t32 * (uint32_t)G);
   const int64_t tg = tg32, t = t32;
@@ -1193,9 +1200,19 @@ size_t decode_workspace_bytes(int64_t T, int H, int S) {
 
 hipError_t launch_decode(const DecodeParams& p, int fmt, bool bf16, hipStream_t stream,
                          const KernelEvents& ev) {
-  const int64_t blocks = p.T * p.G * p.S;
+  // A (token, head group)'s splits share an XCD (xcd_shift = 3) unless
+  // that would take more rounds of resident workgroups than the plain
+  // order: grouping puts ceil(units / 8) * S workgroups on each XCD's
+  // eighth of the CUs.
+  DecodeParams a = p;
+  const int64_t units = p.T * p.G;
+  const int64_t cus = device_cus() > 0 ? device_cus() : 256, per_xcd = cus >= 8 ? cus / 8 : 1;
+  const int64_t rounds_plain = (units * p.S + cus - 1) / cus;
+  const int64_t rounds_grouped = ((units + 7) / 8 * p.S + per_xcd - 1) / per_xcd;
+  a.xcd_shift = p.S > 1 && rounds_grouped <= rounds_plain ? 3 : 0;
+  const int64_t blocks = a.xcd_shift ? (units + 7) / 8 * 8 * p.S : units * p.S;
   dim3 grid((unsigned)blocks), block(kThreads);
-  void* args[] = {const_cast<DecodeParams*>(&p)};
+  void* args[] = {&a};
   const void* fn;
   if (fmt == kFmtNvfp4)
     fn = bf16 ? (const void*)sparse_decode_kernel<kFmtNvfp4, true>

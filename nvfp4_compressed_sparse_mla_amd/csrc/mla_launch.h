@@ -44,6 +44,7 @@ struct DecodeParams {
   float* part_lse;          // [T*G][S][32]
   _Float16* part_o;         // [T*G][S][32][512]
   int S;                    // splits per (token, head group)
+  int xcd_shift;            // set by launch_decode: 3 = a unit's splits share an XCD, 0 = plain order
 };
 
 int decode_auto_splits(int64_t T, int H, int topk);
