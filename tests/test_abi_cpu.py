@@ -90,6 +90,9 @@ def test_decode_rejects_bad_arguments(lib):
     assert _decode(lib, bt=0x7000) == INVALID               # block table without token_seq
     assert _decode(lib, bt=0x7000, ts=0x8000, brows=0, bcols=4, bst=4) == INVALID
     assert _decode(lib, splits=65) == INVALID
+    # the launch grid (units rounded up to 8, times the splits) stays below 2^24 workgroups
+    assert _decode(lib, T=1 << 21, splits=8) == INVALID
+    assert _decode(lib, T=(1 << 21) - 8, splits=8, wsb=16) == WORKSPACE
     assert _decode(lib, fmt=1, kv=0.3) == INVALID
     assert _decode(lib, sm=float("inf")) == INVALID
     assert _decode(lib, ws=None) == WORKSPACE
