@@ -336,7 +336,9 @@ def _cpu_baseline(w, seconds):
     per_tok = []
     for t in tokens:
         v = idx[t][idx[t] >= 0]
-        rows = attention.physical_rows(v, None if seq is None else int(seq[t]), bt, w.block_size)
+        rows = attention.physical_rows(v, None if seq is None else int(seq[t]), bt, w.block_size,
+                                       w.pool_rows)
+        rows = rows[rows >= 0]
         sel = __import__("torch").from_numpy(rows).to(w.latent.device)
         lat16 = w.latent.index_select(0, sel).cpu().numpy().astype(np.float64)
         rope16 = w.rope.index_select(0, sel).cpu().numpy().astype(np.float64)

@@ -23,6 +23,11 @@ Readings taken where the pages are silent:
 * A4  With a block table, logical position p of sequence b lives at
       physical row block_table[b, p // block_size] * block_size
       + p % block_size.
+* A8  A slot that names no cache row is masked like a pad: without a
+      block table, an index at or past the pool's last row; with one, a
+      token whose sequence id is not a row of the table, a position whose
+      block number is past the table's width, a block entry that is
+      negative (unassigned), or a physical row at or past the pool's end.
 * A5  lse is the natural-log log-sum-exp of the *scaled* scores.
 * A6  A token with no valid slot has output 0 and lse = -inf.
 * A7  q arrives as fp16 or bf16 and is taken at its exact value; sm_scale is
@@ -47,13 +52,34 @@ import numpy as np
 from .codec import LATENT_DIM, ROPE_DIM
 
 
-def physical_rows(positions, seq, block_table, block_size):
-    """Map logical positions of one sequence to physical cache rows (A4)."""
+def physical_rows(positions, seq, block_table, block_size, cache_rows):
+    """Physical cache rows of one token's non-negative slot indices (A4, A8).
+
+    positions:   the token's indices that are >= 0, in list order.
+    seq:         the token's sequence id (a row of block_table), or None.
+    block_table: [B, W] integer table or None (indices are physical rows).
+    cache_rows:  number of rows in the pool.
+
+    Returns an int64 array of the same length: the physical row of each
+    slot, or -1 where the slot names no row (A8), so that the caller masks it.
+    """
     p = np.asarray(positions, dtype=np.int64)
+    rows = np.full(p.shape, -1, dtype=np.int64)
     if block_table is None:
-        return p
+        ok = p < cache_rows
+        rows[ok] = p[ok]
+        return rows
     bt = np.asarray(block_table, dtype=np.int64)
-    return bt[seq, p // block_size] * block_size + p % block_size
+    if seq is None or not 0 <= int(seq) < bt.shape[0]:
+        return rows
+    block = p // block_size
+    entry = np.full(p.shape, -1, dtype=np.int64)
+    inside = block < bt.shape[1]
+    entry[inside] = bt[int(seq), block[inside]]
+    phys = entry * block_size + p % block_size
+    ok = (entry >= 0) & (phys < cache_rows)
+    rows[ok] = phys[ok]
+    return rows
 
 
 def sparse_mla_token(q_t, lat_rows, rope_rows, sm_scale):
@@ -86,7 +112,8 @@ def sparse_mla(q, lat, rope, indices, sm_scale, block_table=None,
     rope:     [R, 64]  FP64 decoded rope
     indices:  [T, K] int, negative = masked (A2)
     sm_scale: python float holding the caller's float32 value (A7)
-    block_table / token_seq / block_size: optional logical -> physical map (A4)
+    block_table / token_seq / block_size: optional logical -> physical map (A4);
+    slots that name no row are masked (A8)
 
     Returns (out [T, H, 512] FP64, lse [T, H] FP64).
     """
@@ -99,7 +126,8 @@ def sparse_mla(q, lat, rope, indices, sm_scale, block_table=None,
     for t in range(t_count):
         valid = idx[t][idx[t] >= 0]                                 # A2, A3
         seq = None if token_seq is None else int(token_seq[t])
-        rows = physical_rows(valid, seq, block_table, block_size)
+        rows = physical_rows(valid, seq, block_table, block_size, lat.shape[0])
+        rows = rows[rows >= 0]                                      # A8
         out[t], lse[t] = sparse_mla_token(q[t], lat[rows], rope[rows], sm_scale)
     return out, lse
 

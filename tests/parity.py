@@ -37,15 +37,16 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
-def physical_lists(indices, block_table, token_seq, block_size, tokens):
-    """Per token: the physical rows of its valid slots (oracle's mapping, A4)."""
+def physical_lists(indices, block_table, token_seq, block_size, tokens, cache_rows):
+    """Per token: the physical rows of its valid slots (oracle's mapping, A4 and A8)."""
     idx = indices.cpu().numpy().astype(np.int64)
     bt = None if block_table is None else block_table.cpu().numpy().astype(np.int64)
     seq = None if token_seq is None else token_seq.cpu().numpy().astype(np.int64)
     lists = []
     for t in tokens:
         v = idx[t][idx[t] >= 0]
-        lists.append(attention.physical_rows(v, None if seq is None else int(seq[t]), bt, block_size))
+        rows = attention.physical_rows(v, None if seq is None else int(seq[t]), bt, block_size, cache_rows)
+        lists.append(rows[rows >= 0])
     return lists
 
 
@@ -57,7 +58,7 @@ def oracle_reference(latent, rope, q, indices, sm_scale, tokens=None, block_tabl
     """
     T = q.shape[0]
     tokens = list(range(T)) if tokens is None else list(tokens)
-    lists = physical_lists(indices, block_table, token_seq, block_size, tokens)
+    lists = physical_lists(indices, block_table, token_seq, block_size, tokens, latent.shape[0])
     touched = np.unique(np.concatenate(lists)) if any(len(l) for l in lists) else np.zeros(0, np.int64)
     sel = torch.from_numpy(touched).to(latent.device)
     lat16 = host(latent.index_select(0, sel)) if len(touched) else np.zeros((0, 512))

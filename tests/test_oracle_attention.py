@@ -160,29 +160,109 @@ def test_empty_list_gives_zero_and_minus_inf():
     assert np.all(np.isfinite(lse[1]))
 
 
-def test_block_table_relayout_is_transparent():
-    bs, n_blocks = 4, 12
-    lat, rope = _rows(bs * n_blocks, 12)
-    rng = np.random.default_rng(12)
-    # two sequences of 10 and 14 logical rows placed on scattered blocks
-    bt = np.array([[7, 2, 10, -1], [0, 5, 3, 11]])
-    ctx = [10, 14]
-    q = _q(2, 2, 12)
-    idx = np.full((2, 8), -1)
-    idx[0, :6] = rng.choice(ctx[0], 6, replace=False)
-    idx[1, :8] = rng.choice(ctx[1], 8, replace=False)
-    out, lse = attention.sparse_mla(q, lat, rope, idx, SM, block_table=bt,
-                                    token_seq=np.array([0, 1]), block_size=bs)
-    # same rows laid out contiguously per sequence, addressed directly
-    phys = np.full_like(idx, -1)
-    for t in range(2):
-        v = idx[t] >= 0
-        p = idx[t][v]
-        phys[t][v] = bt[t, p // bs] * bs + p % bs
-    o2, l2 = attention.sparse_mla(q, lat, rope, phys, SM)
-    np.testing.assert_array_equal(out, o2)
-    np.testing.assert_array_equal(lse, l2)
-    assert phys[0, 0] == bt[0, idx[0, 0] // bs] * bs + idx[0, 0] % bs
+def _paged_case(bs, seed):
+    """Sequences held as contiguous decoded arrays, and the same rows copied
+    block by block into a shared pool through a block table.
+
+    Returns (pool_lat, pool_rope, bt, seqs, q, idx, token_seq, expected) where
+    expected[t] lists token t's logical positions that exist in its sequence.
+    Index lists mix positions inside the sequence, positions in unassigned
+    blocks (entry -1), positions past the table's width and, for one token, a
+    sequence id outside the table: all of those name no row (A8).
+    """
+    rng = np.random.default_rng(seed)
+    ctx = [3 * bs + 1, 5 * bs, 2 * bs + bs // 2]
+    width = 7                                        # table columns
+    n_blocks = 24
+    seqs = [_rows(c, seed + 10 * b) for b, c in enumerate(ctx)]
+    # the pool starts out holding unrelated rows: a wrong address reads them
+    pool_lat, pool_rope = _rows(n_blocks * bs, seed + 99)
+    pool_lat, pool_rope = pool_lat.copy(), pool_rope.copy()
+    bt = np.full((len(ctx), width), -1, dtype=np.int64)
+    free = list(rng.permutation(n_blocks))
+    for b, c in enumerate(ctx):
+        nb = -(-c // bs)
+        for k in range(nb):
+            blk = free.pop()
+            bt[b, k] = blk
+            n = min(bs, c - k * bs)
+            pool_lat[blk * bs:blk * bs + n] = seqs[b][0][k * bs:k * bs + n]
+            pool_rope[blk * bs:blk * bs + n] = seqs[b][1][k * bs:k * bs + n]
+    token_seq = np.array([0, 1, 2, 1, 5])            # token 4: no such sequence
+    T, K = len(token_seq), 24
+    q = _q(T, 2, seed)
+    idx = np.full((T, K), -1, dtype=np.int64)
+    expected = []
+    for t, b in enumerate(token_seq):
+        c = ctx[b] if b < len(ctx) else 0
+        inside = list(rng.choice(c, min(c, 12), replace=False)) if c else []
+        nb = -(-c // bs) if c else 0
+        unassigned = [nb * bs + int(x) for x in rng.integers(0, (width - nb) * bs, 3)] if c else [1, 2]
+        past_width = [width * bs + int(x) for x in rng.integers(0, 50, 2)]
+        lst = inside + unassigned + past_width
+        pos = np.sort(rng.choice(K, len(lst), replace=False))
+        idx[t, pos] = rng.permutation(np.array(lst, dtype=np.int64))
+        expected.append([int(p) for p in idx[t] if 0 <= p < c and b < len(ctx)])
+    return pool_lat, pool_rope, bt, seqs, q, idx, token_seq, expected
+
+
+def _paged_matches_contiguous(bs, seed):
+    """Attention through the block table equals attention over each
+    sequence's contiguous rows addressed directly by logical position."""
+    pool_lat, pool_rope, bt, seqs, q, idx, token_seq, expected = _paged_case(bs, seed)
+    out, lse = attention.sparse_mla(q, pool_lat, pool_rope, idx, SM, block_table=bt,
+                                    token_seq=token_seq, block_size=bs)
+    for t, b in enumerate(token_seq):
+        if b >= len(seqs) or not expected[t]:
+            if not (np.all(out[t] == 0.0) and np.all(np.isneginf(lse[t]))):
+                return False
+            continue
+        lat, rope = seqs[b]
+        o2, l2 = attention.sparse_mla_token(q[t], lat[expected[t]], rope[expected[t]], SM)
+        if not (np.array_equal(out[t], o2) and np.array_equal(lse[t], l2)):
+            return False
+    return True
+
+
+@pytest.mark.parametrize("bs", [4, 5, 64])
+def test_block_table_relayout_against_contiguous_sequences(bs):
+    assert _paged_matches_contiguous(bs, 40 + bs)
+
+
+def test_relayout_pin_catches_a_swapped_block_and_offset(monkeypatch):
+    """The pin above fails when the mapping swaps p // bs and p % bs, or
+    wraps an unassigned entry instead of masking it (mistakes planted in the
+    oracle)."""
+    good = attention.physical_rows
+
+    def swapped(positions, seq, block_table, block_size, cache_rows):
+        p = np.asarray(positions, dtype=np.int64)
+        q = (p % block_size) * block_size + p // block_size
+        return good(q, seq, block_table, block_size, cache_rows)
+
+    def wraps(positions, seq, block_table, block_size, cache_rows):
+        p = np.asarray(positions, dtype=np.int64)
+        bt = np.asarray(block_table)
+        blk = np.minimum(p // block_size, bt.shape[1] - 1)
+        r = bt[min(int(seq), bt.shape[0] - 1), blk] * block_size + p % block_size
+        return np.where(r < 0, r % cache_rows, r)
+
+    for bad in (swapped, wraps):
+        monkeypatch.setattr(attention, "physical_rows", bad)
+        assert not _paged_matches_contiguous(5, 45)
+    monkeypatch.setattr(attention, "physical_rows", good)
+    assert _paged_matches_contiguous(5, 45)
+
+
+def test_index_past_the_pool_is_masked():
+    """Without a block table an index at or past the last row names no row
+    (A8): the result equals the list without it."""
+    lat, rope = _rows(16, 13)
+    q = _q(1, 3, 13)
+    o1, l1 = attention.sparse_mla(q, lat, rope, np.array([[3, 16, 7, 1000]]), SM)
+    o2, l2 = attention.sparse_mla_token(q[0], lat[[3, 7]], rope[[3, 7]], SM)
+    np.testing.assert_array_equal(o1[0], o2)
+    np.testing.assert_array_equal(l1[0], l2)
 
 
 def test_staged_path_equals_native_on_fp8_exact_rows():

@@ -329,6 +329,61 @@ def test_fp8_rows_match_torch_cast():
     assert np.array_equal(l2, ref.to(torch.float64).numpy()[:, :512])
 
 
+def _fp8_scaled_case(kv, seed):
+    """fp16 rows whose quotients v / kv stay below 464 (torch's cast turns
+    larger values into NaN instead of saturating), with E4M3 rounding
+    midpoints times kv planted among them."""
+    rng = np.random.default_rng(seed)
+    lat = rng.standard_normal((40, 512)) * np.exp(rng.standard_normal((40, 1)))
+    grid = codec.E4M3_POS
+    mids = (grid[1:] + grid[:-1]) / 2                  # exact in FP64
+    lat[:, :len(mids)] = mids * kv * np.where(rng.random(len(mids)) < 0.5, -1, 1)
+    lat = np.clip(lat, -440 * kv, 440 * kv)
+    rope = rng.standard_normal((40, 64)) * 4 * kv
+    return _fp16(lat), _fp16(rope)
+
+
+def _fp8_scaled_matches_torch(kv, seed):
+    lat, rope = _fp8_scaled_case(kv, seed)
+    rows = codec.fp8_encode_rows(lat, rope, kv)
+    v = np.concatenate([lat, rope], 1)
+    # v / kv is exact in float32 (kv is a power of two, v an fp16 value)
+    ref = torch.from_numpy((v / kv).astype(np.float32)).to(torch.float8_e4m3fn)
+    if not np.array_equal(rows, ref.view(torch.uint8).numpy()):
+        return False
+    l2, r2 = codec.fp8_decode_rows(rows, kv)
+    dec = ref.to(torch.float64).numpy() * kv
+    return np.array_equal(l2, dec[:, :512]) and np.array_equal(r2, dec[:, 512:])
+
+
+@pytest.mark.parametrize("kv", [0.25, 0.5, 2.0])
+def test_fp8_rows_with_kv_scale_match_torch_cast(kv):
+    """Bytes are E4M3(v / kv_scale) and decode to byte value * kv_scale, as
+    torch's float8_e4m3fn cast of the quotient gives them (ties included)."""
+    assert _fp8_scaled_matches_torch(kv, 20 + int(4 * kv))
+
+
+@pytest.mark.parametrize("kv", [0.25, 2.0])
+def test_fp8_rows_with_kv_scale_saturate(kv):
+    lat = np.zeros((1, 512))
+    lat[0, :4] = [464 * kv, -1e4 * kv, 448 * kv, -449 * kv]
+    rows = codec.fp8_encode_rows(_fp16(lat), np.zeros((1, 64)), kv)
+    assert rows[0, :4].tolist() == [0x7E, 0xFE, 0x7E, 0xFE]
+
+
+def test_fp8_kv_scale_pin_catches_a_flipped_scale(monkeypatch):
+    """The pin fails when the encoder multiplies by kv_scale instead of
+    dividing, or the decoder divides (mistakes planted in the oracle)."""
+    enc, dec = codec.fp8_encode_rows, codec.fp8_decode_rows
+    monkeypatch.setattr(codec, "fp8_encode_rows", lambda l, r, kv=1.0: enc(l, r, 1.0 / kv))
+    assert not _fp8_scaled_matches_torch(0.5, 7)
+    monkeypatch.setattr(codec, "fp8_encode_rows", enc)
+    monkeypatch.setattr(codec, "fp8_decode_rows", lambda rows, kv=1.0: dec(rows, 1.0 / kv))
+    assert not _fp8_scaled_matches_torch(0.5, 7)
+    monkeypatch.setattr(codec, "fp8_decode_rows", dec)
+    assert _fp8_scaled_matches_torch(0.5, 7)
+
+
 def test_staged_rows_definition():
     rng = np.random.default_rng(13)
     lat = _fp16(rng.standard_normal((40, 512)))
