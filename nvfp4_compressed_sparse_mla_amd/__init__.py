@@ -51,6 +51,46 @@ def _rows2d(x: torch.Tensor, width: int, name: str) -> torch.Tensor:
     return x
 
 
+def _device_of(t: torch.Tensor, name: str) -> torch.device:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a tensor in GPU memory")
+    return t.device
+
+
+def _same_device(dev: torch.device, **tensors) -> None:
+    """Every given tensor (None = absent) lives on the GPU `dev`."""
+    for name, t in tensors.items():
+        if t is not None and (not isinstance(t, torch.Tensor) or t.device != dev):
+            raise ValueError(f"{name} must be on {dev} like the other arguments")
+
+
+def _exact(t: torch.Tensor, name: str, shape, dtype) -> None:
+    """A contiguous tensor of exactly this shape and dtype (the library writes
+    it densely and takes no strides for it)."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+
+
+def _cache_tensor(cache: torch.Tensor, row_bytes: int) -> None:
+    if cache.dtype != torch.uint8 or cache.dim() != 2 or cache.shape[1] != row_bytes or not cache.is_contiguous():
+        raise ValueError(f"cache must be contiguous uint8 [rows, {row_bytes}]")
+
+
+def _block_table_args(block_table, token_seq, T: int, dev):
+    """Pointers and sizes of an optional block table and its token -> sequence map."""
+    if block_table is None:
+        return None, None, 0, 0, 0, None
+    _same_device(dev, block_table=block_table, token_seq=token_seq)
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be int32 [seqs, blocks] with unit last stride")
+    if token_seq is None or token_seq.dtype != torch.int32 or tuple(token_seq.shape) != (T,):
+        raise ValueError("token_seq must be int32 [T] when a block table is given")
+    token_seq = token_seq.contiguous()
+    return (block_table.data_ptr(), token_seq.data_ptr(), block_table.stride(0),
+            block_table.shape[0], block_table.shape[1], token_seq)
+
+
 def _append(fn_name, latent, rope, slots, cache, row_bytes, extra=()):
     lib = load()
     _rows2d(latent, LATENT_DIM, "latent")
@@ -61,8 +101,8 @@ def _append(fn_name, latent, rope, slots, cache, row_bytes, extra=()):
         raise ValueError("slots must be int64 [n]")
     if rope.shape[0] != latent.shape[0]:
         raise ValueError("latent and rope must have the same number of rows")
-    if cache.dtype != torch.uint8 or cache.dim() != 2 or cache.shape[1] != row_bytes or not cache.is_contiguous():
-        raise ValueError(f"cache must be contiguous uint8 [rows, {row_bytes}]")
+    _cache_tensor(cache, row_bytes)
+    _same_device(_device_of(cache, "cache"), latent=latent, rope=rope, slots=slots)
     slots = slots.contiguous()
     st = getattr(lib, fn_name)(_ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0),
                                _dtype_code(latent), latent.shape[0], _ptr(slots), _ptr(cache),
@@ -102,32 +142,30 @@ def sparse_decode(q: torch.Tensor, cache: torch.Tensor, indices: torch.Tensor, s
                   block_size: int = 64, workspace=None, num_splits: int = 0, out=None, lse=None):
     """Sparse MLA decode; returns (out [T, H, 512] in q's dtype, lse [T, H] float32)."""
     lib = load()
+    dev = _device_of(q, "q")
     if q.dim() != 3 or q.shape[2] != QK_DIM or q.stride(2) != 1:
         raise ValueError("q must be [T, H, 576] with unit last stride")
+    _dtype_code(q)
     T, H = q.shape[0], q.shape[1]
+    if fmt not in _FMT:
+        raise ValueError(f"fmt must be one of {sorted(_FMT)}")
     fmt_code = _FMT[fmt]
-    row_bytes = NVFP4_ROW_BYTES if fmt_code == FMT_NVFP4 else FP8_ROW_BYTES
-    if cache.dtype != torch.uint8 or cache.dim() != 2 or cache.shape[1] != row_bytes or not cache.is_contiguous():
-        raise ValueError(f"cache must be contiguous uint8 [rows, {row_bytes}]")
+    _cache_tensor(cache, NVFP4_ROW_BYTES if fmt_code == FMT_NVFP4 else FP8_ROW_BYTES)
+    _same_device(dev, cache=cache, indices=indices, workspace=workspace, out=out, lse=lse)
     if indices.dtype != torch.int32 or indices.dim() != 2 or indices.shape[0] != T or indices.stride(1) != 1:
         raise ValueError("indices must be int32 [T, topk] with unit last stride")
     topk = indices.shape[1]
-    bt_ptr = ts_ptr = None
-    bt_stride = bt_rows = bt_cols = 0
-    if block_table is not None:
-        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
-            raise ValueError("block_table must be int32 [seqs, blocks] with unit last stride")
-        if token_seq is None or token_seq.dtype != torch.int32 or token_seq.shape != (T,):
-            raise ValueError("token_seq must be int32 [T] when a block table is given")
-        token_seq = token_seq.contiguous()
-        bt_ptr, ts_ptr = block_table.data_ptr(), token_seq.data_ptr()
-        bt_stride, bt_rows, bt_cols = block_table.stride(0), block_table.shape[0], block_table.shape[1]
+    bt_ptr, ts_ptr, bt_stride, bt_rows, bt_cols, token_seq = _block_table_args(block_table, token_seq, T, dev)
     if out is None:
-        out = torch.empty((T, H, LATENT_DIM), dtype=q.dtype, device=q.device)
+        out = torch.empty((T, H, LATENT_DIM), dtype=q.dtype, device=dev)
+    _exact(out, "out", (T, H, LATENT_DIM), q.dtype)
     if lse is None:
-        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _exact(lse, "lse", (T, H), torch.float32)
     if workspace is None:
-        workspace = make_workspace(T, H, topk, q.device, num_splits)
+        workspace = make_workspace(T, H, topk, dev, num_splits)
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 vector (see make_workspace)")
     st = lib.mla_sparse_decode(
         q.data_ptr(), _dtype_code(q), T, H, q.stride(0), q.stride(1),
         cache.data_ptr(), fmt_code, cache.shape[0], float(kv_scale),
@@ -144,23 +182,19 @@ def gather_dequant_fp8(cache: torch.Tensor, indices: torch.Tensor, fp8_scale: fl
                        rows=None, staged_indices=None):
     """Staged comparator step 1: selected NVFP4 rows -> FP8 rows [T*topk, 576] in HBM."""
     lib = load()
-    if cache.dtype != torch.uint8 or cache.dim() != 2 or cache.shape[1] != NVFP4_ROW_BYTES:
-        raise ValueError("cache must be uint8 [rows, 352]")
+    dev = _device_of(cache, "cache")
+    _cache_tensor(cache, NVFP4_ROW_BYTES)
+    _same_device(dev, indices=indices, rows=rows, staged_indices=staged_indices)
+    if indices.dtype != torch.int32 or indices.dim() != 2 or indices.stride(1) != 1:
+        raise ValueError("indices must be int32 [T, topk] with unit last stride")
     T, topk = indices.shape
     if rows is None:
-        rows = torch.empty((T * topk, FP8_ROW_BYTES), dtype=torch.uint8, device=cache.device)
+        rows = torch.empty((T * topk, FP8_ROW_BYTES), dtype=torch.uint8, device=dev)
+    _exact(rows, "rows", (T * topk, FP8_ROW_BYTES), torch.uint8)
     if staged_indices is None:
-        staged_indices = torch.empty((T, topk), dtype=torch.int32, device=cache.device)
-    bt_ptr = ts_ptr = None
-    bt_stride = bt_rows = bt_cols = 0
-    if block_table is not None:
-        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
-            raise ValueError("block_table must be int32 [seqs, blocks] with unit last stride")
-        if token_seq is None or token_seq.dtype != torch.int32 or token_seq.shape != (T,):
-            raise ValueError("token_seq must be int32 [T] when a block table is given")
-        token_seq = token_seq.contiguous()
-        bt_ptr, ts_ptr = block_table.data_ptr(), token_seq.data_ptr()
-        bt_stride, bt_rows, bt_cols = block_table.stride(0), block_table.shape[0], block_table.shape[1]
+        staged_indices = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    _exact(staged_indices, "staged_indices", (T, topk), torch.int32)
+    bt_ptr, ts_ptr, bt_stride, bt_rows, bt_cols, token_seq = _block_table_args(block_table, token_seq, T, dev)
     st = lib.mla_nvfp4_gather_dequant_fp8(
         cache.data_ptr(), cache.shape[0], indices.data_ptr(), T, topk, indices.stride(0),
         bt_ptr, int(block_size), bt_stride, bt_rows, bt_cols, ts_ptr, float(fp8_scale),
