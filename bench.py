@@ -1,30 +1,35 @@
 #!/usr/bin/env python3
 """Benchmark: NVFP4 sparse-MLA decode on one MI355X.
 
-One step = the whole hot path for one decode step of the workload: the
-quantize-append of the step's new rows (one per token) plus one sparse
-decode launch over every token's selected rows.  Inputs are synthetic and
-seeded (synth/), resident in HBM before timing starts.
+One step = the whole hot path for one decode step of a workload: the
+quantize-append of the step's new rows plus one sparse decode launch over
+every token's selected rows.  Inputs are synthetic and seeded (synth/),
+resident in HBM before timing starts.
 
-Default workload: 15 query tokens (one per sequence), 32 heads, top-2048
-distinct picks from each sequence's 146,000 rows, 2.2M-row NVFP4 pool.
+The headline workload (default ``batch128``, the largest decode batch: 128
+tokens x 32 heads, top-2048 of 140K-146K rows through a 64-row block table
+in a 1.63M-row pool) gives `value`, `roofline` and `cpu_baseline`.  Every
+other workload (tiny, decode15, padded35, prefill4k) is timed in the same
+run with the same protocol and reported under `configs`, next to the
+headline's own entry.
 
-Timing: W untimed warm-up steps, then K timed steps.  By default the caches
-are cold for every step: a 1 GiB read sweep runs between steps (outside the
-per-step events) so neither the 256 MB Infinity Cache nor L2 holds the
-gathered rows; the step's small inputs (q, index lists, block table, new
-rows), which the kernels before attention have just written in a real decode
-step, are read once after the sweep (--cold-inputs leaves them cold).  Every step is bracketed by HIP events on the stream the
-kernels run on, with no event inside a step; `value` and `us_per_step`
-come from that pass.  A second pass puts an event between the append and
-the decode (`append_us`, `decode_us`).  A third pass repeats the steps with
-the library's kernel timing on
-(hipExtLaunchKernel events at each kernel's own start and end): those
-durations give `decode_kernel_us`, the roofline figure and the comparators'
-`*_kernel_us`.  Prints one JSON line.
+Timing, per workload: W untimed warm-up steps, then K timed steps.  The
+caches are cold for every step: a 1 GiB read sweep runs between steps
+(outside the per-step events) so neither the 256 MB Infinity Cache nor L2
+holds the gathered rows; the step's small inputs (q, index lists, block
+table, new rows), which the kernels before attention have just written in
+a real decode step, are read once after the sweep (--cold-inputs leaves
+them cold).  Pass A brackets each step with HIP events on the stream the
+kernels run on, with nothing inside a step (`us_per_step`, `value`).  Pass
+A2 puts an event between the append and the decode (`append_us`,
+`decode_us`).  Pass B repeats the launches with the library's kernel timing
+on (hipExtLaunchKernel events at each kernel's own start and end), which
+gives `decode_kernel_us`, `append_kernel_us`, the roofline figure and the
+comparators' kernel times.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--warm] [--no-comparators] [--no-cpu-baseline]
+                    [--configs a,b,...] [--warm] [--no-comparators]
+                    [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -45,6 +50,9 @@ HBM_PEAK_GBS = 8000.0
 MFMA_FP16_PEAK_TFLOPS = 2500.0
 ROW_BYTES = 352
 FP8_ROW_BYTES = 576
+ALL_CONFIGS = ("tiny", "decode15", "padded35", "batch128", "prefill4k")
+# the pages' comparison trio (native / FP8-576 / staged) is reported at these
+TRIO_CONFIGS = ("decode15", "padded35", "batch128")
 
 DESCRIPTIONS = {
     "tiny": "1 token x 16 heads, 256 picks of a 4,096-row NVFP4 pool",
@@ -55,12 +63,14 @@ DESCRIPTIONS = {
 }
 
 
-def _parse():
+def _parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode15")
+    ap.add_argument("--workload", default="batch128", help="headline workload")
+    ap.add_argument("--configs", default=",".join(ALL_CONFIGS),
+                    help="comma-separated workloads timed besides the headline ('' = none)")
     ap.add_argument("--warm", action="store_true", help="no cache flush between steps")
     ap.add_argument("--cold-inputs", action="store_true",
                     help="leave q, index lists and block table cold too (default: only the gathered rows)")
@@ -70,7 +80,7 @@ def _parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def _copy_calibration(mib: int, reps: int = 10):
@@ -110,7 +120,6 @@ class Timer:
     """Per-launch HIP events on torch's current stream (the stream the library uses)."""
 
     def __init__(self, torch, n):
-        self.torch = torch
         self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
 
     def mark(self, i, k):
@@ -120,205 +129,190 @@ class Timer:
         return [e[a].elapsed_time(e[b]) for e in self.ev]
 
 
-def _gpu_run(args):
-    import torch
+def _stats_us(ms):
+    s = sorted(ms)
+    return {"mean": round(1e3 * statistics.mean(ms), 3), "median": round(1e3 * statistics.median(ms), 3),
+            "p10": round(1e3 * s[len(s) // 10], 3), "p90": round(1e3 * s[(9 * len(s)) // 10], 3)}
 
-    import nvfp4_compressed_sparse_mla_amd as mla
-    from synth import make_workload
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    w = make_workload(args.workload, dev)
-    T, H, K = w.tokens, w.heads, w.topk
-    rows = w.pool_rows
-    cache = torch.empty((rows, ROW_BYTES), dtype=torch.uint8, device=dev)
-    mla.quantize_append(w.latent, w.rope, torch.arange(rows, dtype=torch.int64, device=dev), cache)
-    keep = w.append_slots >= 0
-    app_slots = w.append_slots.clone()
-    app_idx = torch.where(keep, w.append_slots, torch.zeros_like(w.append_slots))
-    app_lat = w.latent[app_idx].contiguous()      # each token's own row, same values: the step is repeatable
-    app_rope = w.rope[app_idx].contiguous()
-    splits = args.splits or mla.num_splits(T, H, K)
-    ws = mla.make_workspace(T, H, K, dev, splits)
-    out = torch.empty((T, H, 512), dtype=w.q.dtype, device=dev)
-    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
-    flush = None if args.warm else torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev)
-    if flush is not None:
-        flush.fill_(1.0)
-    valid = w.valid_slots()
-    gathered = valid * ROW_BYTES
-    copy_gbs = _copy_peak(torch, dev)
+class Case:
+    """One workload, prepared on the device: the encoded pool, the step's new
+    rows, workspace and outputs."""
 
-    # The step's own small inputs (q, index lists, block table, the new rows)
-    # are written by the kernels that precede attention in a decode step, so
-    # after the sweep they are read once more to leave them in cache; only
-    # the gathered cache rows stay cold.  --cold-inputs skips that.
-    step_inputs = [w.q, w.indices, app_lat, app_rope, app_slots]
-    if w.block_table is not None:
-        step_inputs += [w.block_table, w.token_seq]
+    def __init__(self, torch, mla, name, dev, q_dtype, splits, flush, cold_inputs):
+        from synth import make_workload
 
-    def do_flush():
-        if flush is not None:
-            flush.sum()
-            if not args.cold_inputs:
-                for x in step_inputs:
+        self.torch, self.mla, self.name = torch, mla, name
+        w = make_workload(name, dev, q_dtype=q_dtype)
+        self.w = w
+        T, H, K = w.tokens, w.heads, w.topk
+        self.cache = torch.empty((w.pool_rows, ROW_BYTES), dtype=torch.uint8, device=dev)
+        mla.quantize_append(w.latent, w.rope, torch.arange(w.pool_rows, dtype=torch.int64, device=dev),
+                            self.cache)
+        keep = w.append_slots >= 0
+        self.app_slots = w.append_slots.clone()
+        app_idx = torch.where(keep, w.append_slots, torch.zeros_like(w.append_slots))
+        # each token's own row with the same values: the step is repeatable
+        self.app_lat = w.latent[app_idx].contiguous()
+        self.app_rope = w.rope[app_idx].contiguous()
+        self.splits = splits or mla.num_splits(T, H, K)
+        self.ws = mla.make_workspace(T, H, K, dev, self.splits)
+        self.out = torch.empty((T, H, 512), dtype=w.q.dtype, device=dev)
+        self.lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        self.valid = w.valid_slots()
+        self.gathered = self.valid * ROW_BYTES
+        self.app_rows = int(keep.sum().item())
+        self.app_bytes = (self.app_lat.numel() * self.app_lat.element_size()
+                          + self.app_rope.numel() * self.app_rope.element_size()
+                          + self.app_slots.numel() * 8 + self.app_rows * ROW_BYTES)
+        inputs = [w.q, w.indices, self.app_lat, self.app_rope, self.app_slots]
+        if w.block_table is not None:
+            inputs += [w.block_table, w.token_seq]
+        self._flush, self._inputs, self._cold = flush, inputs, cold_inputs
+
+    def flush(self):
+        """The cache sweep between steps (see the module docstring)."""
+        if self._flush is not None:
+            self._flush.sum()
+            if not self._cold:
+                for x in self._inputs:
                     x.sum()
 
-    def step(tm=None, i=0, split=False):
+    def append(self):
+        self.mla.quantize_append(self.app_lat, self.app_rope, self.app_slots, self.cache)
+
+    def decode(self, cache=None, indices=None, fmt="nvfp4", block=True):
+        w = self.w
+        self.mla.sparse_decode(w.q, self.cache if cache is None else cache,
+                               w.indices if indices is None else indices, w.sm_scale, fmt=fmt,
+                               block_table=w.block_table if block else None,
+                               token_seq=w.token_seq if block else None, block_size=w.block_size,
+                               workspace=self.ws, num_splits=self.splits, out=self.out, lse=self.lse)
+
+    def step(self, tm=None, i=0, split=False):
         if tm:
             tm.mark(i, 0)
-        mla.quantize_append(app_lat, app_rope, app_slots, cache)
+        self.append()
         if tm and split:
             tm.mark(i, 1)
-        mla.sparse_decode(w.q, cache, w.indices, w.sm_scale, block_table=w.block_table,
-                          token_seq=w.token_seq, block_size=w.block_size, workspace=ws,
-                          num_splits=splits, out=out, lse=lse)
+        self.decode()
         if tm:
             tm.mark(i, 2)
 
-    for _ in range(args.warmup):
-        do_flush()
-        step()
-    torch.cuda.synchronize()
-    # pass A, the timed region: K steps, each bracketed by HIP events, no
-    # instrumentation inside a step
-    tm = Timer(torch, args.steps)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        do_flush()
-        step(tm, i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # pass A2: the same steps with an event between the append and the decode
-    # (the split into append_us and decode_us; that event costs the step time)
-    tm2 = Timer(torch, max(20, args.steps // 2))
-    for i in range(len(tm2.ev)):
-        do_flush()
-        step(tm2, i, split=True)
-    torch.cuda.synchronize()
-    # pass B: the same steps with the library's kernel timing on (each kernel's own
-    # start/end events), for the roofline and the per-kernel figures
-    # (the decode follows its append on the GPU with no host round trip in
-    # between, as in pass A; the append's own duration is taken in a loop of
-    # its own)
-    kern_ms, app_kern_ms = [], []
+
+def _kernel_ms(mla, fn, n, flush):
+    """Durations (ms) of the last library kernel `fn` launches, each after a sweep."""
+    out = []
     mla.kernel_timing(True)
     try:
-        for i in range(max(20, args.steps // 2)):
-            do_flush()
-            mla.quantize_append(app_lat, app_rope, app_slots, cache)
-            mla.sparse_decode(w.q, cache, w.indices, w.sm_scale, block_table=w.block_table,
-                              token_seq=w.token_seq, block_size=w.block_size, workspace=ws,
-                              num_splits=splits, out=out, lse=lse)
-            kern_ms.append(mla.last_kernel_ms())
-        for i in range(max(10, args.steps // 4)):
-            do_flush()
-            mla.quantize_append(app_lat, app_rope, app_slots, cache)
-            app_kern_ms.append(mla.last_kernel_ms())
+        for _ in range(n):
+            flush()
+            fn()
+            out.append(mla.last_kernel_ms())
     finally:
         mla.kernel_timing(False)
-    step_ms = tm.spans(0, 2)
-    dec_ms = tm2.spans(1, 2)
-    app_ms = tm2.spans(0, 1)
-    res = {
-        "T": T, "H": H, "K": K, "rows": rows, "splits": splits, "valid": valid, "gathered": gathered,
-        "step_ms": statistics.mean(step_ms), "decode_ms": statistics.mean(dec_ms),
-        "decode_ms_median": statistics.median(dec_ms),
-        "decode_ms_p10": sorted(dec_ms)[len(dec_ms) // 10],
-        "decode_ms_p90": sorted(dec_ms)[(9 * len(dec_ms)) // 10],
-        "step_ms_median": statistics.median(step_ms),
-        "step_ms_p10": sorted(step_ms)[len(step_ms) // 10],
-        "step_ms_p90": sorted(step_ms)[(9 * len(step_ms)) // 10],
-        "append_ms": statistics.mean(app_ms), "wall_ms_per_iter": 1e3 * wall / args.steps,
-        "kernel_ms": statistics.mean(kern_ms), "kernel_ms_median": statistics.median(kern_ms),
-        "append_kernel_ms": statistics.mean(app_kern_ms),
-        "copy_gbs": copy_gbs,
-        "append_bytes": int(app_lat.numel() * app_lat.element_size() + app_rope.numel() * app_rope.element_size()
-                            + app_slots.numel() * 8 + int((app_slots >= 0).sum()) * ROW_BYTES),
+    return out
+
+
+def _measure(torch, mla, c: Case, steps: int, warmup: int, comparators: bool):
+    """Passes A, A2 and B (module docstring) plus the comparators for one workload."""
+    for _ in range(warmup):
+        c.flush()
+        c.step()
+    torch.cuda.synchronize()
+    tm = Timer(torch, steps)
+    for i in range(steps):
+        c.flush()
+        c.step(tm, i)
+    torch.cuda.synchronize()
+    tm2 = Timer(torch, max(10, steps // 2))
+    for i in range(len(tm2.ev)):
+        c.flush()
+        c.step(tm2, i, split=True)
+    torch.cuda.synchronize()
+    n = max(10, steps // 2)
+
+    def append_then_decode():
+        # the decode follows its append on the GPU, as in pass A; only the
+        # decode's own duration is read back
+        c.append()
+        c.decode()
+
+    kern = _kernel_ms(mla, append_then_decode, n, c.flush)
+    app_kern = _kernel_ms(mla, c.append, max(10, steps // 4), c.flush)
+    step_ms, dec_ms, app_ms = tm.spans(0, 2), tm2.spans(1, 2), tm2.spans(0, 1)
+    k_mean = statistics.mean(kern)
+    w = c.w
+    flops = 2.0 * w.heads * (576 + 512) * c.valid
+    r = {
+        "workload": DESCRIPTIONS[c.name], "tokens": w.tokens, "heads": w.heads, "topk": w.topk,
+        "q_dtype": str(w.q.dtype).replace("torch.", ""), "pool_rows": w.pool_rows,
+        "valid_slots": c.valid, "gathered_bytes": c.gathered, "splits": c.splits,
+        "us_per_step": _stats_us(step_ms),
+        "decode_us": _stats_us(dec_ms),
+        "decode_kernel_us": _stats_us(kern),
+        "gathered_gbs_per_step": round(c.gathered / (statistics.mean(step_ms) * 1e-3) / 1e9, 2),
+        "gathered_gbs_kernel": round(c.gathered / (k_mean * 1e-3) / 1e9, 2),
+        "frac_of_8tbs_kernel": round(c.gathered / (k_mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "mfma_tflops": round(flops / (k_mean * 1e-3) / 1e12, 2),
+        "mfma_frac_of_fp16_peak": round(flops / (k_mean * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
+        "append_rows": c.app_rows,
+        "append_us": round(1e3 * statistics.mean(app_ms), 3),
+        "append_kernel_us": round(1e3 * statistics.mean(app_kern), 3),
+        "append_kernel_gbs": round(c.app_bytes / (statistics.mean(app_kern) * 1e-3) / 1e9, 2),
     }
+    if comparators and c.name in TRIO_CONFIGS:
+        r["trio"] = _comparators(torch, mla, c, n)
+    return r, kern
 
-    if not args.no_comparators:
-        res["comparators"] = _comparators(args, torch, mla, w, cache, dev, splits, do_flush)
-    return res, w
 
-
-def _comparators(args, torch, mla, w, cache, dev, splits, do_flush):
-    """FP8-576 rows (same values, 576-byte rows) and the staged path
-    (gather-dequant the selected NVFP4 rows into an FP8 buffer, then FP8 decode)."""
-    T, H, K = w.tokens, w.heads, w.topk
-    n = max(10, args.steps // 2)
+def _comparators(torch, mla, c: Case, n: int):
+    """The pages' comparison at the same shapes: FP8-576 rows (same values,
+    576-byte rows) and the staged path (gather-dequant the selected NVFP4
+    rows into an FP8 buffer, then FP8 decode); kernel times in µs."""
+    w = c.w
+    T, K = w.tokens, w.topk
+    dev = c.cache.device
     c8 = torch.empty((w.pool_rows, FP8_ROW_BYTES), dtype=torch.uint8, device=dev)
     mla.fp8_quantize_append(w.latent, w.rope, torch.arange(w.pool_rows, device=dev), c8, 1.0)
-    ws = mla.make_workspace(T, H, K, dev, splits)
     staged_rows = torch.empty((T * K, FP8_ROW_BYTES), dtype=torch.uint8, device=dev)
     staged_idx = torch.empty((T, K), dtype=torch.int32, device=dev)
-    out = torch.empty((T, H, 512), dtype=w.q.dtype, device=dev)
-    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
 
-    def fp8_decode():
-        mla.sparse_decode(w.q, c8, w.indices, w.sm_scale, fmt="fp8", block_table=w.block_table,
-                          token_seq=w.token_seq, block_size=w.block_size, workspace=ws,
-                          num_splits=splits, out=out, lse=lse)
-
-    def staged(tm=None, i=0):
-        mla.gather_dequant_fp8(cache, w.indices, 1.0, block_table=w.block_table, token_seq=w.token_seq,
+    def gather():
+        mla.gather_dequant_fp8(c.cache, w.indices, 1.0, block_table=w.block_table, token_seq=w.token_seq,
                                block_size=w.block_size, rows=staged_rows, staged_indices=staged_idx)
-        if tm:
-            tm.mark(i, 1)
-        mla.sparse_decode(w.q, staged_rows, staged_idx, w.sm_scale, fmt="fp8", workspace=ws,
-                          num_splits=splits, out=out, lse=lse)
 
-    r = {}
     for _ in range(3):
-        do_flush(); fp8_decode(); do_flush(); staged()
+        c.flush(); c.decode(cache=c8, fmt="fp8"); c.flush(); gather(); c.decode(staged_rows, staged_idx, "fp8", False)
     torch.cuda.synchronize()
-    tm = Timer(torch, n)
-    for i in range(n):
-        do_flush()
-        tm.mark(i, 0)
-        fp8_decode()
-        tm.mark(i, 2)
-    torch.cuda.synchronize()
-    r["fp8_576_decode_us"] = 1e3 * statistics.mean(tm.spans(0, 2))
-    tm = Timer(torch, n)
-    for i in range(n):
-        do_flush()
-        tm.mark(i, 0)
-        staged(tm, i)
-        tm.mark(i, 2)
-    torch.cuda.synchronize()
-    r["staged_total_us"] = 1e3 * statistics.mean(tm.spans(0, 2))
-    r["staged_gather_dequant_us"] = 1e3 * statistics.mean(tm.spans(0, 1))
-    r["staged_fp8_decode_us"] = 1e3 * statistics.mean(tm.spans(1, 2))
-    # the same launches with kernel timing on: each kernel's own duration
-    k_fp8, k_gather, k_sfp8 = [], [], []
+    native = _kernel_ms(mla, c.decode, n, c.flush)
+    fp8 = _kernel_ms(mla, lambda: c.decode(cache=c8, fmt="fp8"), n, c.flush)
+    k_gather, k_sfp8 = [], []
     mla.kernel_timing(True)
     try:
-        for i in range(n):
-            do_flush()
-            fp8_decode()
-            k_fp8.append(mla.last_kernel_ms())
-            do_flush()
-            mla.gather_dequant_fp8(cache, w.indices, 1.0, block_table=w.block_table, token_seq=w.token_seq,
-                                   block_size=w.block_size, rows=staged_rows, staged_indices=staged_idx)
+        for _ in range(n):
+            c.flush()
+            gather()
             k_gather.append(mla.last_kernel_ms())
-            mla.sparse_decode(w.q, staged_rows, staged_idx, w.sm_scale, fmt="fp8", workspace=ws,
-                              num_splits=splits, out=out, lse=lse)
+            c.decode(staged_rows, staged_idx, "fp8", False)
             k_sfp8.append(mla.last_kernel_ms())
     finally:
         mla.kernel_timing(False)
-    r["fp8_576_decode_kernel_us"] = 1e3 * statistics.mean(k_fp8)
-    r["staged_gather_dequant_kernel_us"] = 1e3 * statistics.mean(k_gather)
-    r["staged_fp8_decode_kernel_us"] = 1e3 * statistics.mean(k_sfp8)
-    r["staged_total_kernel_us"] = r["staged_gather_dequant_kernel_us"] + r["staged_fp8_decode_kernel_us"]
-    return r
+    del c8, staged_rows, staged_idx
+    g, s8 = statistics.mean(k_gather), statistics.mean(k_sfp8)
+    return {"native_nvfp4_kernel_us": round(1e3 * statistics.mean(native), 3),
+            "fp8_576_kernel_us": round(1e3 * statistics.mean(fp8), 3),
+            "staged_gather_dequant_kernel_us": round(1e3 * g, 3),
+            "staged_fp8_decode_kernel_us": round(1e3 * s8, 3),
+            "staged_total_kernel_us": round(1e3 * (g + s8), 3)}
 
 
-def _cpu_baseline(w, seconds):
+def _cpu_baseline(w, seconds, tokens=None):
     """The oracle as it stands, on the host cores, over a bounded sample of the
     same workload: per pass, decode the sampled tokens' selected rows from
     their 352-byte encodings and run the FP64 attention."""
     import numpy as np
+    import torch
 
     from oracle import attention, codec
 
@@ -331,23 +325,23 @@ def _cpu_baseline(w, seconds):
     bt = None if w.block_table is None else w.block_table.cpu().numpy().astype(np.int64)
     seq = None if w.token_seq is None else w.token_seq.cpu().numpy().astype(np.int64)
     q = w.q.float().cpu().numpy().astype(np.float64)
-    tokens = list(range(w.tokens))
+    tokens = list(range(w.tokens)) if tokens is None else list(tokens)
     # the encoded rows the sample touches (setup, not timed): the pool is already encoded
-    per_tok = []
+    per_tok = {}
     for t in tokens:
         v = idx[t][idx[t] >= 0]
         rows = attention.physical_rows(v, None if seq is None else int(seq[t]), bt, w.block_size,
                                        w.pool_rows)
-        rows = rows[rows >= 0]
-        sel = __import__("torch").from_numpy(rows).to(w.latent.device)
+        sel = torch.from_numpy(rows[rows >= 0]).to(w.latent.device)
         lat16 = w.latent.index_select(0, sel).cpu().numpy().astype(np.float64)
         rope16 = w.rope.index_select(0, sel).cpu().numpy().astype(np.float64)
-        per_tok.append(codec.nvfp4_encode_rows(lat16, rope16))
+        per_tok[t] = codec.nvfp4_encode_rows(lat16, rope16)
+
     def run(limit):
         done_bytes = 0
         n_tok = 0
         t0 = time.perf_counter()
-        while True:
+        while time.perf_counter() - t0 <= limit:
             for t in tokens:
                 enc = per_tok[t]
                 lat, rope = codec.nvfp4_decode_rows(enc)
@@ -356,26 +350,24 @@ def _cpu_baseline(w, seconds):
                 n_tok += 1
                 if time.perf_counter() - t0 > limit:
                     break
-            if time.perf_counter() - t0 > limit:
-                break
         return done_bytes, n_tok, time.perf_counter() - t0
 
     done_bytes, n_tok, el = run(seconds)
     out = {
-        "value": done_bytes / el / 1e9, "unit": "GB/s", "cores": blas_threads,
+        "value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": blas_threads,
         "kind": "oracle",
-        "sample": f"{n_tok} token-passes of the {w.name} workload ({n_tok / max(1, len(tokens)):.1f} steps), "
+        "sample": f"{n_tok} token-passes over {len(tokens)} tokens of the {w.name} workload, "
                   f"NVFP4 row decode + FP64 attention, {el:.1f} s; host os.cpu_count()={os.cpu_count()}, "
                   f"affinity {len(os.sched_getaffinity(0))} cores",
-        "us_per_step": 1e6 * el * len(tokens) / max(1, n_tok),
+        "us_per_step": round(1e6 * el * w.tokens / max(1, n_tok), 1),
     }
     # the same with the BLAS pool limited to one thread (half the time budget)
     try:
         from threadpoolctl import threadpool_limits
         with threadpool_limits(1):
             b1, n1, e1 = run(seconds / 2)
-        out["single_thread"] = {"value": b1 / e1 / 1e9, "unit": "GB/s", "cores": 1,
-                                "us_per_step": 1e6 * e1 * len(tokens) / max(1, n1),
+        out["single_thread"] = {"value": round(b1 / e1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                "us_per_step": round(1e6 * e1 * w.tokens / max(1, n1), 1),
                                 "sample": f"{n1} token-passes, {e1:.1f} s"}
     except Exception:  # pragma: no cover
         pass
@@ -416,8 +408,49 @@ def _traffic(workload: str, splits: int):
     return None
 
 
-def main():
-    args = _parse()
+def _gpu_run(args):
+    import torch
+
+    import nvfp4_compressed_sparse_mla_amd as mla
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    flush = None if args.warm else torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+    if flush is not None:
+        flush.fill_(1.0)
+    copy_gbs = _copy_peak(torch, dev)
+    names = [n for n in (args.configs.split(",") if args.configs else []) if n]
+    for n in names + [args.workload]:
+        if n not in ALL_CONFIGS:
+            raise SystemExit(f"unknown workload {n!r}; known: {ALL_CONFIGS}")
+    order = [args.workload] + [n for n in names if n != args.workload]
+    head = None
+    configs = {}
+    for name in order:
+        dtypes = [torch.float16, torch.bfloat16] if name == "prefill4k" else [torch.float16]
+        for qdt in dtypes:
+            c = Case(torch, mla, name, dev, qdt, args.splits, flush, args.cold_inputs)
+            r, kern = _measure(torch, mla, c, args.steps, args.warmup, not args.no_comparators)
+            key = name if qdt == torch.float16 else f"{name}_bf16q"
+            configs[key] = r
+            print(f"[bench] {key}: kernel {r['decode_kernel_us']['mean']} us, "
+                  f"step {r['us_per_step']['mean']} us", file=sys.stderr, flush=True)
+            if name == args.workload and head is None:
+                head = (c, r, kern)
+                if not args.no_cpu_baseline:
+                    r["cpu_baseline"] = _cpu_baseline(c.w, args.cpu_seconds)
+            elif name == "prefill4k" and qdt == torch.float16 and not args.no_cpu_baseline:
+                # the oracle once at the prefill chunk, on 12 of its tokens
+                r["cpu_baseline"] = _cpu_baseline(c.w, min(6.0, args.cpu_seconds),
+                                                  tokens=[b * 1024 + j for b in range(4) for j in (0, 511, 1023)])
+            if head is None or c is not head[0]:
+                del c
+                torch.cuda.empty_cache()
+    return head, configs, copy_gbs
+
+
+def main(argv=None):
+    args = _parse(argv)
     if args.calibrate_copy:
         _copy_calibration(args.calibrate_copy)
         return
@@ -427,34 +460,24 @@ def main():
                                    "by token/sequence or by head with no exchange, and no multi-GPU "
                                    "figure is produced", "n_gpus": args.gpus}))
         sys.exit(2)
-    res, w = _gpu_run(args)
-    # roofline: algorithmic bytes of one launch over the kernel's own duration
-    # (HIP events recorded at kernel start and end by hipExtLaunchKernel)
-    achieved = res["gathered"] / (res["kernel_ms"] * 1e-3) / 1e9
-    # scores (576) and values (512) per valid slot and head, 2 flops per multiply-add
-    mfma_flops = 2.0 * res["H"] * (576 + 512) * res["valid"]
-    traffic = None if (args.splits or args.warm) else _traffic(args.workload, res["splits"])
+    (c, r, kern), configs, copy_gbs = _gpu_run(args)
+    k_ms = statistics.mean(kern)
+    # roofline: algorithmic bytes of one launch over the kernel's own mean
+    # duration (HIP events recorded at kernel start and end by hipExtLaunchKernel)
+    achieved = c.gathered / (k_ms * 1e-3) / 1e9
+    traffic = None if (args.splits or args.warm) else _traffic(args.workload, c.splits)
+    step_s = r["us_per_step"]["mean"] * 1e-6
     line = {
         "metric": METRIC,
-        "value": round(res["gathered"] / (res["step_ms"] * 1e-3) / 1e9, 2),
+        "value": round(c.gathered / step_s / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(res["step_ms"], 5),
-        "us_per_step": round(1e3 * res["step_ms"], 3),
-        "us_per_step_median": round(1e3 * res["step_ms_median"], 3),
-        "us_per_step_p10_p90": [round(1e3 * res["step_ms_p10"], 3), round(1e3 * res["step_ms_p90"], 3)],
-        "decode_kernel_us": round(1e3 * res["kernel_ms"], 3),
-        "decode_kernel_us_median": round(1e3 * res["kernel_ms_median"], 3),
-        "decode_us": round(1e3 * res["decode_ms"], 3),
-        "decode_us_median": round(1e3 * res["decode_ms_median"], 3),
-        "decode_us_p10_p90": [round(1e3 * res["decode_ms_p10"], 3), round(1e3 * res["decode_ms_p90"], 3)],
-        "append_us": round(1e3 * res["append_ms"], 3),
-        "append_kernel_us": round(1e3 * res["append_kernel_ms"], 3),
-        "append_kernel_gbs": round(res["append_bytes"] / (res["append_kernel_ms"] * 1e-3) / 1e9, 2),
-        "mfma_tflops": round(mfma_flops / (res["kernel_ms"] * 1e-3) / 1e12, 2),
-        "mfma_frac_of_fp16_peak": round(mfma_flops / (res["kernel_ms"] * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
+        "ms_per_step": round(step_s * 1e3, 5),
+        "us_per_step": r["us_per_step"]["mean"],
+        "decode_kernel_us": r["decode_kernel_us"]["mean"],
+        "append_kernel_us": r["append_kernel_us"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -463,23 +486,22 @@ def main():
         "cache_state": "warm" if args.warm else (
             "cold (1 GiB sweep between steps, inputs included)" if args.cold_inputs else
             "cold rows (1 GiB sweep between steps; q, index lists, block table and new rows re-read after it)"),
-        "config": {"workload": f"{args.workload}: {DESCRIPTIONS.get(args.workload, '')}",
-                   "tokens": res["T"], "heads": res["H"], "topk": res["K"], "pool_rows": res["rows"],
-                   "valid_slots": res["valid"], "gathered_bytes": res["gathered"],
-                   "splits": res["splits"], "cache": "nvfp4-352"},
+        "config": {"workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}",
+                   "tokens": c.w.tokens, "heads": c.w.heads, "topk": c.w.topk, "pool_rows": c.w.pool_rows,
+                   "valid_slots": c.valid, "gathered_bytes": c.gathered, "splits": c.splits,
+                   "cache": "nvfp4-352"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "copy_peak_measured": res["copy_gbs"],
-                     "frac_of_copy_peak": round(achieved / res["copy_gbs"], 4),
+                     "copy_peak_measured": copy_gbs,
+                     "frac_of_copy_peak": round(achieved / copy_gbs, 4),
                      "traffic": traffic["total"] if traffic else None,
                      "traffic_read_write": [traffic["read"], traffic["write"]] if traffic else None,
-                     "kernel": "sparse_decode_kernel", "bytes_per_launch": res["gathered"],
-                     "kernel_us": round(1e3 * res["kernel_ms"], 3)},
+                     "kernel": "sparse_decode_kernel", "bytes_per_launch": c.gathered,
+                     "kernel_us": round(1e3 * k_ms, 3)},
+        "configs": configs,
     }
-    if "comparators" in res:
-        line["comparators"] = {k: round(v, 3) for k, v in res["comparators"].items()}
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = _cpu_baseline(w, args.cpu_seconds)
+    if "cpu_baseline" in r:
+        line["cpu_baseline"] = r["cpu_baseline"]
     print(json.dumps(line), flush=True)
 
 
