@@ -186,6 +186,40 @@ int mla_sparse_decode(const void* q, int q_dtype, int64_t num_tokens,
                       int32_t num_splits, void* stream);
 
 /*
+ * mla_sparse_decode_noalloc -- mla_sparse_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops or
+ * harnesses that forbid hipMalloc).  It computes exactly what
+ * mla_sparse_decode computes with the same arguments and split count, and
+ * allocates nothing: its workspace is a scratch array inside the library,
+ * one per GPU, held until the process ends.
+ *
+ * Arguments are those of mla_sparse_decode without the workspace.  Limits
+ * of the scratch: at most MLA_NOALLOC_MAX_UNITS (token, head group) units
+ * (T * H / 32 rounded up to H >= 32 groups), and the split partials
+ * (T * ceil(H/32) * num_splits * 32 KiB plus their log-sum-exps) within
+ * MLA_NOALLOC_SCRATCH_BYTES - 256 KiB; a call beyond either returns
+ * MLA_ERR_WORKSPACE and enqueues nothing.  The first call on a device also
+ * enqueues, on its stream and before its decode, a small kernel that zeroes
+ * the scratch's arrival counters.
+ *
+ * Every call on a GPU shares that GPU's scratch: calls that overlap in time
+ * on one GPU (different streams without ordering between them) race and
+ * give wrong results.  Calls ordered on one stream are safe.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define MLA_NOALLOC_MAX_UNITS 65536
+int mla_sparse_decode_noalloc(const void* q, int q_dtype, int64_t num_tokens,
+                              int32_t num_heads, int64_t q_stride_t, int64_t q_stride_h,
+                              const uint8_t* cache, int cache_fmt, int64_t cache_rows,
+                              float kv_scale,
+                              const int32_t* indices, int32_t topk, int64_t idx_stride_t,
+                              const int32_t* block_table, int32_t block_size,
+                              int64_t bt_stride, int32_t bt_rows, int32_t bt_cols,
+                              const int32_t* token_seq,
+                              float sm_scale, void* out, float* lse,
+                              int32_t num_splits, void* stream);
+
+/*
  * mla_nvfp4_gather_dequant_fp8 -- first step of the staged comparator the
  * write-up measures against its native kernel (mo.ai.kr article, KV-cache
  * section; wireai.ir, 4-bit-caches section): unpack the selected NVFP4

@@ -8,6 +8,7 @@ PyTorch only provides device memory and streams.
     quantize_append(latent, rope, slots, cache)        352-byte NVFP4 rows
     fp8_quantize_append(latent, rope, slots, cache)    576-byte FP8 rows
     sparse_decode(q, cache, indices, sm_scale, ...)    -> (out, lse)
+    sparse_decode_noalloc(q, cache, indices, ...)      the same without a workspace
     gather_dequant_fp8(cache, indices, ...)            staged comparator step
 """
 
@@ -137,11 +138,8 @@ def make_workspace(tokens: int, heads: int, topk: int, device, splits: int = 0) 
     return torch.zeros(workspace_size(tokens, heads, topk, splits), dtype=torch.uint8, device=device)
 
 
-def sparse_decode(q: torch.Tensor, cache: torch.Tensor, indices: torch.Tensor, sm_scale: float, *,
-                  fmt: str = "nvfp4", kv_scale: float = 1.0, block_table=None, token_seq=None,
-                  block_size: int = 64, workspace=None, num_splits: int = 0, out=None, lse=None):
-    """Sparse MLA decode; returns (out [T, H, 512] in q's dtype, lse [T, H] float32)."""
-    lib = load()
+def _decode_args(q, cache, indices, fmt, block_table, token_seq, out, lse, workspace):
+    """Checked tensors and the C arguments shared by both decode entry points."""
     dev = _device_of(q, "q")
     if q.dim() != 3 or q.shape[2] != QK_DIM or q.stride(2) != 1:
         raise ValueError("q must be [T, H, 576] with unit last stride")
@@ -154,7 +152,6 @@ def sparse_decode(q: torch.Tensor, cache: torch.Tensor, indices: torch.Tensor, s
     _same_device(dev, cache=cache, indices=indices, workspace=workspace, out=out, lse=lse)
     if indices.dtype != torch.int32 or indices.dim() != 2 or indices.shape[0] != T or indices.stride(1) != 1:
         raise ValueError("indices must be int32 [T, topk] with unit last stride")
-    topk = indices.shape[1]
     bt_ptr, ts_ptr, bt_stride, bt_rows, bt_cols, token_seq = _block_table_args(block_table, token_seq, T, dev)
     if out is None:
         out = torch.empty((T, H, LATENT_DIM), dtype=q.dtype, device=dev)
@@ -162,6 +159,18 @@ def sparse_decode(q: torch.Tensor, cache: torch.Tensor, indices: torch.Tensor, s
     if lse is None:
         lse = torch.empty((T, H), dtype=torch.float32, device=dev)
     _exact(lse, "lse", (T, H), torch.float32)
+    return dev, fmt_code, (bt_ptr, ts_ptr, bt_stride, bt_rows, bt_cols, token_seq), out, lse
+
+
+def sparse_decode(q: torch.Tensor, cache: torch.Tensor, indices: torch.Tensor, sm_scale: float, *,
+                  fmt: str = "nvfp4", kv_scale: float = 1.0, block_table=None, token_seq=None,
+                  block_size: int = 64, workspace=None, num_splits: int = 0, out=None, lse=None):
+    """Sparse MLA decode; returns (out [T, H, 512] in q's dtype, lse [T, H] float32)."""
+    lib = load()
+    dev, fmt_code, bt, out, lse = _decode_args(q, cache, indices, fmt, block_table, token_seq, out, lse,
+                                               workspace)
+    bt_ptr, ts_ptr, bt_stride, bt_rows, bt_cols, _keep = bt
+    T, H, topk = q.shape[0], q.shape[1], indices.shape[1]
     if workspace is None:
         workspace = make_workspace(T, H, topk, dev, num_splits)
     if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous():
@@ -174,6 +183,26 @@ def sparse_decode(q: torch.Tensor, cache: torch.Tensor, indices: torch.Tensor, s
         float(sm_scale), out.data_ptr(), lse.data_ptr(),
         workspace.data_ptr(), workspace.numel(), int(num_splits), _stream(q))
     check(st, "mla_sparse_decode")
+    return out, lse
+
+
+def sparse_decode_noalloc(q: torch.Tensor, cache: torch.Tensor, indices: torch.Tensor, sm_scale: float,
+                          out: torch.Tensor, lse: torch.Tensor, *, fmt: str = "nvfp4", kv_scale: float = 1.0,
+                          block_table=None, token_seq=None, block_size: int = 64, num_splits: int = 0):
+    """``sparse_decode`` without a workspace, for callers that cannot allocate:
+    the library's own per-GPU scratch array serves as workspace.  The caller
+    passes out and lse; calls that overlap in time on one GPU race."""
+    lib = load()
+    _, fmt_code, bt, out, lse = _decode_args(q, cache, indices, fmt, block_table, token_seq, out, lse, None)
+    bt_ptr, ts_ptr, bt_stride, bt_rows, bt_cols, _keep = bt
+    T, H, topk = q.shape[0], q.shape[1], indices.shape[1]
+    st = lib.mla_sparse_decode_noalloc(
+        q.data_ptr(), _dtype_code(q), T, H, q.stride(0), q.stride(1),
+        cache.data_ptr(), fmt_code, cache.shape[0], float(kv_scale),
+        indices.data_ptr(), topk, indices.stride(0),
+        bt_ptr, int(block_size), bt_stride, bt_rows, bt_cols, ts_ptr,
+        float(sm_scale), out.data_ptr(), lse.data_ptr(), int(num_splits), _stream(q))
+    check(st, "mla_sparse_decode_noalloc")
     return out, lse
 
 

@@ -24,6 +24,11 @@ SIGNATURES = {
                                   c_vp, c_i32, c_i64,
                                   c_vp, c_i32, c_i64, c_i32, c_i32, c_vp,
                                   c_f32, c_vp, c_vp, c_vp, c_size, c_i32, c_vp]),
+    "mla_sparse_decode_noalloc": (c_int, [c_vp, c_int, c_i64, c_i32, c_i64, c_i64,
+                                          c_vp, c_int, c_i64, c_f32,
+                                          c_vp, c_i32, c_i64,
+                                          c_vp, c_i32, c_i64, c_i32, c_i32, c_vp,
+                                          c_f32, c_vp, c_vp, c_i32, c_vp]),
     "mla_nvfp4_gather_dequant_fp8": (c_int, [c_vp, c_i64, c_vp, c_i64, c_i32, c_i64,
                                              c_vp, c_i32, c_i64, c_i32, c_i32, c_vp,
                                              c_f32, c_vp, c_vp, c_vp]),

@@ -7,6 +7,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -60,6 +62,144 @@ int quantize_checks(const void* latent, int64_t ls, const void* rope, int64_t rs
   if (!aligned16(latent) || !aligned16(rope) || !aligned16(cache)) return MLA_ERR_INVALID_ARG;
   if (n > (int64_t)0x7FFFFFFF * 8) return MLA_ERR_INVALID_ARG;
   return MLA_OK;
+}
+
+// Size of the allocation-free entry point's scratch array (see below): the
+// arrival counters of up to kScratchCounters (token, head group) units,
+// then the split partials.
+constexpr size_t kScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+constexpr int64_t kScratchCounters = MLA_NOALLOC_MAX_UNITS;  // (token, head group) units per call
+constexpr size_t kScratchCounterBytes = kScratchCounters * sizeof(uint32_t);
+static_assert(kScratchCounterBytes % 256 == 0, "partials stay 256-byte aligned");
+
+// Shared body of the two decode entry points.  With static_layout the
+// workspace is the library's own scratch array: the arrival counters sit at
+// a fixed place (only the arrival protocol writes them, and every completed
+// call leaves them at zero, so they stay zero between calls of any size)
+// and the split partials follow them.  check_only stops after the argument
+// checks.
+int decode_call(const void* q, int q_dtype, int64_t num_tokens, int32_t num_heads,
+                int64_t q_stride_t, int64_t q_stride_h, const uint8_t* cache, int cache_fmt,
+                int64_t cache_rows, float kv_scale, const int32_t* indices, int32_t topk,
+                int64_t idx_stride_t, const int32_t* block_table, int32_t block_size,
+                int64_t bt_stride, int32_t bt_rows, int32_t bt_cols, const int32_t* token_seq,
+                float sm_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                int32_t num_splits, void* stream, bool static_layout, bool check_only = false) {
+  if (q_dtype != MLA_F16 && q_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (cache_fmt != MLA_CACHE_NVFP4_352 && cache_fmt != MLA_CACHE_FP8_576) return MLA_ERR_UNSUPPORTED;
+  const int G = head_groups(num_heads);
+  if (G == 0) return MLA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || topk < 1 || topk > MLA_MAX_TOPK) return MLA_ERR_INVALID_ARG;
+  if (num_splits < 0 || num_splits > 64) return MLA_ERR_INVALID_ARG;
+  if (cache_rows < 0 || cache_rows > 0x7FFFFFFF) return MLA_ERR_INVALID_ARG;
+  if (!isfinite(sm_scale)) return MLA_ERR_INVALID_ARG;
+  if (cache_fmt == MLA_CACHE_FP8_576 && !pow2_scale(kv_scale)) return MLA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return MLA_OK;
+  if (!q || !cache || !indices || !out) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(cache) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
+  if (q_stride_h < MLA_QK_DIM || (q_stride_h % 8) || (q_stride_t % 8) ||
+      q_stride_t < (int64_t)num_heads * q_stride_h)
+    return MLA_ERR_INVALID_ARG;
+  if (idx_stride_t < topk) return MLA_ERR_INVALID_ARG;
+  if (block_table) {
+    if (!token_seq || block_size < 1 || bt_rows < 1 || bt_cols < 1 || bt_stride < bt_cols)
+      return MLA_ERR_INVALID_ARG;
+  }
+  const int S = num_splits ? num_splits : mla::decode_auto_splits(num_tokens, num_heads, topk);
+  // the grid (units rounded up to 8, times S workgroups of 256 threads)
+  // must hold fewer than 2^32 work-items
+  if ((num_tokens * G + 7) / 8 * 8 * S >= (int64_t)1 << 24) return MLA_ERR_INVALID_ARG;
+  const int64_t tg = num_tokens * G;
+  uint32_t* counters;
+  float* part_lse;
+  _Float16* part_o;
+  if (static_layout) {
+    if (tg > kScratchCounters) return MLA_ERR_WORKSPACE;
+    const size_t parts = S > 1 ? mla::decode_workspace_bytes(num_tokens, num_heads, S) -
+                                     mla::decode_workspace_bytes(num_tokens, num_heads, 1)
+                               : 0;
+    if (kScratchCounterBytes + parts > kScratchBytes) return MLA_ERR_WORKSPACE;
+    if (check_only) return MLA_OK;
+    counters = reinterpret_cast<uint32_t*>(workspace);
+    part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + kScratchCounterBytes);
+  } else {
+    const size_t need = mla::decode_workspace_bytes(num_tokens, num_heads, S);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
+    if (check_only) return MLA_OK;
+    const size_t ctr = ((size_t)tg * sizeof(uint32_t) + 255) & ~(size_t)255;
+    counters = reinterpret_cast<uint32_t*>(workspace);
+    part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ctr);
+  }
+  const size_t pl = ((size_t)tg * S * 32 * sizeof(float) + 255) & ~(size_t)255;
+  part_o = reinterpret_cast<_Float16*>(reinterpret_cast<char*>(part_lse) + pl);
+
+  mla::DecodeParams p;
+  p.q = q;
+  p.q_st = q_stride_t;
+  p.q_sh = q_stride_h;
+  p.T = num_tokens;
+  p.H = num_heads;
+  p.G = G;
+  p.cache = cache;
+  p.cache_rows = cache_rows;
+  p.kv_scale = cache_fmt == MLA_CACHE_FP8_576 ? kv_scale : 1.0f;
+  p.idx = indices;
+  p.topk = topk;
+  p.idx_st = idx_stride_t;
+  p.bt = block_table;
+  p.bs = block_table ? block_size : 1;
+  p.bs_log2 = (p.bs & (p.bs - 1)) == 0 ? __builtin_ctz((unsigned)p.bs) : -1;
+  p.bt_cols = block_table ? bt_cols : 0;
+  p.bt_rows = block_table ? bt_rows : 0;
+  p.bt_st = block_table ? bt_stride : 0;
+  p.tok_seq = block_table ? token_seq : nullptr;
+  p.sm_log2 = fabsf(sm_scale) * 1.4426950408889634f * p.kv_scale;
+  p.q_neg = sm_scale < 0.0f;
+  p.out = out;
+  p.lse = lse;
+  p.counters = counters;
+  p.part_lse = part_lse;
+  p.part_o = part_o;
+  p.S = S;
+  const mla::KernelEvents ev = timing_events();
+  return launched(mla::launch_decode(p, cache_fmt, q_dtype == MLA_BF16, (hipStream_t)stream, ev), ev);
+}
+
+// ---------------------------------------------------------------- static scratch
+//
+// The allocation-free decode entry point keeps its workspace in this array
+// instead of one the caller allocates.  Each GPU the library runs on holds
+// its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: only the address that
+// hipGetSymbolAddress returns for the current device may be used.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  int status = MLA_ERR_HIP;
+};
+constexpr int kMaxDevices = 64;
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch array.  The first call on
+// a device looks the address up (with that device current) and zero-fills
+// the counter region with a kernel on the caller's stream, ahead of the
+// caller's decode on that stream.
+int static_scratch(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return;
+    if (mla::launch_zero_u32(static_cast<uint32_t*>(p), (size_t)kScratchCounters, stream) != hipSuccess)
+      return;
+    slot.ptr = p;
+    slot.status = MLA_OK;
+  });
+  *ptr = slot.ptr;
+  return slot.status;
 }
 
 }  // namespace
@@ -128,66 +268,33 @@ int mla_sparse_decode(const void* q, int q_dtype, int64_t num_tokens, int32_t nu
                       float sm_scale,
                       void* out, float* lse, void* workspace, size_t workspace_bytes,
                       int32_t num_splits, void* stream) {
-  if (q_dtype != MLA_F16 && q_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
-  if (cache_fmt != MLA_CACHE_NVFP4_352 && cache_fmt != MLA_CACHE_FP8_576) return MLA_ERR_UNSUPPORTED;
-  const int G = head_groups(num_heads);
-  if (G == 0) return MLA_ERR_UNSUPPORTED;
-  if (num_tokens < 0 || topk < 1 || topk > MLA_MAX_TOPK) return MLA_ERR_INVALID_ARG;
-  if (num_splits < 0 || num_splits > 64) return MLA_ERR_INVALID_ARG;
-  if (cache_rows < 0 || cache_rows > 0x7FFFFFFF) return MLA_ERR_INVALID_ARG;
-  if (!isfinite(sm_scale)) return MLA_ERR_INVALID_ARG;
-  if (cache_fmt == MLA_CACHE_FP8_576 && !pow2_scale(kv_scale)) return MLA_ERR_INVALID_ARG;
-  if (num_tokens == 0) return MLA_OK;
-  if (!q || !cache || !indices || !out) return MLA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(cache) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
-  if (q_stride_h < MLA_QK_DIM || (q_stride_h % 8) || (q_stride_t % 8) ||
-      q_stride_t < (int64_t)num_heads * q_stride_h)
-    return MLA_ERR_INVALID_ARG;
-  if (idx_stride_t < topk) return MLA_ERR_INVALID_ARG;
-  if (block_table) {
-    if (!token_seq || block_size < 1 || bt_rows < 1 || bt_cols < 1 || bt_stride < bt_cols)
-      return MLA_ERR_INVALID_ARG;
-  }
-  const int S = num_splits ? num_splits : mla::decode_auto_splits(num_tokens, num_heads, topk);
-  // the grid (units rounded up to 8, times S workgroups of 256 threads)
-  // must hold fewer than 2^32 work-items
-  if ((num_tokens * G + 7) / 8 * 8 * S >= (int64_t)1 << 24) return MLA_ERR_INVALID_ARG;
-  const size_t need = mla::decode_workspace_bytes(num_tokens, num_heads, S);
-  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
+  return decode_call(q, q_dtype, num_tokens, num_heads, q_stride_t, q_stride_h, cache, cache_fmt,
+                     cache_rows, kv_scale, indices, topk, idx_stride_t, block_table, block_size,
+                     bt_stride, bt_rows, bt_cols, token_seq, sm_scale, out, lse, workspace,
+                     workspace_bytes, num_splits, stream, false);
+}
 
-  mla::DecodeParams p;
-  p.q = q;
-  p.q_st = q_stride_t;
-  p.q_sh = q_stride_h;
-  p.T = num_tokens;
-  p.H = num_heads;
-  p.G = G;
-  p.cache = cache;
-  p.cache_rows = cache_rows;
-  p.kv_scale = cache_fmt == MLA_CACHE_FP8_576 ? kv_scale : 1.0f;
-  p.idx = indices;
-  p.topk = topk;
-  p.idx_st = idx_stride_t;
-  p.bt = block_table;
-  p.bs = block_table ? block_size : 1;
-  p.bs_log2 = (p.bs & (p.bs - 1)) == 0 ? __builtin_ctz((unsigned)p.bs) : -1;
-  p.bt_cols = block_table ? bt_cols : 0;
-  p.bt_rows = block_table ? bt_rows : 0;
-  p.bt_st = block_table ? bt_stride : 0;
-  p.tok_seq = block_table ? token_seq : nullptr;
-  p.sm_log2 = fabsf(sm_scale) * 1.4426950408889634f * p.kv_scale;
-  p.q_neg = sm_scale < 0.0f;
-  p.out = out;
-  p.lse = lse;
-  const int64_t tg = num_tokens * G;
-  size_t ctr = ((size_t)tg * sizeof(uint32_t) + 255) & ~(size_t)255;
-  size_t pl = ((size_t)tg * S * 32 * sizeof(float) + 255) & ~(size_t)255;
-  p.counters = reinterpret_cast<uint32_t*>(workspace);
-  p.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ctr);
-  p.part_o = reinterpret_cast<_Float16*>(reinterpret_cast<char*>(workspace) + ctr + pl);
-  p.S = S;
-  const mla::KernelEvents ev = timing_events();
-  return launched(mla::launch_decode(p, cache_fmt, q_dtype == MLA_BF16, (hipStream_t)stream, ev), ev);
+int mla_sparse_decode_noalloc(const void* q, int q_dtype, int64_t num_tokens, int32_t num_heads,
+                              int64_t q_stride_t, int64_t q_stride_h, const uint8_t* cache,
+                              int cache_fmt, int64_t cache_rows, float kv_scale,
+                              const int32_t* indices, int32_t topk, int64_t idx_stride_t,
+                              const int32_t* block_table, int32_t block_size, int64_t bt_stride,
+                              int32_t bt_rows, int32_t bt_cols, const int32_t* token_seq,
+                              float sm_scale, void* out, float* lse, int32_t num_splits,
+                              void* stream) {
+  // argument errors are reported before the scratch is set up
+  const int st = decode_call(q, q_dtype, num_tokens, num_heads, q_stride_t, q_stride_h, cache,
+                             cache_fmt, cache_rows, kv_scale, indices, topk, idx_stride_t,
+                             block_table, block_size, bt_stride, bt_rows, bt_cols, token_seq,
+                             sm_scale, out, lse, nullptr, 0, num_splits, stream, true, true);
+  if (st != MLA_OK || num_tokens == 0) return st;
+  void* scratch_ptr = nullptr;
+  const int s2 = static_scratch((hipStream_t)stream, &scratch_ptr);
+  if (s2 != MLA_OK) return s2;
+  return decode_call(q, q_dtype, num_tokens, num_heads, q_stride_t, q_stride_h, cache, cache_fmt,
+                     cache_rows, kv_scale, indices, topk, idx_stride_t, block_table, block_size,
+                     bt_stride, bt_rows, bt_cols, token_seq, sm_scale, out, lse, scratch_ptr,
+                     kScratchBytes, num_splits, stream, true);
 }
 
 int mla_kernel_timing(int enable) {

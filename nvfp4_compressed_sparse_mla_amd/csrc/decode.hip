@@ -1150,6 +1150,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   }
 }
 
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
 // ------------------------------------------------------------------ host side
 
 namespace {
@@ -1167,6 +1171,13 @@ int device_cus() {
 }
 
 }  // namespace
+
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
 
 int decode_auto_splits(int64_t T, int H, int topk) {
   const int G = H <= kHG ? 1 : H / kHG;

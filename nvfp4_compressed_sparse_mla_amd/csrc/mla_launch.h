@@ -48,6 +48,8 @@ struct DecodeParams {
 };
 
 int decode_auto_splits(int64_t T, int H, int topk);
+// n zero words at p, by a kernel on `stream` (no memset node in a captured graph)
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream);
 size_t decode_workspace_bytes(int64_t T, int H, int S);
 
 hipError_t launch_decode(const DecodeParams& p, int fmt, bool bf16, hipStream_t stream,

@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -127,3 +127,20 @@ def test_gather_dequant_rejects_bad_arguments(lib):
     assert f(0x1000, 10, 0x2000, 1, 0, 8, None, 64, 0, 0, 0, None, ctypes.c_float(1.0), 0x3000, 0x4000, None) == INVALID
     assert f(0x1000, 10, 0x2000, 0, 8, 8, None, 64, 0, 0, 0, None, ctypes.c_float(1.0), 0x3000, 0x4000, None) == OK
     assert f(0x1000, 10, None, 1, 8, 8, None, 64, 0, 0, 0, None, ctypes.c_float(1.0), 0x3000, 0x4000, None) == INVALID
+
+
+def test_noalloc_decode_rejects_bad_arguments_and_oversized_calls(lib):
+    """Argument and scratch-size errors come back before any HIP call."""
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced: every case fails its checks first
+
+    def call(T, H, topk, splits, fmt=0):
+        return lib.mla_sparse_decode_noalloc(fake, 0, T, H, H * 576, 576, fake, fmt, 1000, 1.0,
+                                             fake, topk, topk, None, 64, 0, 0, 0, None,
+                                             0.1, fake, fake, splits, None)
+    assert call(0, 32, 16, 1) == OK
+    assert call(4, 33, 16, 1) == UNSUPPORTED
+    assert call(4, 32, 0, 1) == INVALID
+    assert call(4, 32, 16, 1, fmt=7) == UNSUPPORTED
+    assert call(70000, 32, 2048, 1) == WORKSPACE        # more units than arrival counters
+    assert call(1000, 32, 2048, 2) == WORKSPACE         # partials past the scratch array
+    assert call(300, 32, 2048, 4) == WORKSPACE
