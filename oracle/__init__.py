@@ -14,6 +14,8 @@ the format definitions and the attention formula:
                     in numpy FP64 with exact comparisons.
 * ``attention``  -- sparse MLA decode over the selected rows, dense softmax
                     in FP64.
+* ``indexer``    -- the sparse indexer's exact scores and per-token top-k
+                    position lists.
 
 Sources: the Prime Inference write-up ("Prime Inference: Fast, Reliable
 Serving for Frontier Open Models", sections "Making room for low-latency
@@ -23,4 +25,4 @@ wireai.ir, section on 4-bit caches).  Where those pages leave a step
 open, the reading taken is stated at the function that takes it.
 """
 
-from . import codec, attention  # noqa: F401
+from . import codec, attention, indexer  # noqa: F401
