@@ -25,7 +25,8 @@ the order of the list.  Readings taken:
       exactly, in any order.
 * X3  Token t sees positions 0 .. ctx[t]-1 of its sequence (causal: the
       positions cached before it, plus its own where the caller counts it).
-* X4  The list holds the min(k, ctx[t]) positions with the largest scores;
+* X4  The list holds the min(k, n) positions with the largest scores, n the
+      number of candidate positions (X3, X6);
       equal scores go to the smaller position.  It is written in ascending
       position order and padded with -1 to width k (any negative index is a
       masked pad for the attention, reading A2).
@@ -34,6 +35,10 @@ the order of the list.  Readings taken:
       from base[t]), as the decode's index lists do for contiguous pools;
       with a block table it holds logical positions, and key p of sequence b
       lives at row block_table[b, p // bs] * bs + p % bs (reading A4).
+* X6  A position that names no key row (a negative or past-the-pool row, a
+      block past the table's width, an unassigned block entry, a sequence
+      id outside the table) is not a candidate, as such a slot is masked in
+      the attention (reading A8).
 """
 
 from __future__ import annotations
@@ -45,13 +50,26 @@ from .codec import e4m3_decode
 KEY_DIM = 128
 
 
-def key_rows(positions, seq, base, block_table, block_size):
-    """Physical key rows of a sequence's positions (X5)."""
+def key_rows(positions, seq, base, block_table, block_size, n_rows):
+    """Physical key rows of a sequence's positions, -1 where none (X5, X6)."""
     p = np.asarray(positions, dtype=np.int64)
+    rows = np.full(p.shape, -1, dtype=np.int64)
     if block_table is None:
-        return base + p
+        r = base + p
+        ok = (r >= 0) & (r < n_rows)
+        rows[ok] = r[ok]
+        return rows
     bt = np.asarray(block_table, dtype=np.int64)
-    return bt[seq, p // block_size] * block_size + p % block_size
+    if seq is None or not 0 <= int(seq) < bt.shape[0]:
+        return rows
+    blk = p // block_size
+    entry = np.full(p.shape, -1, dtype=np.int64)
+    inside = blk < bt.shape[1]
+    entry[inside] = bt[int(seq), blk[inside]]
+    r = entry * block_size + p % block_size
+    ok = (entry >= 0) & (r < n_rows)
+    rows[ok] = r[ok]
+    return rows
 
 
 def scores(q_code, key_codes):
@@ -97,7 +115,8 @@ def indexer_topk(q_codes, keys, ctx, k, base=None, block_table=None, token_seq=N
             continue
         seq = None if token_seq is None else int(token_seq[t])
         b = 0 if base is None else int(base[t])
-        rows = key_rows(np.arange(n), seq, b, block_table, block_size)
-        sel = topk_positions(scores(q_codes[t], keys[rows]), k)
+        rows = key_rows(np.arange(n), seq, b, block_table, block_size, keys.shape[0])
+        cand = np.nonzero(rows >= 0)[0]                            # X6
+        sel = cand[topk_positions(scores(q_codes[t], keys[rows[cand]]), k)]
         out[t, :sel.shape[0]] = sel if block_table is not None else sel + b
     return out

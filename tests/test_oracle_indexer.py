@@ -115,10 +115,7 @@ def _paged(bs, seed):
 
 def _paged_matches(bs, seed):
     pool, bt, seq_keys, q, token_seq, tctx = _paged(bs, seed)
-    try:
-        got = indexer.indexer_topk(q, pool, tctx, 8, block_table=bt, token_seq=token_seq, block_size=bs)
-    except IndexError:                     # a wrong mapping may also leave the table
-        return False
+    got = indexer.indexer_topk(q, pool, tctx, 8, block_table=bt, token_seq=token_seq, block_size=bs)
     for t in range(3):
         want = indexer.indexer_topk(q[t:t + 1], seq_keys[token_seq[t]], tctx[t:t + 1], 8,
                                     base=np.zeros(1, np.int64))
@@ -157,13 +154,37 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         assert got[0].tolist() != [7, 12, 25, 30]
     monkeypatch.setattr(indexer, "topk_positions", good_topk)
 
-    def swapped(positions, seq, base, block_table, block_size):
+    def swapped(positions, seq, base, block_table, block_size, n_rows):
         p = np.asarray(positions, dtype=np.int64)
         if block_table is not None:                      # the paged path only
             p = (p % block_size) * block_size + p // block_size
-        return good_rows(p, seq, base, block_table, block_size)
+        return good_rows(p, seq, base, block_table, block_size, n_rows)
 
     monkeypatch.setattr(indexer, "key_rows", swapped)
     assert not _paged_matches(4, 14)
     monkeypatch.setattr(indexer, "key_rows", good_rows)
     assert _paged_matches(4, 14)
+
+
+def test_positions_without_a_key_row_are_not_candidates():
+    """X6: past the pool, unassigned blocks, blocks past the table and an
+    unknown sequence contribute no candidate; the rest is the top-k of the
+    positions that do name a row."""
+    rng = np.random.default_rng(30)
+    keys = _codes(rng, (64, 128))
+    q = _codes(rng, (4, 128))
+    # contiguous: positions 0..39 from base 40 -> rows 40..79, rows >= 64 do not exist
+    got = indexer.indexer_topk(q[:1], keys, [40], 30, base=np.array([40]))
+    want = indexer.indexer_topk(q[:1], keys[40:], [24], 30, base=np.zeros(1, np.int64))
+    assert np.array_equal(got[0], np.where(want[0] >= 0, want[0] + 40, -1))
+    # paged, block size 8: sequence 0 has blocks 2, -1, 5 (width 3)
+    bt = np.array([[2, -1, 5]])
+    got = indexer.indexer_topk(q[1:4], keys, [40, 20, 20], 12, block_table=bt,
+                               token_seq=np.array([0, 0, 3]), block_size=8)
+    pos = np.array(list(range(8)) + list(range(16, 24)))        # positions with a row
+    rows = np.concatenate([np.arange(16, 24), np.arange(40, 48)])
+    s = indexer.scores(q[1], keys[rows])
+    want = np.sort(pos[np.lexsort((pos, -s))[:12]])
+    assert got[0].tolist() == want.tolist()
+    assert got[1, :12].tolist() == sorted(got[1, :12].tolist()) and got[1].max() < 20
+    assert np.all(got[2] == -1)                                  # sequence 3 is not in the table
