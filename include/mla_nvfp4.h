@@ -248,6 +248,60 @@ int mla_nvfp4_gather_dequant_fp8(const uint8_t* cache, int64_t cache_rows,
                                  int32_t* staged_indices, void* stream);
 
 /*
+ * mla_indexer_topk -- the sparse indexer: for each query token, the list of
+ * cache positions its attention reads (Prime Inference write-up, "A native
+ * NVFP4 sparse-MLA decode kernel": the decode consumes the positions the
+ * sparse indexer selected; wireai.ir article, 4-bit-caches section, third
+ * decision: a fixed-width list of up to 2048 positions, unused slots padded).
+ *
+ * The pages give no scoring formula; this library takes the plainest one.
+ * Each cached position holds a 128-value E4M3 indexer key, each token a
+ * 128-value E4M3 indexer query, and the score of position p for token t is
+ * q_idx[t] . key(p), computed exactly (FP64 holds every partial sum of E4M3
+ * products exactly).  Token t's candidates are its positions 0 .. ctx[t]-1
+ * that name a key row.  Its list holds the min(topk, n) candidates with the
+ * largest scores (equal scores: the smaller position first), in ascending
+ * position order, padded with -1 to width topk.
+ *
+ *   q_idx             device, [T, 128] E4M3 bytes, row stride q_stride_t
+ *                     bytes (a multiple of 16, >= 128), 16-byte aligned.
+ *   keys              device, [key_rows, 128] E4M3 bytes, 16-byte aligned.
+ *   ctx_len           device, [T] int32: visible positions per token,
+ *                     clamped on the device to [0, max_ctx].
+ *   max_ctx           host bound on every ctx_len (sizes the workspace).
+ *   key_base          device, [T] int64, used without a block table: key p
+ *                     of token t is row key_base[t] + p and the list holds
+ *                     these rows (the physical indices mla_sparse_decode takes
+ *                     without a block table).
+ *   block_table ...   optional, as in mla_sparse_decode: key p of sequence
+ *                     token_seq[t] is row block_table[seq, p / block_size] *
+ *                     block_size + p % block_size, and the list holds logical
+ *                     positions p (the indices mla_sparse_decode translates
+ *                     through the same table).
+ *   A position whose row is negative, at or past key_rows, in a block past
+ *   bt_cols or unassigned, or of a sequence outside [0, bt_rows), is not a
+ *   candidate (its key is never read).
+ *   topk              1 .. 2048.  out: device, [T, topk] int32, row stride
+ *                     out_stride_t >= topk.
+ *   workspace         device, >= mla_indexer_workspace_size(T, max_ctx)
+ *                     bytes, 16-byte aligned, zero-filled before first use
+ *                     (every completed call leaves its histogram part zero).
+ * The result is deterministic.  Calls that overlap in time must not share a
+ * workspace.  Non-finite E4M3 codes (0x7F, 0xFF) are outside the contract.
+ */
+#define MLA_INDEXER_DIM 128
+size_t mla_indexer_workspace_size(int64_t num_tokens, int32_t max_ctx);
+int mla_indexer_topk(const uint8_t* q_idx, int64_t q_stride_t,
+                     const uint8_t* keys, int64_t key_rows,
+                     int64_t num_tokens, const int32_t* ctx_len, int32_t max_ctx,
+                     const int64_t* key_base,
+                     const int32_t* block_table, int32_t block_size,
+                     int64_t bt_stride, int32_t bt_rows, int32_t bt_cols,
+                     const int32_t* token_seq,
+                     int32_t topk, int32_t* out, int64_t out_stride_t,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Kernel timing for benchmarks (instrumentation, not part of the method).
  *
  * mla_kernel_timing(1) makes every later launching call of this library

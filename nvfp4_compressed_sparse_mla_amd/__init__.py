@@ -10,6 +10,7 @@ PyTorch only provides device memory and streams.
     sparse_decode(q, cache, indices, sm_scale, ...)    -> (out, lse)
     sparse_decode_noalloc(q, cache, indices, ...)      the same without a workspace
     gather_dequant_fp8(cache, indices, ...)            staged comparator step
+    indexer_topk(q_idx, keys, ctx_len, topk, ...)      the sparse indexer's lists
 """
 
 from __future__ import annotations
@@ -230,6 +231,55 @@ def gather_dequant_fp8(cache: torch.Tensor, indices: torch.Tensor, fp8_scale: fl
         rows.data_ptr(), staged_indices.data_ptr(), _stream(cache))
     check(st, "mla_nvfp4_gather_dequant_fp8")
     return rows, staged_indices
+
+
+INDEXER_DIM = 128
+
+
+def indexer_workspace(tokens: int, max_ctx: int, device) -> torch.Tensor:
+    """A zero-filled workspace for ``indexer_topk`` (reusable across calls)."""
+    n = int(load().mla_indexer_workspace_size(tokens, max_ctx))
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def indexer_topk(q_idx: torch.Tensor, keys: torch.Tensor, ctx_len: torch.Tensor, topk: int, max_ctx: int, *,
+                 key_base=None, block_table=None, token_seq=None, block_size: int = 64,
+                 out=None, workspace=None) -> torch.Tensor:
+    """The sparse indexer's lists: int32 [T, topk] of each token's best positions
+    (physical rows key_base[t] + p without a block table, logical positions with
+    one), ascending, padded with -1."""
+    lib = load()
+    dev = _device_of(keys, "keys")
+    if keys.dtype != torch.uint8 or keys.dim() != 2 or keys.shape[1] != INDEXER_DIM or not keys.is_contiguous():
+        raise ValueError("keys must be contiguous uint8 [rows, 128] (E4M3 bytes)")
+    if q_idx.dtype != torch.uint8 or q_idx.dim() != 2 or q_idx.shape[1] != INDEXER_DIM or q_idx.stride(1) != 1:
+        raise ValueError("q_idx must be uint8 [T, 128] (E4M3 bytes) with unit last stride")
+    T = q_idx.shape[0]
+    _same_device(dev, q_idx=q_idx, ctx_len=ctx_len, key_base=key_base, out=out, workspace=workspace)
+    if ctx_len.dtype != torch.int32 or tuple(ctx_len.shape) != (T,):
+        raise ValueError("ctx_len must be int32 [T]")
+    ctx_len = ctx_len.contiguous()
+    bt_ptr, ts_ptr, bt_stride, bt_rows, bt_cols, _keep = _block_table_args(block_table, token_seq, T, dev)
+    base_ptr = None
+    if block_table is None:
+        if key_base is None or key_base.dtype != torch.int64 or tuple(key_base.shape) != (T,):
+            raise ValueError("key_base must be int64 [T] without a block table")
+        key_base = key_base.contiguous()
+        base_ptr = key_base.data_ptr()
+    if out is None:
+        out = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    if out.dtype != torch.int32 or out.dim() != 2 or out.shape != (T, topk) or out.stride(1) != 1:
+        raise ValueError(f"out must be int32 [T, {topk}] with unit last stride")
+    if workspace is None:
+        workspace = indexer_workspace(T, max_ctx, dev)
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 vector (see indexer_workspace)")
+    st = lib.mla_indexer_topk(q_idx.data_ptr(), q_idx.stride(0), keys.data_ptr(), keys.shape[0], T,
+                              ctx_len.data_ptr(), int(max_ctx), base_ptr, bt_ptr, int(block_size), bt_stride,
+                              bt_rows, bt_cols, ts_ptr, int(topk), out.data_ptr(), out.stride(0),
+                              workspace.data_ptr(), workspace.numel(), _stream(keys))
+    check(st, "mla_indexer_topk")
+    return out
 
 
 def kernel_timing(enable: bool) -> None:

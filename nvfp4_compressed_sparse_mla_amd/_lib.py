@@ -32,6 +32,10 @@ SIGNATURES = {
     "mla_nvfp4_gather_dequant_fp8": (c_int, [c_vp, c_i64, c_vp, c_i64, c_i32, c_i64,
                                              c_vp, c_i32, c_i64, c_i32, c_i32, c_vp,
                                              c_f32, c_vp, c_vp, c_vp]),
+    "mla_indexer_workspace_size": (c_size, [c_i64, c_i32]),
+    "mla_indexer_topk": (c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_vp, c_i32, c_vp,
+                                 c_vp, c_i32, c_i64, c_i32, c_i32, c_vp,
+                                 c_i32, c_vp, c_i64, c_vp, c_size, c_vp]),
     "mla_kernel_timing": (c_int, [c_int]),
     "mla_last_kernel_ms": (c_int, [ctypes.POINTER(ctypes.c_float)]),
     "mla_status_string": (ctypes.c_char_p, [c_int]),

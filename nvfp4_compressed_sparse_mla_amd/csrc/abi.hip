@@ -297,6 +297,61 @@ int mla_sparse_decode_noalloc(const void* q, int q_dtype, int64_t num_tokens, in
                      kScratchBytes, num_splits, stream, true);
 }
 
+size_t mla_indexer_workspace_size(int64_t num_tokens, int32_t max_ctx) {
+  if (num_tokens < 0 || max_ctx < 0) return 0;
+  return mla::indexer_workspace_bytes(num_tokens, max_ctx);
+}
+
+int mla_indexer_topk(const uint8_t* q_idx, int64_t q_stride_t, const uint8_t* keys, int64_t key_rows,
+                     int64_t num_tokens, const int32_t* ctx_len, int32_t max_ctx,
+                     const int64_t* key_base, const int32_t* block_table, int32_t block_size,
+                     int64_t bt_stride, int32_t bt_rows, int32_t bt_cols, const int32_t* token_seq,
+                     int32_t topk, int32_t* out, int64_t out_stride_t, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (num_tokens < 0 || max_ctx < 0 || key_rows < 0 || topk < 1 || topk > MLA_MAX_TOPK)
+    return MLA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return MLA_OK;
+  if (!q_idx || !keys || !ctx_len || !out) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_idx) || !aligned16(keys)) return MLA_ERR_INVALID_ARG;
+  if (q_stride_t < MLA_INDEXER_DIM || (q_stride_t % 16) || out_stride_t < topk) return MLA_ERR_INVALID_ARG;
+  if (block_table) {
+    if (!token_seq || block_size < 1 || bt_rows < 1 || bt_cols < 1 || bt_stride < bt_cols)
+      return MLA_ERR_INVALID_ARG;
+  } else if (!key_base) {
+    return MLA_ERR_INVALID_ARG;
+  }
+  const int64_t nchunks = ((int64_t)max_ctx + 1023) / 1024;
+  if (num_tokens * nchunks >= ((int64_t)1 << 31) || num_tokens >= ((int64_t)1 << 31)) return MLA_ERR_INVALID_ARG;
+  const size_t need = mla::indexer_workspace_bytes(num_tokens, max_ctx);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
+  mla::IndexerParams p;
+  p.q = q_idx;
+  p.q_st = q_stride_t;
+  p.keys = keys;
+  p.key_rows = key_rows;
+  p.T = num_tokens;
+  p.ctx = ctx_len;
+  p.max_ctx = max_ctx;
+  p.key_stride = (max_ctx + 1) & ~1;
+  p.base = block_table ? nullptr : key_base;
+  p.bt = block_table;
+  p.bs = block_table ? block_size : 1;
+  p.bs_log2 = (p.bs & (p.bs - 1)) == 0 ? __builtin_ctz((unsigned)p.bs) : -1;
+  p.bt_rows = block_table ? bt_rows : 0;
+  p.bt_cols = block_table ? bt_cols : 0;
+  p.bt_st = block_table ? bt_stride : 0;
+  p.tok_seq = block_table ? token_seq : nullptr;
+  p.topk = topk;
+  p.out = out;
+  p.out_st = out_stride_t;
+  const size_t hist = ((size_t)num_tokens * 4096 * sizeof(uint32_t) + 255) & ~(size_t)255;
+  p.hist = reinterpret_cast<uint32_t*>(workspace);
+  p.keys_ws = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(workspace) + hist);
+  p.nchunks = 0;
+  const mla::KernelEvents ev = timing_events();
+  return launched(mla::launch_indexer(p, (hipStream_t)stream, ev), ev);
+}
+
 int mla_kernel_timing(int enable) {
   Timing& tm = timing();
   if (tm.enabled) {

@@ -1,0 +1,319 @@
+// Sparse indexer (gfx950): exact scores of every visible cached position and
+// the per-token top-k position list the decode consumes.
+//
+// What is computed (Prime Inference write-up, "A native NVFP4 sparse-MLA
+// decode kernel": the decode reads the positions a sparse indexer selected;
+// wireai.ir article, 4-bit-caches section, third decision: a fixed-width list
+// of up to 2048 positions with padded slots).  The pages give no scoring
+// formula; the library takes the plainest one: a 128-value E4M3 key per
+// cached position, a 128-value E4M3 query per token, score = their dot
+// product, computed exactly (every E4M3 product is a multiple of 2^-18 and
+// 128 of them sum to less than 2^25, so FP64 holds every partial sum exactly,
+// in any order).  A token's list holds the min(k, n) best of its n candidate
+// positions (0 .. ctx-1 that name a key row), equal scores to the smaller
+// position, in ascending position order, padded with -1.
+//
+//   score kernel   workgroup = (token, chunk of 1024 positions); 8 lanes per
+//                  position, each with 16 of the 128 dimensions (one 16-byte
+//                  load; a wave's load covers 8 consecutive rows), FP64
+//                  products and sums, a 3-step lane reduction.  The score
+//                  becomes a 64-bit key whose unsigned order is the score's
+//                  order (0 marks a position that is not a candidate); its
+//                  top 12 bits are counted in a per-token histogram.
+//   select kernel  one workgroup per token: radix select on the keys.  The
+//                  histogram names the 12-bit bucket that holds the k-th
+//                  best key; while that bucket holds more keys than are still
+//                  needed, one pass over the token's keys histograms the next
+//                  12 bits of the keys in it.  A last pass over the positions
+//                  in order writes every key above the bucket and the first
+//                  still-needed keys inside it (equal keys are equal scores,
+//                  so the smaller positions come first), then pads.
+#include "mla_device.h"
+#include "mla_launch.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kIdxDim = 128;
+constexpr int kChunk = 1024;              // positions per score workgroup
+constexpr int kBins = 1 << kIdxHistBits;  // 4096
+constexpr int kSelThreads = 1024;
+
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+
+// Order-preserving key of an exact score: larger score <=> larger key;
+// -0 and +0 give the same key; no finite score gives 0.
+__device__ __forceinline__ uint64_t score_key(double s) {
+  s += 0.0;                                     // -0 -> +0
+  const uint64_t b = (uint64_t)__double_as_longlong(s);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// Key row of position pos of token t, or -1 if it names none.
+__device__ __forceinline__ int64_t key_row(const IndexerParams& p, int64_t base, int64_t seq, int pos) {
+  if (!p.bt) {
+    const int64_t r = base + pos;
+    return (r >= 0 && r < p.key_rows) ? r : -1;
+  }
+  if (seq < 0 || seq >= p.bt_rows) return -1;
+  const int blk = p.bs_log2 >= 0 ? pos >> p.bs_log2 : pos / p.bs;
+  if (blk >= p.bt_cols) return -1;
+  const int e = p.bt[seq * p.bt_st + blk];
+  if (e < 0) return -1;
+  const int64_t r = (int64_t)e * p.bs + (pos - blk * p.bs);
+  return r < p.key_rows ? r : -1;
+}
+
+__device__ __forceinline__ int token_ctx(const IndexerParams& p, int64_t t) {
+  const int c = p.ctx[t];
+  return c < 0 ? 0 : (c > p.max_ctx ? p.max_ctx : c);
+}
+
+// 16 E4M3 bytes -> 16 doubles (exact: the conversions apply scale 1.0)
+__device__ __forceinline__ void e4m3x16_to_f64(const u32x4& w, double (&d)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[i], 1.0f, false);
+    const float2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[i], 1.0f, true);
+    d[4 * i] = (double)a.x;
+    d[4 * i + 1] = (double)a.y;
+    d[4 * i + 2] = (double)b.x;
+    d[4 * i + 3] = (double)b.y;
+  }
+}
+
+// Inclusive prefix sum over the 1024 threads of the select workgroup in
+// thread order.  `ws` holds 16 words of scratch; all threads must call.
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* ws) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t u = (uint32_t)__shfl_up((int)v, d, 64);
+    if (lane >= d) v += u;
+  }
+  if (lane == 63) ws[w] = v;
+  __syncthreads();
+  uint32_t add = 0;
+#pragma unroll
+  for (int i = 0; i < kSelThreads / 64; ++i)
+    if (i < w) add += ws[i];
+  __syncthreads();
+  return v + add;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void indexer_score_kernel(IndexerParams p) {
+  __shared__ uint32_t hist[kBins];
+  const uint32_t nch = (uint32_t)p.nchunks;
+  const uint32_t t32 = blockIdx.x / nch;
+  const int c = (int)(blockIdx.x - t32 * nch);
+  const int64_t t = t32;
+  const int ctx = token_ctx(p, t);
+  const int p0 = c * kChunk;
+  if (p0 >= ctx) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, sub = lane & 7;
+  for (int i = tid; i < kBins; i += 256) hist[i] = 0;
+
+  double q[16];
+  e4m3x16_to_f64(*reinterpret_cast<const u32x4*>(p.q + t * p.q_st + 16 * sub), q);
+  const int64_t base = p.bt ? 0 : p.base[t];
+  const int64_t seq = p.bt ? (int64_t)p.tok_seq[t] : 0;
+  uint64_t* const kout = p.keys_ws + t * p.key_stride;
+  __syncthreads();
+
+  // wave w takes positions p0 + 256 w + 8 i + (lane >> 3), i = 0 .. 31, four at a time
+  constexpr int kUnroll = 4;
+  for (int i0 = 0; i0 < 32; i0 += kUnroll) {
+    u32x4 raw[kUnroll];
+    bool ok[kUnroll];
+    int pos[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      pos[u] = p0 + 256 * wave + 8 * (i0 + u) + (lane >> 3);
+      const int64_t r = pos[u] < ctx ? key_row(p, base, seq, pos[u]) : -1;
+      ok[u] = r >= 0;
+      raw[u] = ok[u] ? *reinterpret_cast<const u32x4*>(p.keys + r * kIdxDim + 16 * sub) : (u32x4){0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      double k[16];
+      e4m3x16_to_f64(raw[u], k);
+      double s = 0.0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s = __builtin_fma(q[j], k[j], s);   // exact (see above)
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      s += __shfl_xor(s, 4, 64);
+      if (sub == 0 && pos[u] < ctx) {
+        const uint64_t key = ok[u] ? score_key(s) : 0ull;
+        kout[pos[u]] = key;
+        if (key) atomicAdd(&hist[key >> (64 - kIdxHistBits)], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t* const g = p.hist + t * kBins;
+  for (int i = tid; i < kBins; i += 256)
+    if (hist[i]) atomicAdd(&g[i], hist[i]);
+}
+
+__global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerParams p) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t ws[kSelThreads / 64];
+  __shared__ uint32_t sh_bin, sh_above, sh_cnt, sh_tot;
+  const int tid = threadIdx.x;
+  const int64_t t = blockIdx.x;
+  const int ctx = token_ctx(p, t);
+  const uint64_t* const keys = p.keys_ws + t * p.key_stride;
+  int32_t* const out = p.out + t * p.out_st;
+  const int64_t out_base = p.bt ? 0 : p.base[t];
+
+  // the score kernel's histogram of the top 12 bits; zero it for the next call
+  uint32_t* const g = p.hist + t * kBins;
+  uint32_t mine = 0;
+  for (int i = tid; i < kBins; i += kSelThreads) {
+    hist[i] = g[i];
+    mine += hist[i];
+    g[i] = 0u;
+  }
+  const uint32_t total = block_scan(mine, ws);
+  if (tid == kSelThreads - 1) sh_tot = total;
+  __syncthreads();
+  const uint32_t n_cand = sh_tot;
+  const uint32_t need = n_cand < (uint32_t)p.topk ? n_cand : (uint32_t)p.topk;
+  const bool all = need == n_cand;            // every candidate is selected
+
+  // Find the bucket b of the histogram (bins of `bits` bits) holding the
+  // need_in-th best key: thread i owns bins 4 (1023 - i) + 3 .. + 0, so the
+  // scan in thread order counts keys from the top.
+  auto find_bin = [&](uint32_t need_in, int nbins) {
+    const int hi = 4 * (kSelThreads - 1 - tid);
+    uint32_t v = 0;
+#pragma unroll
+    for (int j = 3; j >= 0; --j) v += (hi + j < nbins) ? hist[hi + j] : 0u;
+    const uint32_t incl = block_scan(v, ws);
+    uint32_t excl = incl - v;
+    if (excl < need_in && need_in <= incl) {
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        const uint32_t h = (hi + j < nbins) ? hist[hi + j] : 0u;
+        if (excl + h >= need_in) {
+          sh_bin = (uint32_t)(hi + j);
+          sh_above = excl;
+          sh_cnt = h;
+          break;
+        }
+        excl += h;
+      }
+    }
+    __syncthreads();
+  };
+
+  uint64_t prefix = 0;
+  int pbits = 0;
+  uint32_t need_in = need;
+  if (!all) {
+    find_bin(need_in, kBins);
+    prefix = sh_bin;
+    pbits = kIdxHistBits;
+    need_in -= sh_above;
+    uint32_t cnt = sh_cnt;
+    // refine while the bucket holds more keys than are still needed
+    while (cnt > need_in && pbits < 64) {
+      const int d = 64 - pbits < kIdxHistBits ? 64 - pbits : kIdxHistBits;
+      for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0u;
+      __syncthreads();
+      for (int i = 2 * tid; i < ctx; i += 2 * kSelThreads) {
+        u64x2 kk;
+        if (i + 1 < ctx) kk = *reinterpret_cast<const u64x2*>(keys + i);
+        else kk = (u64x2){keys[i], 0ull};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint64_t k = kk[j];
+          if (k && (k >> (64 - pbits)) == prefix)
+            atomicAdd(&hist[(uint32_t)(k >> (64 - pbits - d)) & ((1u << d) - 1u)], 1u);
+        }
+      }
+      __syncthreads();
+      find_bin(need_in, 1 << d);
+      prefix = (prefix << d) | sh_bin;
+      pbits += d;
+      need_in -= sh_above;
+      cnt = sh_cnt;
+    }
+  }
+
+  // Emit in position order: thread i takes positions 4 i .. 4 i + 3 of each
+  // block of 4096.  A key is selected if it is above the bucket, or inside
+  // it among the first need_in in position order.
+  uint32_t run_tie = 0, run_sel = 0;
+  for (int blk = 0; blk < ctx; blk += 4 * kSelThreads) {
+    const int p4 = blk + 4 * tid;
+    uint64_t k[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k[j] = p4 + j < ctx ? keys[p4 + j] : 0ull;
+    bool above[4], tie[4];
+    uint32_t ntie = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (all) {
+        above[j] = k[j] != 0ull;
+        tie[j] = false;
+      } else {
+        const uint64_t top = pbits == 64 ? k[j] : k[j] >> (64 - pbits);
+        above[j] = k[j] != 0ull && top > prefix;
+        tie[j] = k[j] != 0ull && top == prefix;
+      }
+      ntie += tie[j];
+    }
+    const uint32_t tie_incl = block_scan(ntie, ws);
+    uint32_t rank = run_tie + tie_incl - ntie;
+    bool sel[4];
+    uint32_t nsel = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sel[j] = above[j] || (tie[j] && rank < need_in);
+      rank += tie[j];
+      nsel += sel[j];
+    }
+    const uint32_t sel_incl = block_scan(nsel, ws);
+    uint32_t o = run_sel + sel_incl - nsel;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (sel[j]) out[o++] = (int32_t)(out_base + p4 + j);
+    if (tid == kSelThreads - 1) {
+      sh_tot = tie_incl;
+      sh_cnt = sel_incl;
+    }
+    __syncthreads();
+    run_tie += sh_tot;
+    run_sel += sh_cnt;
+    __syncthreads();
+  }
+  for (int i = (int)need + tid; i < p.topk; i += kSelThreads) out[i] = -1;
+}
+
+size_t indexer_workspace_bytes(int64_t T, int max_ctx) {
+  const size_t hist = ((size_t)T * kBins * sizeof(uint32_t) + 255) & ~(size_t)255;
+  return hist + (size_t)T * (size_t)((max_ctx + 1) & ~1) * sizeof(uint64_t);
+}
+
+hipError_t launch_indexer(const IndexerParams& p, hipStream_t stream, const KernelEvents& ev) {
+  IndexerParams a = p;
+  a.nchunks = (p.max_ctx + kChunk - 1) / kChunk;
+  void* args[] = {&a};
+  hipError_t e = hipSuccess;
+  // the benchmark events (if any) bracket both kernels: start at the first
+  // kernel's start, stop at the second's end
+  if (a.nchunks > 0) {
+    e = launch_kernel((const void*)indexer_score_kernel, dim3((unsigned)(p.T * a.nchunks)), dim3(256), args,
+                      stream, {ev.start, nullptr});
+    if (e != hipSuccess) return e;
+  }
+  return launch_kernel((const void*)indexer_select_kernel, dim3((unsigned)p.T), dim3(kSelThreads), args,
+                       stream, {a.nchunks > 0 ? nullptr : ev.start, ev.stop});
+}
+
+}  // namespace mla

@@ -16,7 +16,7 @@ struct KernelEvents {
 
 inline hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, hipStream_t stream,
                                 const KernelEvents& ev) {
-  if (ev.start) return hipExtLaunchKernel(fn, grid, block, args, 0, stream, ev.start, ev.stop, 0);
+  if (ev.start || ev.stop) return hipExtLaunchKernel(fn, grid, block, args, 0, stream, ev.start, ev.stop, 0);
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
@@ -80,5 +80,33 @@ struct StagedParams {
   int32_t* sidx;
 };
 hipError_t launch_gather_dequant_fp8(const StagedParams& p, hipStream_t stream, const KernelEvents& ev);
+
+// Sparse indexer (indexer.hip)
+constexpr int kIdxHistBits = 12;
+
+struct IndexerParams {
+  const uint8_t* q;         // [T, 128] E4M3 queries, row stride q_st bytes
+  int64_t q_st;
+  const uint8_t* keys;      // [key_rows, 128] E4M3 keys
+  int64_t key_rows;
+  int64_t T;
+  const int32_t* ctx;       // [T] visible positions
+  int max_ctx;              // bound on ctx (sizes the key workspace)
+  int64_t key_stride;       // workspace keys per token (max_ctx rounded up to even)
+  const int64_t* base;      // [T] first key row of each sequence (no block table)
+  const int32_t* bt;        // optional block table
+  int bs, bt_rows, bt_cols;
+  int bs_log2;
+  int64_t bt_st;
+  const int32_t* tok_seq;
+  int topk;
+  int32_t* out;             // [T, topk], row stride out_st
+  int64_t out_st;
+  uint64_t* keys_ws;        // [T][key_stride] order-preserving score keys
+  uint32_t* hist;           // [T][4096] histogram of the keys' top 12 bits (zero between calls)
+  int nchunks;              // set by launch_indexer
+};
+size_t indexer_workspace_bytes(int64_t T, int max_ctx);
+hipError_t launch_indexer(const IndexerParams& p, hipStream_t stream, const KernelEvents& ev);
 
 }  // namespace mla

@@ -231,6 +231,55 @@ def _prefill4k(device, q_dtype):
                     meta={"seed": seed, "cached": cached, "new": new, "window": window})
 
 
+@dataclass
+class IndexerInputs:
+    keys: torch.Tensor              # [R, 128] uint8 E4M3 bytes, one key per pool row
+    q: torch.Tensor                 # [T, 128] uint8 E4M3 bytes
+    ctx: torch.Tensor               # [T] int32 visible positions per token
+    base: Optional[torch.Tensor]    # [T] int64 first row of each token's sequence (no block table)
+    max_ctx: int
+
+
+def fp8_values(shape, seed: int, chunk: int, device) -> torch.Tensor:
+    """E4M3 bytes of N(0,1) draws (torch's cast to float8_e4m3fn)."""
+    g = _torch_gen(device, seed, chunk)
+    v = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return v.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def indexer_inputs(w: Workload) -> IndexerInputs:
+    """Indexer keys of every pool row and one indexer query per token, N(0,1)
+    values stored as E4M3, with each token's visible context: its whole
+    sequence for the decode workloads, the positions up to and including its
+    own for the prefill chunk."""
+    dev = w.q.device
+    seed = int(w.meta.get("seed", 0))
+    keys = torch.empty((w.pool_rows, 128), dtype=torch.uint8, device=dev)
+    for c, r0 in enumerate(range(0, w.pool_rows, CHUNK_ROWS)):
+        n = min(CHUNK_ROWS, w.pool_rows - r0)
+        keys[r0:r0 + n] = fp8_values((n, 128), seed, 3 * 10**6 + c, dev)
+    q = fp8_values((w.tokens, 128), seed, 4 * 10**6, dev)
+    T = w.tokens
+    if w.name == "decode15":
+        ctx = [w.meta["ctx"]] * T
+        base = [b * w.meta["ctx"] for b in range(T)]
+    elif w.name == "padded35":
+        ctx = list(w.meta["ctx"])
+        base = list(np.concatenate([[0], np.cumsum(ctx)[:-1]]))
+    elif w.name == "batch128":
+        ctx, base = list(w.meta["ctx"]), None
+    elif w.name == "prefill4k":
+        span = w.meta["cached"] + w.meta["new"]
+        ctx = [w.meta["cached"] + j + 1 for b in range(4) for j in range(w.meta["new"])]
+        base = [b * span for b in range(4) for j in range(w.meta["new"])]
+    else:                                              # one sequence over the whole pool
+        ctx, base = [w.pool_rows] * T, [0] * T
+    return IndexerInputs(keys=keys, q=q, ctx=torch.tensor(ctx, dtype=torch.int32, device=dev),
+                         base=None if base is None else torch.tensor([int(b) for b in base],
+                                                                     dtype=torch.int64, device=dev),
+                         max_ctx=int(max(ctx)) if ctx else 0)
+
+
 def make_workload(name: str, device, q_dtype=torch.float16, pad_random: bool = False) -> Workload:
     if name == "tiny":
         return _tiny(device, q_dtype)

@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -144,3 +144,23 @@ def test_noalloc_decode_rejects_bad_arguments_and_oversized_calls(lib):
     assert call(70000, 32, 2048, 1) == WORKSPACE        # more units than arrival counters
     assert call(1000, 32, 2048, 2) == WORKSPACE         # partials past the scratch array
     assert call(300, 32, 2048, 4) == WORKSPACE
+
+
+def test_indexer_rejects_bad_arguments(lib):
+    """Host-side checks of mla_indexer_topk, before any HIP call."""
+    fake = ctypes.c_void_p(1 << 20)
+
+    def call(T=2, q_st=128, topk=16, out_st=16, max_ctx=100, base=fake, bt=None, seq=None, ws_bytes=1 << 30):
+        return lib.mla_indexer_topk(fake, q_st, fake, 1000, T, fake, max_ctx, base, bt, 64, 4, 2, 4, seq,
+                                    topk, fake, out_st, fake, ws_bytes, None)
+    assert call(T=0) == OK
+    assert call(topk=0) == INVALID and call(topk=2049) == INVALID
+    assert call(q_st=120) == INVALID and call(q_st=136) == INVALID      # stride: >= 128, multiple of 16
+    assert call(out_st=8) == INVALID
+    assert call(base=None) == INVALID                                   # rows need a base or a table
+    assert call(base=None, bt=fake) == INVALID                          # a table needs token_seq
+    assert call(max_ctx=-1) == INVALID
+    assert call(ws_bytes=16) == WORKSPACE
+    need = lib.mla_indexer_workspace_size(2, 100)
+    assert need == 2 * 4096 * 4 + 2 * 100 * 8
+    assert lib.mla_indexer_workspace_size(3, 101) == ((3 * 4096 * 4 + 255) // 256) * 256 + 3 * 102 * 8
