@@ -53,6 +53,10 @@ FP8_ROW_BYTES = 576
 ALL_CONFIGS = ("tiny", "decode15", "padded35", "batch128", "prefill4k")
 # the pages' comparison trio (native / FP8-576 / staged) is reported at these
 TRIO_CONFIGS = ("decode15", "padded35", "batch128")
+# the sparse indexer (the step before the decode) is timed at the decode batches;
+# at the prefill chunk every token would rescan its whole sequence
+INDEXER_CONFIGS = ("tiny", "decode15", "padded35", "batch128")
+INDEXER_KEY_BYTES = 128
 
 DESCRIPTIONS = {
     "tiny": "1 token x 16 heads, 256 picks of a 4,096-row NVFP4 pool",
@@ -263,7 +267,40 @@ def _measure(torch, mla, c: Case, steps: int, warmup: int, comparators: bool):
     }
     if comparators and c.name in TRIO_CONFIGS:
         r["trio"] = _comparators(torch, mla, c, n)
+    if c.name in INDEXER_CONFIGS:
+        r["indexer"] = _indexer(torch, mla, c, n)
     return r, kern
+
+
+def _indexer(torch, mla, c: Case, n: int):
+    """The sparse indexer over every token's visible positions (kernel time of
+    its two kernels, from the first one's start to the second one's end)."""
+    from synth import indexer_inputs
+
+    w = c.w
+    ix = indexer_inputs(w)
+    out = torch.empty((w.tokens, w.topk), dtype=torch.int32, device=ix.keys.device)
+    ws = mla.indexer_workspace(w.tokens, ix.max_ctx, ix.keys.device)
+    kw = dict(key_base=ix.base, out=out, workspace=ws)
+    if w.block_table is not None:
+        kw = dict(block_table=w.block_table, token_seq=w.token_seq, block_size=w.block_size, out=out,
+                  workspace=ws)
+
+    def run():
+        mla.indexer_topk(ix.q, ix.keys, ix.ctx, w.topk, ix.max_ctx, **kw)
+
+    for _ in range(3):
+        c.flush()
+        run()
+    torch.cuda.synchronize()
+    ms = _kernel_ms(mla, run, n, c.flush)
+    positions = int(ix.ctx.sum().item())
+    key_bytes = positions * INDEXER_KEY_BYTES
+    m = statistics.mean(ms)
+    del ix, out, ws
+    return {"kernel_us": _stats_us(ms), "positions_scored": positions, "key_bytes": key_bytes,
+            "key_gbs": round(key_bytes / (m * 1e-3) / 1e9, 1),
+            "frac_of_8tbs": round(key_bytes / (m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def _comparators(torch, mla, c: Case, n: int):

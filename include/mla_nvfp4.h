@@ -49,7 +49,8 @@ enum mla_status {
     MLA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, stride or alignment */
     MLA_ERR_UNSUPPORTED = 2,  /* enum value or head count not supported       */
     MLA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required   */
-    MLA_ERR_HIP = 4           /* the HIP runtime reported an error            */
+    MLA_ERR_HIP = 4,          /* the HIP runtime reported an error            */
+    MLA_ERR_CAPACITY = 5      /* the pool has too few free blocks             */
 };
 
 enum mla_dtype { MLA_F16 = 0, MLA_BF16 = 1 };
@@ -300,6 +301,81 @@ int mla_indexer_topk(const uint8_t* q_idx, int64_t q_stride_t,
                      const int32_t* token_seq,
                      int32_t topk, int32_t* out, int64_t out_stride_t,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Paged cache pool (host side, no GPU calls) -- capacity accounting and a
+ * block allocator for the cache rows and the indexer and other per-token
+ * state of every layer (Prime Inference write-up, "Making room for
+ * low-latency decode": 576 -> 352-byte rows with the other state unchanged
+ * took one decoder's cache from about 1.09 M to 1.63 M tokens at the same
+ * memory budget; 64-row blocks as in "Changing the layout to reduce
+ * fragmentation").
+ *
+ * Capacity, in whole blocks of block_rows tokens:
+ *   budget_bytes / (layers * block_rows * (row_bytes + other_bytes)).
+ * A sequence grows by whole blocks, each the lowest-numbered free block
+ * (consecutive blocks on an unfragmented pool), all or nothing; releasing it
+ * frees them all.  Physical row of position p: table[p / block_rows] *
+ * block_rows + p % block_rows, in every layer's cache.
+ *
+ * mla_pool_create         max_seqs sequences of at most max_blocks_per_seq
+ *                         blocks; *out receives the pool (MLA_ERR_INVALID_ARG
+ *                         on bad sizes, or more than 2^31 physical rows).
+ * mla_pool_reserve        grow `seq` to hold `tokens` positions;
+ *                         MLA_ERR_CAPACITY (nothing taken) if the free blocks
+ *                         or the table width do not suffice.
+ * mla_pool_block_table    host [max_seqs, max_blocks_per_seq] int32 copy of
+ *                         every table, row stride `stride`, -1 = no block.
+ * mla_pool_slots          host int64 physical rows of positions first_pos ..
+ *                         first_pos + n - 1 of `seq` (the slot mapping
+ *                         mla_nvfp4_quantize_append takes); the positions must
+ *                         be reserved.
+ * mla_pool_descriptors    copy descriptors (maximal contiguous byte runs) and
+ *                         bytes of `seq`'s (layer, block) regions of
+ *                         block_rows * row_bytes bytes, visited in table order,
+ *                         under a layer-major pool (region (l, b) at
+ *                         (l * n_blocks + b) * R) or a block-major pool (at
+ *                         (b * layers + l) * R).
+ * Calls on one pool are serialised by the pool's own lock.
+ */
+typedef struct mla_pool mla_pool;
+enum mla_layout { MLA_LAYOUT_LAYER_MAJOR = 0, MLA_LAYOUT_BLOCK_MAJOR = 1 };
+int64_t mla_pool_capacity_blocks(int64_t budget_bytes, int32_t layers, int32_t row_bytes,
+                                 int32_t other_bytes, int32_t block_rows);
+int mla_pool_create(int64_t budget_bytes, int32_t layers, int32_t row_bytes, int32_t other_bytes,
+                    int32_t block_rows, int32_t max_seqs, int32_t max_blocks_per_seq, mla_pool** out);
+void mla_pool_destroy(mla_pool* pool);
+int64_t mla_pool_num_blocks(mla_pool* pool);
+int64_t mla_pool_free_blocks(mla_pool* pool);
+int mla_pool_reserve(mla_pool* pool, int32_t seq, int64_t tokens);
+int mla_pool_release(mla_pool* pool, int32_t seq);
+int mla_pool_block_table(mla_pool* pool, int32_t* table, int64_t stride);
+int mla_pool_slots(mla_pool* pool, int32_t seq, int64_t first_pos, int64_t n, int64_t* slots);
+int mla_pool_descriptors(mla_pool* pool, int32_t seq, int32_t layout, int64_t* descriptors,
+                         int64_t* bytes);
+
+/*
+ * mla_kv_pack_blocks / mla_kv_unpack_blocks -- move a request's cache blocks
+ * between a pool and one contiguous staging buffer, the form that needs a
+ * single copy descriptor to transfer (Prime Inference write-up, "Changing
+ * the layout to reduce fragmentation"; mo.ai.kr article, KV-transfer
+ * section: a block-major layout groups one block's data from all layers).
+ *
+ * A region is one (layer, block): block_rows * row_bytes bytes (a multiple
+ * of 16).  The pool holds pool_blocks blocks of `layers` layers, layer-major
+ * (region (l, b) at (l * pool_blocks + b) * R) or block-major (at
+ * (b * layers + l) * R).  staging is [n][layers][R], block-major over the
+ * request's n blocks.  pack copies pool region (l, block_ids[i]) to staging
+ * (i, l); unpack copies staging (i, l) to pool region (l, block_ids[i]).
+ * block_ids (device, int32 [n]) outside [0, pool_blocks) are skipped on the
+ * device.  pool and staging are device memory, 16-byte aligned.
+ */
+int mla_kv_pack_blocks(const uint8_t* pool, int32_t layout, int64_t pool_blocks, int32_t layers,
+                       int32_t block_rows, int32_t row_bytes, const int32_t* block_ids, int64_t n,
+                       uint8_t* staging, void* stream);
+int mla_kv_unpack_blocks(const uint8_t* staging, int64_t n, const int32_t* block_ids, uint8_t* pool,
+                         int32_t layout, int64_t pool_blocks, int32_t layers, int32_t block_rows,
+                         int32_t row_bytes, void* stream);
 
 /*
  * Kernel timing for benchmarks (instrumentation, not part of the method).

@@ -11,6 +11,8 @@ PyTorch only provides device memory and streams.
     sparse_decode_noalloc(q, cache, indices, ...)      the same without a workspace
     gather_dequant_fp8(cache, indices, ...)            staged comparator step
     indexer_topk(q_idx, keys, ctx_len, topk, ...)      the sparse indexer's lists
+    Pool(budget, layers, ...)                          paged pool: capacity, blocks, tables
+    kv_pack_blocks / kv_unpack_blocks                  a request's blocks <-> staging buffer
 """
 
 from __future__ import annotations
@@ -280,6 +282,122 @@ def indexer_topk(q_idx: torch.Tensor, keys: torch.Tensor, ctx_len: torch.Tensor,
                               workspace.data_ptr(), workspace.numel(), _stream(keys))
     check(st, "mla_indexer_topk")
     return out
+
+
+LAYOUTS = {"layer": 0, "block": 1}
+
+
+class Pool:
+    """The library's paged cache pool (host side): capacity in 64-row (or
+    block_rows) blocks for `layers` layers of rows plus other per-token state,
+    a lowest-free-first block allocator and per-sequence block tables."""
+
+    def __init__(self, budget_bytes: int, layers: int, row_bytes: int = NVFP4_ROW_BYTES,
+                 other_bytes: int = 0, block_rows: int = 64, max_seqs: int = 1,
+                 max_blocks_per_seq: int = 1):
+        import ctypes
+
+        self._lib = load()
+        h = ctypes.c_void_p()
+        check(self._lib.mla_pool_create(budget_bytes, layers, row_bytes, other_bytes, block_rows, max_seqs,
+                                        max_blocks_per_seq, ctypes.byref(h)), "mla_pool_create")
+        self._h = h
+        self.layers, self.row_bytes, self.block_rows = layers, row_bytes, block_rows
+        self.max_seqs, self.max_blocks = max_seqs, max_blocks_per_seq
+
+    def close(self):
+        if self._h:
+            self._lib.mla_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self._lib.mla_pool_num_blocks(self._h))
+
+    @property
+    def free_blocks(self) -> int:
+        return int(self._lib.mla_pool_free_blocks(self._h))
+
+    def reserve(self, seq: int, tokens: int) -> bool:
+        """Grow `seq` to hold `tokens` positions; False (nothing taken) if it cannot."""
+        st = self._lib.mla_pool_reserve(self._h, seq, tokens)
+        if st == 5:
+            return False
+        check(st, "mla_pool_reserve")
+        return True
+
+    def release(self, seq: int) -> None:
+        check(self._lib.mla_pool_release(self._h, seq), "mla_pool_release")
+
+    def block_table(self) -> torch.Tensor:
+        """Host int32 [max_seqs, max_blocks_per_seq], -1 = no block."""
+        t = torch.empty((self.max_seqs, self.max_blocks), dtype=torch.int32)
+        check(self._lib.mla_pool_block_table(self._h, t.data_ptr(), self.max_blocks), "mla_pool_block_table")
+        return t
+
+    def slots(self, seq: int, first_pos: int, n: int) -> torch.Tensor:
+        """Host int64 physical rows of positions first_pos .. first_pos + n - 1."""
+        t = torch.empty(n, dtype=torch.int64)
+        check(self._lib.mla_pool_slots(self._h, seq, first_pos, n, t.data_ptr() if n else None), "mla_pool_slots")
+        return t
+
+    def descriptors(self, seq: int, layout: str):
+        """(copy descriptors, bytes) of `seq`'s regions under a layer- or block-major pool."""
+        import ctypes
+
+        d, b = ctypes.c_int64(), ctypes.c_int64()
+        check(self._lib.mla_pool_descriptors(self._h, seq, LAYOUTS[layout], ctypes.byref(d), ctypes.byref(b)),
+              "mla_pool_descriptors")
+        return int(d.value), int(b.value)
+
+
+def pool_capacity_blocks(budget_bytes: int, layers: int, row_bytes: int, other_bytes: int,
+                         block_rows: int = 64) -> int:
+    return int(load().mla_pool_capacity_blocks(budget_bytes, layers, row_bytes, other_bytes, block_rows))
+
+
+def _region_args(pool_t, layout, pool_blocks, layers, block_rows, row_bytes, block_ids, staging):
+    dev = _device_of(pool_t, "pool")
+    _same_device(dev, block_ids=block_ids, staging=staging)
+    if pool_t.dtype != torch.uint8 or not pool_t.is_contiguous():
+        raise ValueError("pool must be a contiguous uint8 tensor")
+    region = block_rows * row_bytes
+    if pool_t.numel() < pool_blocks * layers * region:
+        raise ValueError("pool is smaller than pool_blocks * layers * block_rows * row_bytes bytes")
+    if block_ids.dtype != torch.int32 or block_ids.dim() != 1 or not block_ids.is_contiguous():
+        raise ValueError("block_ids must be a contiguous int32 vector")
+    n = block_ids.shape[0]
+    if staging.dtype != torch.uint8 or not staging.is_contiguous() or staging.numel() < n * layers * region:
+        raise ValueError("staging must be a contiguous uint8 tensor of n * layers * block_rows * row_bytes bytes")
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    return n
+
+
+def kv_pack_blocks(pool_t, layout: str, pool_blocks: int, layers: int, block_ids, staging,
+                   block_rows: int = 64, row_bytes: int = NVFP4_ROW_BYTES) -> None:
+    """Gather a request's blocks (all layers) from a pool into a contiguous
+    block-major staging buffer [n][layers][block_rows * row_bytes]."""
+    n = _region_args(pool_t, layout, pool_blocks, layers, block_rows, row_bytes, block_ids, staging)
+    check(load().mla_kv_pack_blocks(pool_t.data_ptr(), LAYOUTS[layout], pool_blocks, layers, block_rows,
+                                    row_bytes, block_ids.data_ptr(), n, staging.data_ptr(), _stream(pool_t)),
+          "mla_kv_pack_blocks")
+
+
+def kv_unpack_blocks(staging, block_ids, pool_t, layout: str, pool_blocks: int, layers: int,
+                     block_rows: int = 64, row_bytes: int = NVFP4_ROW_BYTES) -> None:
+    """Scatter a block-major staging buffer into a pool at block_ids."""
+    n = _region_args(pool_t, layout, pool_blocks, layers, block_rows, row_bytes, block_ids, staging)
+    check(load().mla_kv_unpack_blocks(staging.data_ptr(), n, block_ids.data_ptr(), pool_t.data_ptr(),
+                                      LAYOUTS[layout], pool_blocks, layers, block_rows, row_bytes,
+                                      _stream(pool_t)),
+          "mla_kv_unpack_blocks")
 
 
 def kernel_timing(enable: bool) -> None:

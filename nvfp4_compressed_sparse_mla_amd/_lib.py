@@ -36,6 +36,18 @@ SIGNATURES = {
     "mla_indexer_topk": (c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_vp, c_i32, c_vp,
                                  c_vp, c_i32, c_i64, c_i32, c_i32, c_vp,
                                  c_i32, c_vp, c_i64, c_vp, c_size, c_vp]),
+    "mla_pool_capacity_blocks": (c_i64, [c_i64, c_i32, c_i32, c_i32, c_i32]),
+    "mla_pool_create": (c_int, [c_i64, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_vp)]),
+    "mla_pool_destroy": (None, [c_vp]),
+    "mla_pool_num_blocks": (c_i64, [c_vp]),
+    "mla_pool_free_blocks": (c_i64, [c_vp]),
+    "mla_pool_reserve": (c_int, [c_vp, c_i32, c_i64]),
+    "mla_pool_release": (c_int, [c_vp, c_i32]),
+    "mla_pool_block_table": (c_int, [c_vp, c_vp, c_i64]),
+    "mla_pool_slots": (c_int, [c_vp, c_i32, c_i64, c_i64, c_vp]),
+    "mla_pool_descriptors": (c_int, [c_vp, c_i32, c_i32, ctypes.POINTER(c_i64), ctypes.POINTER(c_i64)]),
+    "mla_kv_pack_blocks": (c_int, [c_vp, c_i32, c_i64, c_i32, c_i32, c_i32, c_vp, c_i64, c_vp, c_vp]),
+    "mla_kv_unpack_blocks": (c_int, [c_vp, c_i64, c_vp, c_vp, c_i32, c_i64, c_i32, c_i32, c_i32, c_vp]),
     "mla_kernel_timing": (c_int, [c_int]),
     "mla_last_kernel_ms": (c_int, [ctypes.POINTER(ctypes.c_float)]),
     "mla_status_string": (ctypes.c_char_p, [c_int]),

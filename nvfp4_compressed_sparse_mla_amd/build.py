@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla_nvfp4.so")
-SOURCES = ["abi.hip", "quantize.hip", "decode.hip", "staged.hip", "indexer.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "decode.hip", "staged.hip", "indexer.hip", "layout.hip"]
+HOST_SOURCES = ["pool.cpp"]     # host-only C++ (no device code)
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -54,11 +55,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def _compile_host(src: str, verbose: bool) -> str:
+    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+    cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"g++ failed on {src}:\n{res.stderr}")
+    return obj
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link the shared library. Returns its path."""
+    """Compile every HIP source for gfx950 (and the host C++ sources) and link
+    the shared library. Returns its path."""
     os.makedirs(OBJDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(HOST_SOURCES)) as ex:
+        jobs = [ex.submit(_compile, s, verbose) for s in SOURCES]
+        jobs += [ex.submit(_compile_host, s, verbose) for s in HOST_SOURCES]
+        objs = [j.result() for j in jobs]
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

@@ -213,6 +213,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_UNSUPPORTED: return "unsupported value";
     case MLA_ERR_WORKSPACE: return "workspace missing or too small";
     case MLA_ERR_HIP: return "HIP runtime error";
+    case MLA_ERR_CAPACITY: return "not enough free blocks in the pool";
     default: return "unknown status";
   }
 }
@@ -350,6 +351,75 @@ int mla_indexer_topk(const uint8_t* q_idx, int64_t q_stride_t, const uint8_t* ke
   p.nchunks = 0;
   const mla::KernelEvents ev = timing_events();
   return launched(mla::launch_indexer(p, (hipStream_t)stream, ev), ev);
+}
+
+namespace {
+// Region geometry of mla_kv_pack_blocks / mla_kv_unpack_blocks; false on bad sizes.
+bool region_geometry(int32_t layout, int64_t pool_blocks, int32_t layers, int32_t block_rows,
+                     int32_t row_bytes, int64_t n, int64_t* region, int64_t* bstride, int64_t* lstride) {
+  if (layout != MLA_LAYOUT_LAYER_MAJOR && layout != MLA_LAYOUT_BLOCK_MAJOR) return false;
+  if (pool_blocks < 0 || layers < 1 || block_rows < 1 || row_bytes < 1 || n < 0) return false;
+  *region = (int64_t)block_rows * row_bytes;
+  if (*region % 16) return false;
+  if (n * layers >= ((int64_t)1 << 31)) return false;
+  *bstride = layout == MLA_LAYOUT_LAYER_MAJOR ? *region : *region * layers;
+  *lstride = layout == MLA_LAYOUT_LAYER_MAJOR ? *region * pool_blocks : *region;
+  return true;
+}
+}  // namespace
+
+int mla_kv_pack_blocks(const uint8_t* pool, int32_t layout, int64_t pool_blocks, int32_t layers,
+                       int32_t block_rows, int32_t row_bytes, const int32_t* block_ids, int64_t n,
+                       uint8_t* staging, void* stream) {
+  int64_t region, bs, ls;
+  if (!region_geometry(layout, pool_blocks, layers, block_rows, row_bytes, n, &region, &bs, &ls))
+    return (layout != MLA_LAYOUT_LAYER_MAJOR && layout != MLA_LAYOUT_BLOCK_MAJOR) ? MLA_ERR_UNSUPPORTED
+                                                                                  : MLA_ERR_INVALID_ARG;
+  if (n == 0) return MLA_OK;
+  if (!pool || !block_ids || !staging || !aligned16(pool) || !aligned16(staging)) return MLA_ERR_INVALID_ARG;
+  mla::RegionCopy c;
+  c.src = pool;
+  c.src_block_stride = bs;
+  c.src_layer_stride = ls;
+  c.src_blocks = pool_blocks;
+  c.src_ids = block_ids;
+  c.dst = staging;
+  c.dst_block_stride = region * layers;
+  c.dst_layer_stride = region;
+  c.dst_blocks = n;
+  c.dst_ids = nullptr;
+  c.n = n;
+  c.layers = layers;
+  c.region_bytes = region;
+  const mla::KernelEvents ev = timing_events();
+  return launched(mla::launch_region_copy(c, (hipStream_t)stream, ev), ev);
+}
+
+int mla_kv_unpack_blocks(const uint8_t* staging, int64_t n, const int32_t* block_ids, uint8_t* pool,
+                         int32_t layout, int64_t pool_blocks, int32_t layers, int32_t block_rows,
+                         int32_t row_bytes, void* stream) {
+  int64_t region, bs, ls;
+  if (!region_geometry(layout, pool_blocks, layers, block_rows, row_bytes, n, &region, &bs, &ls))
+    return (layout != MLA_LAYOUT_LAYER_MAJOR && layout != MLA_LAYOUT_BLOCK_MAJOR) ? MLA_ERR_UNSUPPORTED
+                                                                                  : MLA_ERR_INVALID_ARG;
+  if (n == 0) return MLA_OK;
+  if (!pool || !block_ids || !staging || !aligned16(pool) || !aligned16(staging)) return MLA_ERR_INVALID_ARG;
+  mla::RegionCopy c;
+  c.src = staging;
+  c.src_block_stride = region * layers;
+  c.src_layer_stride = region;
+  c.src_blocks = n;
+  c.src_ids = nullptr;
+  c.dst = pool;
+  c.dst_block_stride = bs;
+  c.dst_layer_stride = ls;
+  c.dst_blocks = pool_blocks;
+  c.dst_ids = block_ids;
+  c.n = n;
+  c.layers = layers;
+  c.region_bytes = region;
+  const mla::KernelEvents ev = timing_events();
+  return launched(mla::launch_region_copy(c, (hipStream_t)stream, ev), ev);
 }
 
 int mla_kernel_timing(int enable) {

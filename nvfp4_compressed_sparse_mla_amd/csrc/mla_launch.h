@@ -107,6 +107,22 @@ struct IndexerParams {
   int nchunks;              // set by launch_indexer
 };
 size_t indexer_workspace_bytes(int64_t T, int max_ctx);
+
+// Copies of (layer, block) regions (layout.hip): region l of entry i moves
+// from src + sid * src_block_stride + l * src_layer_stride to the same form
+// at dst, sid = src_ids[i] (or i if null), likewise for dst.
+struct RegionCopy {
+  const uint8_t* src;
+  int64_t src_block_stride, src_layer_stride, src_blocks;
+  const int32_t* src_ids;
+  uint8_t* dst;
+  int64_t dst_block_stride, dst_layer_stride, dst_blocks;
+  const int32_t* dst_ids;
+  int64_t n;                // entries
+  int layers;
+  int64_t region_bytes;     // a multiple of 16
+};
+hipError_t launch_region_copy(const RegionCopy& c, hipStream_t stream, const KernelEvents& ev);
 hipError_t launch_indexer(const IndexerParams& p, hipStream_t stream, const KernelEvents& ev);
 
 }  // namespace mla

@@ -34,6 +34,8 @@ Readings taken where the pages are silent:
 
 from __future__ import annotations
 
+import numpy as np
+
 
 def capacity_blocks(budget_bytes, layers, row_bytes, other_bytes, block_rows):
     """Whole blocks a budget holds (P1)."""
@@ -100,3 +102,34 @@ def descriptors(blocks, layers, n_blocks, region_bytes, layout):
             runs += 1
         end = s + region_bytes
     return runs, len(starts) * region_bytes
+
+
+def _regions(pool_bytes, layout, n_blocks, layers, region):
+    """View of a pool's bytes as [layer, block, region] (P3)."""
+    a = np.asarray(pool_bytes, dtype=np.uint8)[:n_blocks * layers * region]
+    if layout == "layer":
+        return a.reshape(layers, n_blocks, region)
+    return a.reshape(n_blocks, layers, region).transpose(1, 0, 2)
+
+
+def pack(pool_bytes, layout, n_blocks, layers, region, block_ids):
+    """Staging bytes [n][layers][region] of the request's blocks, in order."""
+    v = _regions(pool_bytes, layout, n_blocks, layers, region)
+    ids = np.asarray(block_ids, dtype=np.int64)
+    out = np.zeros((ids.shape[0], layers, region), dtype=np.uint8)
+    for i, b in enumerate(ids):
+        if 0 <= b < n_blocks:
+            out[i] = v[:, b, :]
+    return out.reshape(-1)
+
+
+def unpack(staging, block_ids, pool_bytes, layout, n_blocks, layers, region):
+    """The pool after writing staging entry i to block block_ids[i] (in
+    order: a later entry naming the same block wins)."""
+    pool = np.array(pool_bytes, dtype=np.uint8, copy=True)
+    v = _regions(pool, layout, n_blocks, layers, region)
+    st = np.asarray(staging, dtype=np.uint8).reshape(-1, layers, region)
+    for i, b in enumerate(np.asarray(block_ids, dtype=np.int64)):
+        if 0 <= b < n_blocks:
+            v[:, b, :] = st[i]
+    return pool

@@ -17,7 +17,7 @@ OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
 
 def _declared():
     text = open(HEADER).read()
-    return re.findall(r"^\s*(?:int|int32_t|size_t|const char\*)\s+(mla_\w+)\s*\(", text, re.M)
+    return re.findall(r"^\s*(?:int|int32_t|int64_t|size_t|void|const char\*)\s+(mla_\w+)\s*\(", text, re.M)
 
 
 @pytest.fixture(scope="module")
@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n

@@ -20,8 +20,8 @@ def test_capacity_reproduces_the_pages_figures():
     nv = pool.capacity_blocks(budget, layers, 352, other, bs) * bs
     assert abs(fp8 - 1_090_000) < bs
     assert round(nv / 1e6, 2) == 1.63
-    # the band of other-state sizes the rounded figures allow (App. B of the
-    # survey derives about 90..111 B; exactly 90..110): the ratio stays within 1.625/1.095 .. 1.635/1.085
+    # the band of other-state sizes the rounded figures allow, 90..110 B: the
+    # ratio stays within 1.625/1.095 .. 1.635/1.085
     for x in (90, 100, 110):
         r = (576 + x) / (352 + x)
         assert 1.625 / 1.095 <= r <= 1.635 / 1.085
@@ -105,3 +105,25 @@ def test_descriptor_closed_forms():
     spread = list(range(0, 6250, 2))                              # every other block
     assert pool.descriptors(spread, L, 7000, R, "layer")[0] == L * len(spread)
     assert pool.descriptors(spread, L, 7000, R, "block")[0] == len(spread)
+
+
+@pytest.mark.parametrize("layout", ["layer", "block"])
+def test_pack_reads_the_regions_the_layout_places(layout):
+    """Byte values that spell out (layer, block, offset) come back from pack
+    in staging order [i][layer][offset]; unpack of a pack into other blocks
+    moves exactly those regions."""
+    n_blocks, layers, region = 7, 3, 8
+    pool_b = np.zeros(n_blocks * layers * region, np.uint8)
+    for l in range(layers):
+        for b in range(n_blocks):
+            start = (l * n_blocks + b) * region if layout == "layer" else (b * layers + l) * region
+            pool_b[start:start + region] = 16 * l + b
+    ids = [5, 0, 3]
+    st = pool.pack(pool_b, layout, n_blocks, layers, region, ids).reshape(3, layers, region)
+    for i, b in enumerate(ids):
+        for l in range(layers):
+            assert np.all(st[i, l] == 16 * l + b)
+    moved = pool.unpack(st.reshape(-1), [1, 2, 6], np.zeros_like(pool_b), layout, n_blocks, layers, region)
+    back = pool.pack(moved, layout, n_blocks, layers, region, [1, 2, 6])
+    assert np.array_equal(back, st.reshape(-1))
+    assert not pool.pack(moved, layout, n_blocks, layers, region, [0, 3, 4, 5]).any()
