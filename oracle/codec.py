@@ -33,6 +33,20 @@ Readings taken where the pages are silent:
 * R7  The rope part is cast to E4M3 directly, with no scale.
 * R8  The FP8 comparison row stores E4M3(v / kv_scale) for all 512 + 64
       values (latent first), decoded as code * kv_scale.
+* R10 Two-level variant (the NVFP4 format's second, per-tensor scale; the
+      pages name only the per-16 FP8 scale): a positive FP32 global scale g
+      multiplies every decoded latent value, code * s * g; the rope is not
+      scaled.  With g arbitrary the exact quotient amax / (6 g) and the
+      code thresholds t * s * g are no longer all FP32 values, so the
+      encoding is defined by the FP32 steps that make its decisions:
+        d   = fl32(6 * g)
+        s   = E4M3 of fl32(amax / d), round to nearest even, saturating
+        thr = fl32(t * s * g) for t in .25, .75, 1.25, 1.75, 2.5, 3.5, 5
+              (t * s is exact; one rounding)
+        magnitude = number of thresholds passed, |x| > thr for t in
+              .25, 1.25, 2.5, 5 and |x| >= thr for t in .75, 1.75, 3.5
+              (ties to the even code, as in R5), 0 when s = 0.
+      With g = 1 every step is exact and this is R4 and R5 exactly.
 
 All arithmetic is FP64 on values that FP64 holds exactly: every fp16 /
 bf16 input, every grid point g * s (at most 7 significant bits) and every
@@ -216,6 +230,49 @@ def nvfp4_encode_rows(latent, rope) -> np.ndarray:
     out[:, SCALE_OFF:ROPE_OFF] = scale_codes
     out[:, ROPE_OFF:] = e4m3_encode(rp)
     return out
+
+
+# E2M1 thresholds between magnitude codes k and k+1, and whether reaching
+# the threshold itself moves up (ties go to the even code k+1)
+E2M1_THRESHOLDS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+E2M1_TIE_UP = (False, True, False, True, False, True, False)
+
+
+def nvfp4_encode_rows_2level(latent, rope, global_scale: float) -> np.ndarray:
+    """352-byte rows of the two-level variant (R10): the group scales and codes
+    of latent / g, decided by the FP32 steps R10 lists; rope as in R7.
+
+    latent: [N, 512], rope: [N, 64] fp16/bf16 values; global_scale: g > 0,
+    taken as the float32 value the caller passes.
+    """
+    lat = np.asarray(latent, dtype=np.float64).reshape(-1, LATENT_DIM)
+    rp = np.asarray(rope, dtype=np.float64).reshape(-1, ROPE_DIM)
+    n = lat.shape[0]
+    g32 = np.float32(global_scale)
+    d = np.float32(6.0) * g32                                     # fl32(6 g)
+    grp = lat.reshape(n, N_GROUPS, GROUP)
+    amax = np.abs(grp).max(axis=2).astype(np.float32)             # exact (fp16/bf16 inputs)
+    q = (amax / d).astype(np.float64)                             # fl32(amax / d), held exactly
+    scale_codes = e4m3_encode(q)                                  # RNE, saturating (R3)
+    sv = e4m3_decode(scale_codes)[:, :, None]                     # [N, 32, 1]
+    ax = np.abs(grp)
+    mag = np.zeros(grp.shape, dtype=np.int64)
+    for t, up in zip(E2M1_THRESHOLDS, E2M1_TIE_UP):
+        thr = (t * sv * np.float64(g32)).astype(np.float32).astype(np.float64)   # exact product, one rounding
+        mag += (ax >= thr) if up else (ax > thr)
+    mag = np.where(sv == 0.0, 0, mag)
+    codes = (mag | (np.signbit(grp).astype(np.int64) << 3)).reshape(n, LATENT_DIM).astype(np.uint16)
+    out = np.empty((n, ROW_BYTES), dtype=np.uint8)
+    out[:, :SCALE_OFF] = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    out[:, SCALE_OFF:ROPE_OFF] = scale_codes
+    out[:, ROPE_OFF:] = e4m3_encode(rp)
+    return out
+
+
+def nvfp4_decode_rows_2level(rows, global_scale: float) -> tuple[np.ndarray, np.ndarray]:
+    """Decoded (latent * g, rope) of two-level rows (R10)."""
+    lat, rope = nvfp4_decode_rows(rows)
+    return lat * float(np.float32(global_scale)), rope
 
 
 def nvfp4_decode_rows(rows) -> tuple[np.ndarray, np.ndarray]:

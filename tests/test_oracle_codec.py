@@ -398,3 +398,78 @@ def test_staged_rows_definition():
     assert np.array_equal(rows[[0, 2, 3, 6, 7]], ref)
     # rope values are already E4M3, so staging keeps them exactly
     assert np.array_equal(rows[[0, 2, 3, 6, 7], 512:], cache[[3, 7, 39, 0, 5], 288:])
+
+
+# ---------------------------------------------------------------- two-level variant (R10)
+
+
+def _wide_rows(rng, n, spread):
+    lat = rng.standard_normal((n, 512)) * np.exp(spread * rng.standard_normal((n, 1)))
+    return _fp16(lat), _fp16(rng.standard_normal((n, 64)))
+
+
+def test_two_level_with_unit_scale_is_the_one_level_encoding():
+    rng = np.random.default_rng(40)
+    lat, rope = _wide_rows(rng, 64, 1.0)
+    lat[0, :16] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 2)     # ties at scale 1
+    assert np.array_equal(codec.nvfp4_encode_rows_2level(lat, rope, 1.0), codec.nvfp4_encode_rows(lat, rope))
+
+
+@pytest.mark.parametrize("k", [-20, -7, -1, 3, 12])
+def test_two_level_with_power_of_two_scale_encodes_the_scaled_values(k):
+    """For g = 2^k every FP32 step is exact, so the bytes equal the one-level
+    encoding of latent / g (an identity of the definitions)."""
+    rng = np.random.default_rng(41 + k)
+    lat, rope = _wide_rows(rng, 64, 1.5)
+    g = 2.0 ** k
+    assert np.array_equal(codec.nvfp4_encode_rows_2level(lat, rope, g), codec.nvfp4_encode_rows(lat / g, rope))
+
+
+def test_two_level_codes_are_the_nearest_grid_points_in_exact_arithmetic():
+    """Away from the few values within an FP32 rounding of a decision boundary,
+    scale and codes are the exact round-to-nearest-even choices for an
+    arbitrary g, checked with rationals."""
+    rng = np.random.default_rng(42)
+    lat, rope = _wide_rows(rng, 12, 1.0)
+    g = float(np.float32(0.0371))
+    rows = codec.nvfp4_encode_rows_2level(lat, rope, g)
+    lv, _ = codec.nvfp4_decode_rows(rows)
+    gf = Fr(g)
+    grid = [Fr(v) for v in codec.E2M1_GRID]
+    e4 = [Fr(float(v)) for v in codec.E4M3_POS]
+    checked = 0
+    for r in range(lat.shape[0]):
+        for gi in range(32):
+            x = [Fr(float(v)) for v in lat[r, 16 * gi:16 * gi + 16]]
+            q = max(abs(v) for v in x) / (6 * gf)
+            # nearest E4M3 to the exact quotient; skip groups near a midpoint
+            dist = sorted((abs(q - v), i) for i, v in enumerate(e4))
+            if dist[1][0] - dist[0][0] <= q * Fr(2, 2 ** 23):
+                continue
+            s = e4[dist[0][1]]
+            assert Fr(float(codec.e4m3_decode(rows[r, 256 + gi]))) == s
+            for j, v in enumerate(x):
+                cand = sorted((abs(abs(v) - c * s * gf), k) for k, c in enumerate(grid))
+                if s == 0 or cand[1][0] - cand[0][0] <= abs(v) * Fr(2, 2 ** 23):
+                    continue
+                assert Fr(abs(float(lv[r, 16 * gi + j]))) == grid[cand[0][1]] * s
+                checked += 1
+    assert checked > 5000
+
+
+def test_two_level_scale_extends_the_range():
+    """Latents far past the one-level range (largest code x largest scale =
+    2688) or far below it keep their E2M1 precision with g = amax / 2688,
+    while the one-level encoding saturates or flushes them."""
+    rng = np.random.default_rng(43)
+    for factor in (1e4, 1e-6):
+        lat = rng.standard_normal((8, 512)) * factor
+        lat = lat.astype(np.float32).astype(np.float64)      # beyond fp16's range: float32 inputs
+        rope = np.zeros((8, 64))
+        g = float(np.float32(np.abs(lat).max() / 2688.0))
+        two, _ = codec.nvfp4_decode_rows_2level(codec.nvfp4_encode_rows_2level(lat, rope, g), g)
+        one, _ = codec.nvfp4_decode_rows(codec.nvfp4_encode_rows(lat, rope))
+        gmax = np.abs(lat.reshape(8, 32, 16)).max(axis=2, keepdims=True)
+        err2 = (np.abs(two - lat).reshape(8, 32, 16) / gmax).max()
+        err1 = (np.abs(one - lat).reshape(8, 32, 16) / gmax).max()
+        assert err2 <= 0.25 and err1 >= 0.9, (factor, err1, err2)
