@@ -96,6 +96,31 @@ int mla_nvfp4_quantize_append(const void* latent, int64_t latent_row_stride,
                               void* stream);
 
 /*
+ * mla_nvfp4_quantize_append_2level -- the two-level NVFP4 variant: the same
+ * 352-byte rows, with a per-tensor FP32 scale g (global_scale, > 0) over the
+ * E4M3 group scales, so latent element j decodes to code_j * scale_g * g
+ * (the rope is not scaled).  This is NVFP4's second scale level; the
+ * write-up ("Making room for low-latency decode") names the per-16 FP8
+ * scale only.  For an arbitrary g the encoder's decisions are defined by
+ * these float32 steps (all exact when g is a power of two, and equal to the
+ * one-level encoding when g = 1):
+ *   scale_g = E4M3(fl32(amax_g / fl32(6 * g))), nearest even, saturating;
+ *   code_j  = magnitude = thresholds passed among fl32(t * scale_g * g),
+ *             t = .25, .75, 1.25, 1.75, 2.5, 3.5, 5 (|x| > threshold for
+ *             .25, 1.25, 2.5, 5; >= for .75, 1.75, 3.5: ties to even);
+ *             0 when scale_g is 0; sign bit copied.
+ * Decode such rows with mla_sparse_decode(kv_scale = g).  Arguments as for
+ * mla_nvfp4_quantize_append; MLA_ERR_INVALID_ARG unless g and fl32(6 g)
+ * are positive and finite.
+ */
+int mla_nvfp4_quantize_append_2level(const void* latent, int64_t latent_row_stride,
+                                     const void* rope, int64_t rope_row_stride,
+                                     int dtype, int64_t n,
+                                     const int64_t* slot_mapping,
+                                     uint8_t* cache, int64_t cache_rows,
+                                     float global_scale, void* stream);
+
+/*
  * mla_fp8_quantize_append -- the comparison format: 576-byte FP8 rows,
  * byte = E4M3(value / kv_scale) (round to nearest even, saturating), for
  * the 512 latent values then the 64 rope values.  The FP8 row is the format
@@ -152,8 +177,14 @@ size_t mla_sparse_decode_workspace_size(int64_t num_tokens, int32_t num_heads,
  *   cache             device, [cache_rows, 352] (NVFP4) or [cache_rows, 576]
  *                     (FP8), 16-byte aligned.
  *   cache_fmt         MLA_CACHE_NVFP4_352 or MLA_CACHE_FP8_576.
- *   kv_scale          FP8 format only: value = E4M3 byte * kv_scale; ignored
- *                     for NVFP4.
+ *   kv_scale          the cache's per-tensor scale.  FP8 rows: value = E4M3
+ *                     byte * kv_scale (a power of two).  NVFP4 rows: the
+ *                     two-level latent scale g (1 for one-level rows): latent
+ *                     values are code * scale * g, the rope is unscaled.  The
+ *                     FP16 operands leave g out: the kernel scales the rope
+ *                     part of each score by 1/g in FP32 before the latent part
+ *                     adds onto it, and applies g to the softmax scale and to
+ *                     the output.
  *   indices           device, [T, topk] int32, row stride idx_stride_t
  *                     (>= topk); negative = masked pad.  1 <= topk <= 2048.
  *   block_table       optional (NULL = indices are physical cache rows).

@@ -6,6 +6,7 @@ stream.  Every step of the computation runs in the library's HIP kernels;
 PyTorch only provides device memory and streams.
 
     quantize_append(latent, rope, slots, cache)        352-byte NVFP4 rows
+    quantize_append_2level(..., global_scale)          two-level NVFP4 rows
     fp8_quantize_append(latent, rope, slots, cache)    576-byte FP8 rows
     sparse_decode(q, cache, indices, sm_scale, ...)    -> (out, lse)
     sparse_decode_noalloc(q, cache, indices, ...)      the same without a workspace
@@ -120,6 +121,14 @@ def quantize_append(latent: torch.Tensor, rope: torch.Tensor, slots: torch.Tenso
     _append("mla_nvfp4_quantize_append", latent, rope, slots, cache, NVFP4_ROW_BYTES)
 
 
+def quantize_append_2level(latent: torch.Tensor, rope: torch.Tensor, slots: torch.Tensor,
+                           cache: torch.Tensor, global_scale: float) -> None:
+    """Two-level NVFP4 rows: group scales and codes of latent / global_scale
+    (decode with ``sparse_decode(..., kv_scale=global_scale)``)."""
+    _append("mla_nvfp4_quantize_append_2level", latent, rope, slots, cache, NVFP4_ROW_BYTES,
+            (float(global_scale),))
+
+
 def fp8_quantize_append(latent, rope, slots, cache, kv_scale: float = 1.0) -> None:
     """Encode rows to 576-byte FP8 (E4M3 of value / kv_scale) at ``slots``."""
     _append("mla_fp8_quantize_append", latent, rope, slots, cache, FP8_ROW_BYTES, (float(kv_scale),))
@@ -168,7 +177,10 @@ def _decode_args(q, cache, indices, fmt, block_table, token_seq, out, lse, works
 def sparse_decode(q: torch.Tensor, cache: torch.Tensor, indices: torch.Tensor, sm_scale: float, *,
                   fmt: str = "nvfp4", kv_scale: float = 1.0, block_table=None, token_seq=None,
                   block_size: int = 64, workspace=None, num_splits: int = 0, out=None, lse=None):
-    """Sparse MLA decode; returns (out [T, H, 512] in q's dtype, lse [T, H] float32)."""
+    """Sparse MLA decode; returns (out [T, H, 512] in q's dtype, lse [T, H] float32).
+
+    kv_scale is the cache's per-tensor scale: FP8 rows' power-of-two scale,
+    or two-level NVFP4 rows' latent scale (1 for one-level rows)."""
     lib = load()
     dev, fmt_code, bt, out, lse = _decode_args(q, cache, indices, fmt, block_table, token_seq, out, lse,
                                                workspace)

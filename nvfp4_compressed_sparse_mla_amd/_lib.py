@@ -16,6 +16,8 @@ c_i64, c_i32, c_int, c_f32, c_vp, c_size = (ctypes.c_int64, ctypes.c_int32, ctyp
                                             ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t)
 SIGNATURES = {
     "mla_nvfp4_quantize_append": (c_int, [c_vp, c_i64, c_vp, c_i64, c_int, c_i64, c_vp, c_vp, c_i64, c_vp]),
+    "mla_nvfp4_quantize_append_2level": (c_int, [c_vp, c_i64, c_vp, c_i64, c_int, c_i64, c_vp, c_vp, c_i64,
+                                                 c_f32, c_vp]),
     "mla_fp8_quantize_append": (c_int, [c_vp, c_i64, c_vp, c_i64, c_int, c_i64, c_vp, c_vp, c_i64, c_f32, c_vp]),
     "mla_sparse_decode_num_splits": (c_i32, [c_i64, c_i32, c_i32]),
     "mla_sparse_decode_workspace_size": (c_size, [c_i64, c_i32, c_i32, c_i32]),

@@ -19,6 +19,14 @@ bool pow2_scale(float s) {
   return frexpf(s, &e) == 0.5f && e >= -20 && e <= 20;
 }
 
+// A two-level row's per-tensor latent scale: positive, finite, with a finite
+// non-zero fl32(6 g) (the encoder divides by it).
+bool latent_scale_ok(float g) {
+  if (!(g > 0.0f) || !isfinite(g)) return false;
+  const float six_g = 6.0f * g;
+  return isfinite(six_g) && six_g > 0.0f;
+}
+
 // Benchmark timing state of one host thread (see mla_kernel_timing).
 struct Timing {
   bool enabled = false, recorded = false;
@@ -94,6 +102,7 @@ int decode_call(const void* q, int q_dtype, int64_t num_tokens, int32_t num_head
   if (cache_rows < 0 || cache_rows > 0x7FFFFFFF) return MLA_ERR_INVALID_ARG;
   if (!isfinite(sm_scale)) return MLA_ERR_INVALID_ARG;
   if (cache_fmt == MLA_CACHE_FP8_576 && !pow2_scale(kv_scale)) return MLA_ERR_INVALID_ARG;
+  if (cache_fmt == MLA_CACHE_NVFP4_352 && !latent_scale_ok(kv_scale)) return MLA_ERR_INVALID_ARG;
   if (num_tokens == 0) return MLA_OK;
   if (!q || !cache || !indices || !out) return MLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(cache) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
@@ -143,6 +152,8 @@ int decode_call(const void* q, int q_dtype, int64_t num_tokens, int32_t num_head
   p.cache = cache;
   p.cache_rows = cache_rows;
   p.kv_scale = cache_fmt == MLA_CACHE_FP8_576 ? kv_scale : 1.0f;
+  p.lat_scale = cache_fmt == MLA_CACHE_NVFP4_352 ? kv_scale : 1.0f;
+  p.inv_lat_scale = 1.0f / p.lat_scale;
   p.idx = indices;
   p.topk = topk;
   p.idx_st = idx_stride_t;
@@ -153,7 +164,7 @@ int decode_call(const void* q, int q_dtype, int64_t num_tokens, int32_t num_head
   p.bt_rows = block_table ? bt_rows : 0;
   p.bt_st = block_table ? bt_stride : 0;
   p.tok_seq = block_table ? token_seq : nullptr;
-  p.sm_log2 = fabsf(sm_scale) * 1.4426950408889634f * p.kv_scale;
+  p.sm_log2 = fabsf(sm_scale) * 1.4426950408889634f * p.kv_scale * p.lat_scale;
   p.q_neg = sm_scale < 0.0f;
   p.out = out;
   p.lse = lse;
@@ -228,7 +239,23 @@ int mla_nvfp4_quantize_append(const void* latent, int64_t latent_row_stride, con
   const mla::KernelEvents ev = timing_events();
   return launched(mla::launch_nvfp4_quantize(latent, latent_row_stride, rope, rope_row_stride,
                                              dtype == MLA_BF16, n, slot_mapping, cache, cache_rows,
-                                             (hipStream_t)stream, ev),
+                                             1.0f, (hipStream_t)stream, ev),
+                  ev);
+}
+
+int mla_nvfp4_quantize_append_2level(const void* latent, int64_t latent_row_stride, const void* rope,
+                                     int64_t rope_row_stride, int dtype, int64_t n,
+                                     const int64_t* slot_mapping, uint8_t* cache, int64_t cache_rows,
+                                     float global_scale, void* stream) {
+  int st = quantize_checks(latent, latent_row_stride, rope, rope_row_stride, dtype, n, slot_mapping,
+                           cache, cache_rows);
+  if (st != MLA_OK) return st;
+  if (!latent_scale_ok(global_scale)) return MLA_ERR_INVALID_ARG;
+  if (n == 0) return MLA_OK;
+  const mla::KernelEvents ev = timing_events();
+  return launched(mla::launch_nvfp4_quantize(latent, latent_row_stride, rope, rope_row_stride,
+                                             dtype == MLA_BF16, n, slot_mapping, cache, cache_rows,
+                                             global_scale, (hipStream_t)stream, ev),
                   ev);
 }
 

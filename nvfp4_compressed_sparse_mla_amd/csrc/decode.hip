@@ -308,19 +308,18 @@ __device__ __forceinline__ void group_scales(half2_t (&sh)[4], const u32x2& sc) 
   sh[3] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[1], 1.0f, true));
 }
 
+// Eight q elements (fp16 or bf16 bits) as the FP16 score operand: fp16 is
+// taken as is, bf16 is rounded to FP16.
 template <bool kBf16>
-__device__ __forceinline__ half8_t load_q8(const uint16_t* p) {
-  const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+__device__ __forceinline__ u32x4 q8_operand(const u32x4& u) {
   if constexpr (!kBf16) {
-    return __builtin_bit_cast(half8_t, u);
+    return u;
   } else {
-    half8_t h;
+    u32x4 r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h[2 * i] = (half_t)__uint_as_float(u[i] << 16);
-      h[2 * i + 1] = (half_t)__uint_as_float(u[i] & 0xFFFF0000u);
-    }
-    return h;
+    for (int i = 0; i < 4; ++i)
+      r[i] = as_u32((half2_t){(half_t)__uint_as_float(u[i] << 16), (half_t)__uint_as_float(u[i] & 0xFFFF0000u)});
+    return r;
   }
 }
 
@@ -447,6 +446,22 @@ __device__ __forceinline__ void score_mfma_drain(float4_t (&acc)[2]) {
   MLA_DEVICE_ASM("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]));
 }
 
+// Two-level NVFP4 rows: latent values carry a per-tensor scale g that the
+// FP16 operands leave out.  The rope part of a tile's scores (its two
+// K-steps come first) is multiplied by 1/g in FP32 before the latent
+// K-steps add onto it, and the softmax scale carries g, so the score is
+// g * (rope / g + latent) = latent * g + rope to FP32 rounding.  The drain
+// waits out the rope MFMAs' latency; the trailing wait states cover the next
+// (assembly) MFMA's read of the scaled accumulators.
+__device__ __forceinline__ void scale_rope_scores(float4_t (&acc)[2], float inv_g) {
+  score_mfma_drain(acc);
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[hb][j] *= inv_g;
+  MLA_DEVICE_ASM("s_nop 2" : "+v"(acc[0]), "+v"(acc[1]));
+}
+
 // head of accumulator element j of `lane` in the 32x32 MFMA C layout
 __device__ __forceinline__ int c_head(int j, int lane) { return (j >> 2) * 8 + 4 * (lane >> 5) + (j & 3); }
 
@@ -520,7 +535,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   // past H repeat the last one), and later staged through the still idle V
   // buffer, from where each wave reads the B operands of its score MFMAs.
   constexpr int kQChunks = kHG * (kQK / 8) / kThreads;   // 9
-  half8_t qstage[kQChunks];
+  u32x4 qstage[kQChunks];     // raw fp16 / bf16 bits
   half8_t qreg[2][kKSteps];   // filled once the rows' DMA is issued (see below)
   {
     const uint16_t* qt = reinterpret_cast<const uint16_t*>(p.q) + t * p.q_st;
@@ -528,7 +543,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     for (int m = 0; m < kQChunks; ++m) {
       const int c = tid + kThreads * m, h = c / (kQK / 8), dc = c - h * (kQK / 8);
       const int head = min(g * kHG + h, p.H - 1);
-      qstage[m] = load_q8<kBf16>(qt + (int64_t)head * p.q_sh + 8 * dc);
+      qstage[m] = *reinterpret_cast<const u32x4*>(qt + (int64_t)head * p.q_sh + 8 * dc);
     }
   }
 
@@ -651,6 +666,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   // it by more than kLazy (P would leave FP16), one ballot deciding; then O
   // and the row sums are rescaled in place.
   const float sm = p.sm_log2;
+  const bool two_level = kFmt == kFmtNvfp4 && p.lat_scale != 1.0f;
 #pragma unroll
   for (int nb = 0; nb < 16; ++nb)
 #pragma unroll
@@ -808,7 +824,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
         kgq = (d - kLatent) >> 4;
         ks = 16 + (((d - kLatent) >> 3) & 1);
       }
-      u32x4 u = __builtin_bit_cast(u32x4, qstage[m]);
+      u32x4 u = q8_operand<kBf16>(qstage[m]);
       if (p.q_neg) u ^= 0x80008000u;
       const uint32_t a = qs + 16 * (((h >> 4) * kKSteps + ks) * 64 + 16 * kgq + (h & 15));
       MLA_DEVICE_ASM("ds_write_b128 %0, %1" :: "v"(a), "v"(u) : "memory");
@@ -833,6 +849,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
       const uint32_t slot = tile_start(0);
 #pragma unroll
       for (int ks = 16; ks < kKSteps; ++ks) score_step(0, ks, slot);   // rope first: its bytes are then dead
+      if (two_level) scale_rope_scores(sacc, p.inv_lat_scale);
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) score_step(0, ks, slot);
     }
@@ -861,6 +878,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
         const half8_t kop = kstep8<kFmt>(raw, ks);
         score_mfma2(sacc, kop, qreg[0][ks], qreg[1][ks], ks == 16);
       }
+      if (two_level) scale_rope_scores(sacc, p.inv_lat_scale);
       // Slot t (latent K-step t): the value MFMA of one column block of
       // tile k-1, the conversions of K-step t+1 split around the two score
       // MFMAs of K-step t, then the V write of K-step t+1.  The order is
@@ -983,7 +1001,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   // b (column block within the round x 4 + element quad) sits at byte
   // 1136 b + 16 s + 32 (s >> 4): the writers' 64 lanes and the readers' 8
   // consecutive slots (8 columns of 4 heads) are both free of bank conflicts.
-  const float out_mul = p.kv_scale;  // FP8 rows: values carry kv_scale
+  const float out_mul = p.kv_scale * p.lat_scale;  // values carry the cache's per-tensor scale
   const int64_t H = p.H;
   {
     constexpr uint32_t kXBlock = 1136, kXRegion = 32 * kXBlock;

@@ -154,6 +154,16 @@ __device__ __forceinline__ uint32_t e2m1_mag(float ax, float s) {
   return s > 0.0f ? m : 0u;
 }
 
+// The same against the two-level scale s * g: thresholds fl32((t * s) * g),
+// t * s exact; with g = 1 identical to e2m1_mag.
+__device__ __forceinline__ uint32_t e2m1_mag_scaled(float ax, float s, float g) {
+  uint32_t m = (uint32_t)(ax > (0.25f * s) * g) + (uint32_t)(ax >= (0.75f * s) * g) +
+               (uint32_t)(ax > (1.25f * s) * g) + (uint32_t)(ax >= (1.75f * s) * g) +
+               (uint32_t)(ax > (2.5f * s) * g) + (uint32_t)(ax >= (3.5f * s) * g) +
+               (uint32_t)(ax > (5.0f * s) * g);
+  return s > 0.0f ? m : 0u;
+}
+
 // Decoded value of an E4M3 magnitude code (for encoders that need the
 // rounded scale as a float).
 __device__ __forceinline__ float e4m3_mag_value(uint32_t c) {

@@ -28,6 +28,8 @@ struct DecodeParams {
   const uint8_t* cache;
   int64_t cache_rows;
   float kv_scale;           // FP8 rows: value = byte * kv_scale (1 for NVFP4)
+  float lat_scale;          // NVFP4 rows: per-tensor scale g of the latent (1 for FP8 rows)
+  float inv_lat_scale;      // fl32(1 / g)
   const int32_t* idx;
   int topk;
   int64_t idx_st;
@@ -36,7 +38,7 @@ struct DecodeParams {
   int bs_log2;              // log2(bs) if bs is a power of two, else -1
   int64_t bt_st;
   const int32_t* tok_seq;
-  float sm_log2;            // |sm_scale| * log2(e) * kv_scale (>= 0)
+  float sm_log2;            // |sm_scale| * log2(e) * kv_scale * lat_scale (>= 0)
   int q_neg;                // sm_scale < 0: q is negated on load (exact), so sm_log2 >= 0
   void* out;
   float* lse;
@@ -57,7 +59,8 @@ hipError_t launch_decode(const DecodeParams& p, int fmt, bool bf16, hipStream_t 
 
 hipError_t launch_nvfp4_quantize(const void* latent, int64_t ls, const void* rope, int64_t rs,
                                  bool bf16, int64_t n, const int64_t* slots, uint8_t* cache,
-                                 int64_t cache_rows, hipStream_t stream, const KernelEvents& ev);
+                                 int64_t cache_rows, float global_scale, hipStream_t stream,
+                                 const KernelEvents& ev);
 hipError_t launch_fp8_quantize(const void* latent, int64_t ls, const void* rope, int64_t rs,
                                bool bf16, int64_t n, const int64_t* slots, uint8_t* cache,
                                int64_t cache_rows, float kv_scale, hipStream_t stream,

@@ -40,11 +40,15 @@ __device__ __forceinline__ float load_scalar(const uint16_t* p) {
   else return (float)__builtin_bit_cast(half_t, *p);
 }
 
+// Two-level variant: gscale (g) is the per-tensor global scale of the latent
+// (1 for one-level rows) and six_g = fl32(6 g).  The group scale is E4M3 of
+// fl32(amax / six_g) and the code thresholds are fl32((t * s) * g), t * s
+// being exact; with g = 1 every step is exact (the one-level encoding).
 template <bool kBf16>
 __global__ __launch_bounds__(256) void nvfp4_quantize_append_kernel(
     const uint16_t* __restrict__ latent, int64_t lat_stride, const uint16_t* __restrict__ rope,
     int64_t rope_stride, int64_t n, const int64_t* __restrict__ slots, uint8_t* __restrict__ cache,
-    int64_t cache_rows) {
+    int64_t cache_rows, float gscale, float six_g) {
   const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
   const int g = threadIdx.x & 31;
   if (row >= n) return;
@@ -57,15 +61,15 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_append_kernel(
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
-  // scale = E4M3(amax / 6): the correctly rounded float32 quotient rounds to
-  // the same E4M3 value as the exact quotient (an FP16/BF16 amax never puts
-  // it on or across an E4M3 rounding midpoint).
-  const uint32_t sc = e4m3_mag_rne(__fdiv_rn(amax, 6.0f));
+  // scale = E4M3(amax / 6) for one-level rows: the correctly rounded float32
+  // quotient rounds to the same E4M3 value as the exact quotient (an
+  // FP16/BF16 amax never puts it on or across an E4M3 rounding midpoint).
+  const uint32_t sc = e4m3_mag_rne(__fdiv_rn(amax, six_g));
   const float s = e4m3_mag_value(sc);
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    uint32_t nib = e2m1_mag(__builtin_fabsf(v[i]), s) | (((signs >> i) & 1u) << 3);
+    uint32_t nib = e2m1_mag_scaled(__builtin_fabsf(v[i]), s, gscale) | (((signs >> i) & 1u) << 3);
     if (i < 8) lo |= nib << (4 * i);
     else hi |= nib << (4 * (i - 8));
   }
@@ -108,11 +112,13 @@ __global__ __launch_bounds__(256) void fp8_quantize_append_kernel(
 
 hipError_t launch_nvfp4_quantize(const void* latent, int64_t ls, const void* rope, int64_t rs,
                                  bool bf16, int64_t n, const int64_t* slots, uint8_t* cache,
-                                 int64_t cache_rows, hipStream_t stream, const KernelEvents& ev) {
+                                 int64_t cache_rows, float global_scale, hipStream_t stream,
+                                 const KernelEvents& ev) {
   dim3 grid((unsigned)((n + 7) / 8)), block(256);
   const uint16_t* lat = (const uint16_t*)latent;
   const uint16_t* rp = (const uint16_t*)rope;
-  void* args[] = {&lat, &ls, &rp, &rs, &n, &slots, &cache, &cache_rows};
+  float g = global_scale, six_g = 6.0f * global_scale;   // float32 product, rounded once
+  void* args[] = {&lat, &ls, &rp, &rs, &n, &slots, &cache, &cache_rows, &g, &six_g};
   const void* fn = bf16 ? (const void*)nvfp4_quantize_append_kernel<true>
                         : (const void*)nvfp4_quantize_append_kernel<false>;
   return launch_kernel(fn, grid, block, args, stream, ev);

@@ -32,8 +32,13 @@ def encode_rows(lat16: np.ndarray, rope16: np.ndarray, fmt: str = "nvfp4", kv_sc
     for i in range(0, lat16.shape[0], ENC_CHUNK):
         l = lat16[i:i + ENC_CHUNK].astype(np.float64)
         r = rope16[i:i + ENC_CHUNK].astype(np.float64)
-        out.append(codec.nvfp4_encode_rows(l, r) if fmt == "nvfp4" else codec.fp8_encode_rows(l, r, kv_scale))
-    width = codec.ROW_BYTES if fmt == "nvfp4" else codec.FP8_ROW_BYTES
+        if fmt == "nvfp4":
+            out.append(codec.nvfp4_encode_rows(l, r))
+        elif fmt == "nvfp4_2level":
+            out.append(codec.nvfp4_encode_rows_2level(l, r, kv_scale))
+        else:
+            out.append(codec.fp8_encode_rows(l, r, kv_scale))
+    width = codec.FP8_ROW_BYTES if fmt == "fp8" else codec.ROW_BYTES
     return np.concatenate(out, axis=0) if out else np.zeros((0, width), np.uint8)
 
 
@@ -76,6 +81,8 @@ def oracle_reference(latent, rope, q, indices, sm_scale, tokens=None, block_tabl
         assert bad.size == 0, f"{bad.size} cache rows differ from the oracle encoding, e.g. row {touched[bad[0]]}"
     if fmt == "nvfp4":
         lat, rp = codec.nvfp4_decode_rows(enc)
+    elif fmt == "nvfp4_2level":
+        lat, rp = codec.nvfp4_decode_rows_2level(enc, kv_scale)
     else:
         lat, rp = codec.fp8_decode_rows(enc, kv_scale)
     K = max(1, max((len(l) for l in lists), default=1))
