@@ -57,6 +57,8 @@ TRIO_CONFIGS = ("decode15", "padded35", "batch128")
 # at the prefill chunk every token would rescan its whole sequence
 INDEXER_CONFIGS = ("tiny", "decode15", "padded35", "batch128")
 INDEXER_KEY_BYTES = 128
+# two-level NVFP4 rows (per-tensor latent scale) are timed at these
+TWO_LEVEL_CONFIGS = ("decode15", "batch128")
 
 DESCRIPTIONS = {
     "tiny": "1 token x 16 heads, 256 picks of a 4,096-row NVFP4 pool",
@@ -269,7 +271,38 @@ def _measure(torch, mla, c: Case, steps: int, warmup: int, comparators: bool):
         r["trio"] = _comparators(torch, mla, c, n)
     if c.name in INDEXER_CONFIGS:
         r["indexer"] = _indexer(torch, mla, c, n)
+    if c.name in TWO_LEVEL_CONFIGS:
+        r["two_level"] = _two_level(torch, mla, c, n)
     return r, kern
+
+
+def _two_level(torch, mla, c: Case, n: int):
+    """The same decode over two-level NVFP4 rows (global scale amax / 2688),
+    and the two-level quantize-append of the step's new rows."""
+    w = c.w
+    g = float(w.latent.float().abs().max().item()) / 2688.0
+    cache2 = torch.empty_like(c.cache)
+    mla.quantize_append_2level(w.latent, w.rope, torch.arange(w.pool_rows, dtype=torch.int64, device=c.cache.device),
+                               cache2, g)
+
+    def dec():
+        mla.sparse_decode(w.q, cache2, w.indices, w.sm_scale, kv_scale=g, block_table=w.block_table,
+                          token_seq=w.token_seq, block_size=w.block_size, workspace=c.ws, num_splits=c.splits,
+                          out=c.out, lse=c.lse)
+
+    def app():
+        mla.quantize_append_2level(c.app_lat, c.app_rope, c.app_slots, cache2, g)
+
+    for _ in range(3):
+        c.flush()
+        dec()
+    torch.cuda.synchronize()
+    kd = _kernel_ms(mla, dec, n, c.flush)
+    ka = _kernel_ms(mla, app, max(10, n // 2), c.flush)
+    del cache2
+    return {"global_scale": g, "decode_kernel_us": _stats_us(kd),
+            "gathered_gbs_kernel": round(c.gathered / (statistics.mean(kd) * 1e-3) / 1e9, 2),
+            "append_kernel_us": round(1e3 * statistics.mean(ka), 3)}
 
 
 def _indexer(torch, mla, c: Case, n: int):

@@ -136,7 +136,9 @@ int mla_fp8_quantize_append(const void* latent, int64_t latent_row_stride,
                             float kv_scale, void* stream);
 
 /*
- * mla_sparse_decode_num_splits -- the launch sizer.  Number of workgroups
+ * mla_sparse_decode_num_splits -- the launch sizer (Prime Inference write-up,
+ * "A native NVFP4 sparse-MLA decode kernel": several cooperating blocks
+ * divide each token's selected rows).  Number of workgroups
  * that share one token's selected rows for a call with these sizes
  * (num_splits = 0 in mla_sparse_decode).  The split count follows the token
  * batch the way the write-up's cluster size does (wireai.ir, 4-bit-caches
@@ -148,7 +150,11 @@ int32_t mla_sparse_decode_num_splits(int64_t num_tokens, int32_t num_heads,
 /*
  * mla_sparse_decode_workspace_size -- bytes of device workspace
  * mla_sparse_decode needs for these sizes; num_splits = 0 means the launch
- * sizer's choice.  The workspace must be zero-filled before its first use;
+ * sizer's choice.  The workspace holds what the write-up's cooperating
+ * blocks exchange ("A native NVFP4 sparse-MLA decode kernel": the blocks
+ * sharing a token's rows combine their partial results without a second
+ * launch): per (token, group of 32 heads) an arrival counter and, with more
+ * than one split, each split's partial output and log-sum-exp.  The workspace must be zero-filled before its first use;
  * every completed call leaves it in that state again.  Returns 0 on bad
  * arguments.
  */
@@ -156,7 +162,14 @@ size_t mla_sparse_decode_workspace_size(int64_t num_tokens, int32_t num_heads,
                                         int32_t topk, int32_t num_splits);
 
 /*
- * mla_sparse_decode -- sparse MLA decode attention over a compressed cache.
+ * mla_sparse_decode -- sparse MLA decode attention over a compressed cache
+ * (Prime Inference write-up, "A native NVFP4 sparse-MLA decode kernel":
+ * attention reads only the rows the sparse indexer selected, loads them
+ * compressed and unpacks them on chip, with FP16 operands and FP32
+ * accumulation; each token's rows are divided among cooperating blocks whose
+ * partial results are combined within the same launch; wireai.ir article,
+ * 4-bit-caches section: the block count follows the token batch and the
+ * 2048-slot list's unused slots are padded).
  *
  * For token t and head h, with the valid slots j of indices[t] (index >= 0;
  * a row listed twice counts twice) mapped to cache rows r_j, keys
