@@ -44,16 +44,21 @@ __device__ __forceinline__ float load_scalar(const uint16_t* p) {
 // (1 for one-level rows) and six_g = fl32(6 g).  The group scale is E4M3 of
 // fl32(amax / six_g) and the code thresholds are fl32((t * s) * g), t * s
 // being exact; with g = 1 every step is exact (the one-level encoding).
+//
+// Each row is assembled in LDS (nibbles, scales and rope from its 32 lanes)
+// and written with 22 16-byte stores.
 template <bool kBf16>
 __global__ __launch_bounds__(256) void nvfp4_quantize_append_kernel(
     const uint16_t* __restrict__ latent, int64_t lat_stride, const uint16_t* __restrict__ rope,
     int64_t rope_stride, int64_t n, const int64_t* __restrict__ slots, uint8_t* __restrict__ cache,
     int64_t cache_rows, float gscale, float six_g) {
+  __shared__ __align__(16) uint8_t rows_s[8][kRowBytes];
   const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
   const int g = threadIdx.x & 31;
   if (row >= n) return;
   const int64_t slot = slots[row];
   if (slot < 0 || slot >= cache_rows) return;
+  uint8_t* const stage = rows_s[threadIdx.x >> 5];
 
   float v[16];
   uint32_t signs;
@@ -73,13 +78,18 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_append_kernel(
     if (i < 8) lo |= nib << (4 * i);
     else hi |= nib << (4 * (i - 8));
   }
-  uint8_t* dst = cache + slot * kRowBytes;
-  *reinterpret_cast<u32x2*>(dst + 8 * g) = (u32x2){lo, hi};
-  dst[kScaleOff + g] = (uint8_t)sc;
+  *reinterpret_cast<u32x2*>(stage + 8 * g) = (u32x2){lo, hi};
+  stage[kScaleOff + g] = (uint8_t)sc;
   const uint16_t* rp = rope + row * rope_stride + 2 * g;
   uint32_t r0 = e4m3_encode(load_scalar<kBf16>(rp));
   uint32_t r1 = e4m3_encode(load_scalar<kBf16>(rp + 1));
-  *reinterpret_cast<uint16_t*>(dst + kRopeOff + 2 * g) = (uint16_t)(r0 | (r1 << 8));
+  *reinterpret_cast<uint16_t*>(stage + kRopeOff + 2 * g) = (uint16_t)(r0 | (r1 << 8));
+  // the row's 32 lanes belong to one wave, whose LDS operations complete in
+  // order: a wave-level wait makes the staged row visible to its own lanes
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  if (g < kRowBytes / 16)
+    *reinterpret_cast<u32x4*>(cache + slot * kRowBytes + 16 * g) = *reinterpret_cast<const u32x4*>(stage + 16 * g);
 }
 
 template <bool kBf16>
