@@ -102,6 +102,23 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* ws) {
   return v + add;
 }
 
+// N consecutive keys from position i (a multiple of N, N even; the keys
+// array is 16-byte aligned), 0 past ctx (0 marks "not a candidate").
+template <int N>
+__device__ __forceinline__ void load_keys(const uint64_t* keys, int i, int ctx, uint64_t (&k)[N]) {
+  if (i + N <= ctx) {
+#pragma unroll
+    for (int j = 0; j < N; j += 2) {
+      const u64x2 v = *reinterpret_cast<const u64x2*>(keys + i + j);
+      k[j] = v[0];
+      k[j + 1] = v[1];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; ++j) k[j] = i + j < ctx ? keys[i + j] : 0ull;
+  }
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerParams p) {
@@ -225,12 +242,12 @@ __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerPara
       const int d = 64 - pbits < kIdxHistBits ? 64 - pbits : kIdxHistBits;
       for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0u;
       __syncthreads();
-      for (int i = 2 * tid; i < ctx; i += 2 * kSelThreads) {
-        u64x2 kk;
-        if (i + 1 < ctx) kk = *reinterpret_cast<const u64x2*>(keys + i);
-        else kk = (u64x2){keys[i], 0ull};
+      constexpr int kR = 8;   // keys per thread and pass iteration
+      for (int i = kR * tid; i < ctx; i += kR * kSelThreads) {
+        uint64_t kk[kR];
+        load_keys<kR>(keys, i, ctx, kk);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < kR; ++j) {
           const uint64_t k = kk[j];
           if (k && (k >> (64 - pbits)) == prefix)
             atomicAdd(&hist[(uint32_t)(k >> (64 - pbits - d)) & ((1u << d) - 1u)], 1u);
@@ -245,19 +262,19 @@ __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerPara
     }
   }
 
-  // Emit in position order: thread i takes positions 4 i .. 4 i + 3 of each
-  // block of 4096.  A key is selected if it is above the bucket, or inside
-  // it among the first need_in in position order.
+  // Emit in position order: thread i takes positions kE i .. kE i + kE - 1
+  // of each block of kE * 1024.  A key is selected if it is above the
+  // bucket, or inside it among the first need_in in position order.
+  constexpr int kE = 16;
   uint32_t run_tie = 0, run_sel = 0;
-  for (int blk = 0; blk < ctx; blk += 4 * kSelThreads) {
-    const int p4 = blk + 4 * tid;
-    uint64_t k[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) k[j] = p4 + j < ctx ? keys[p4 + j] : 0ull;
-    bool above[4], tie[4];
+  for (int blk = 0; blk < ctx; blk += kE * kSelThreads) {
+    const int p4 = blk + kE * tid;
+    uint64_t k[kE];
+    load_keys<kE>(keys, p4, ctx, k);
+    bool above[kE], tie[kE];
     uint32_t ntie = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kE; ++j) {
       if (all) {
         above[j] = k[j] != 0ull;
         tie[j] = false;
@@ -270,10 +287,10 @@ __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerPara
     }
     const uint32_t tie_incl = block_scan(ntie, ws);
     uint32_t rank = run_tie + tie_incl - ntie;
-    bool sel[4];
+    bool sel[kE];
     uint32_t nsel = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kE; ++j) {
       sel[j] = above[j] || (tie[j] && rank < need_in);
       rank += tie[j];
       nsel += sel[j];
@@ -281,7 +298,7 @@ __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerPara
     const uint32_t sel_incl = block_scan(nsel, ws);
     uint32_t o = run_sel + sel_incl - nsel;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kE; ++j)
       if (sel[j]) out[o++] = (int32_t)(out_base + p4 + j);
     if (tid == kSelThreads - 1) {
       sh_tot = tie_incl;
