@@ -202,7 +202,9 @@ __device__ __forceinline__ void ring_read_a(Raw<kFmt>& r, uint32_t slot, const R
 }
 
 // part B issued without a wait (the caller's next lgkmcnt(0) wait covers it
-// and names these registers)
+// and names these registers).  FP8 rows carry twice the latent bytes: their
+// part B is read in two halves, the second (K-steps 12..15) one value group
+// later (ring_issue_b2), so that fewer row registers are live at once.
 template <int kFmt>
 __device__ __forceinline__ void ring_issue_b(Raw<kFmt>& r, uint32_t slot, const RingOff<kFmt>& o) {
   if constexpr (kFmt == kFmtNvfp4) {
@@ -211,6 +213,11 @@ __device__ __forceinline__ void ring_issue_b(Raw<kFmt>& r, uint32_t slot, const 
   } else {
     r.l[4] = ring_b128<1024>(slot + o.lat);
     r.l[5] = ring_b128<1280>(slot + o.lat);
+  }
+}
+template <int kFmt>
+__device__ __forceinline__ void ring_issue_b2(Raw<kFmt>& r, uint32_t slot, const RingOff<kFmt>& o) {
+  if constexpr (kFmt == kFmtFp8) {
     r.l[6] = ring_b128<1536>(slot + o.lat);
     r.l[7] = ring_b128<1792>(slot + o.lat);
   }
@@ -220,8 +227,16 @@ __device__ __forceinline__ void lgkm_wait_b(u32x4 (&b)[4], Raw<kFmt>& r) {
   if constexpr (kFmt == kFmtNvfp4)
     MLA_DEVICE_ASM("s_waitcnt lgkmcnt(4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(r.l[2]), "+v"(r.l[3]));
   else
-    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(4)"
-                   : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(r.l[4]), "+v"(r.l[5]), "+v"(r.l[6]), "+v"(r.l[7]));
+    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(r.l[4]), "+v"(r.l[5]));
+}
+// value group 2's wait: FP8 rows' second half of part B (issued during group
+// 1, ahead of that group's four V-buffer writes) is complete as well
+template <int kFmt>
+__device__ __forceinline__ void lgkm_wait4_b2(u32x4 (&b)[4], Raw<kFmt>& r) {
+  if constexpr (kFmt == kFmtNvfp4)
+    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+  else
+    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(r.l[6]), "+v"(r.l[7]));
 }
 
 template <int kFmt>
@@ -894,10 +909,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
       // during unit j, before K-step 4(j+1) overwrites it at unit j + 1
       u32x4 bvb[2][4];
       read_v4_group<0>(bvb[0], vb);
-      ring_issue_b<kFmt>(raw, slot, ro);   // latent K-steps 8..15, waited for with group 1
-      // the slot of tile k + 2 held tile k - 1 (3 slots) or tile k (2 slots),
-      // both now in registers
-      if (k + 2 < my_tiles) issue(next_row, (k + 2) % kDepth);
+      ring_issue_b<kFmt>(raw, slot, ro);   // latent K-steps 8..15 (FP8: 8..11), waited for with group 1
+      // the slot of tile k + 2 held tile k - 1 (NVFP4, 3 slots), now in
+      // registers; FP8 rows (2 slots) refill the slot of tile k itself once
+      // the last of its bytes are read, in value group 1
+      if constexpr (kFmt == kFmtNvfp4)
+        if (k + 2 < my_tiles) issue(next_row, (k + 2) % kDepth);
       static_for<0, 4>([&](auto J) {
         constexpr int j = decltype(J)::value;
         u32x4 (&bv)[4] = bvb[j & 1];
@@ -906,8 +923,13 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
         // which it waits for as well)
         if constexpr (j == 0) lgkm_wait(bv);
         else if constexpr (j == 1) lgkm_wait_b<kFmt>(bv, raw);
+        else if constexpr (j == 2) lgkm_wait4_b2<kFmt>(bv, raw);
         else lgkm_wait4(bv);
         if constexpr (j < 3) read_v4_group<j + 1>(bvb[(j + 1) & 1], vb);
+        if constexpr (j == 1 && kFmt == kFmtFp8) {
+          ring_issue_b2<kFmt>(raw, slot, ro);   // K-steps 12..15
+          if (k + 2 < my_tiles) issue(next_row, (k + 2) % kDepth);
+        }
         *reinterpret_cast<half8_t*>(vrow + 8 * (4 * j)) = kop;   // after group j's reads
         if (pending) rescale_group(J);
         static_for<0, 4>([&](auto E) {
