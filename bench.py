@@ -267,6 +267,7 @@ def _measure(torch, mla, c: Case, steps: int, warmup: int, comparators: bool):
         "append_kernel_us": round(1e3 * statistics.mean(app_kern), 3),
         "append_kernel_gbs": round(c.app_bytes / (statistics.mean(app_kern) * 1e-3) / 1e9, 2),
     }
+    r["gather_ceiling"] = _gather_ceiling(torch, mla, c, n, k_mean)
     if comparators and c.name in TRIO_CONFIGS:
         r["trio"] = _comparators(torch, mla, c, n)
     if c.name in INDEXER_CONFIGS:
@@ -274,6 +275,37 @@ def _measure(torch, mla, c: Case, steps: int, warmup: int, comparators: bool):
     if c.name in TWO_LEVEL_CONFIGS:
         r["two_level"] = _two_level(torch, mla, c, n)
     return r, kern
+
+
+def _physical_rows(torch, w):
+    """The cache rows the decode reads (valid slots, in list order), int32."""
+    idx = w.indices.long()
+    keep = idx >= 0
+    if w.block_table is not None:
+        bs = w.block_size
+        bt = w.block_table.long()[w.token_seq.long()]                 # [T, blocks]
+        blk = torch.where(keep, idx // bs, torch.zeros_like(idx))
+        rows = torch.gather(bt, 1, blk) * bs + idx % bs
+    else:
+        rows = idx
+    return rows[keep].to(torch.int32).contiguous()
+
+
+def _gather_ceiling(torch, mla, c: Case, n: int, decode_ms: float):
+    """The same rows read by a kernel that does nothing else (cold, like the
+    decode), and as many rows read contiguously: the HBM ceilings of the
+    decode's gather on this machine."""
+    rows = _physical_rows(torch, c.w)
+    seq = torch.arange(rows.numel(), dtype=torch.int32, device=rows.device)
+    sink = torch.zeros(1, dtype=torch.int32, device=rows.device)
+    out = {}
+    for name, rl in (("selected_rows", rows), ("contiguous_rows", seq)):
+        ms = _kernel_ms(mla, lambda: mla.gather_probe(c.cache, rl, sink), n, c.flush)
+        m = statistics.mean(ms)
+        out[name] = {"kernel_us": round(1e3 * m, 3), "row_gbs": round(c.gathered / (m * 1e-3) / 1e9, 1),
+                     "frac_of_8tbs": round(c.gathered / (m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    out["decode_vs_selected_rows"] = round(out["selected_rows"]["kernel_us"] / (1e3 * decode_ms), 4)
+    return out
 
 
 def _two_level(torch, mla, c: Case, n: int):
@@ -564,6 +596,8 @@ def main(argv=None):
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "copy_peak_measured": copy_gbs,
                      "frac_of_copy_peak": round(achieved / copy_gbs, 4),
+                     "gather_ceiling_measured": r["gather_ceiling"]["selected_rows"]["row_gbs"],
+                     "frac_of_gather_ceiling": round(achieved / r["gather_ceiling"]["selected_rows"]["row_gbs"], 4),
                      "traffic": traffic["total"] if traffic else None,
                      "traffic_read_write": [traffic["read"], traffic["write"]] if traffic else None,
                      "kernel": "sparse_decode_kernel", "bytes_per_launch": c.gathered,

@@ -441,6 +441,23 @@ int mla_kv_unpack_blocks(const uint8_t* staging, int64_t n, const int32_t* block
 int mla_kernel_timing(int enable);
 int mla_last_kernel_ms(float* ms);
 
+/*
+ * mla_gather_probe -- read rows[0..n) of a cache (row_bytes bytes each, a
+ * multiple of 16) and nothing else: a measurement aid, not a step of the
+ * method.  Its duration is the time this GPU needs to fetch exactly that row
+ * list from HBM, the ceiling for any kernel that gathers those rows (the
+ * sparse decode reads 352-byte rows at 16-byte-aligned offsets, each
+ * touching three or four 128-byte lines).  cache (device, 16-byte aligned)
+ * holds cache_rows rows; rows (device, int32 [n]) are physical row numbers,
+ * and entries outside [0, cache_rows) are skipped.  sink (device, one
+ * uint32) is written only if the folded row words equal a fixed constant,
+ * which does not happen in practice; its contents carry no meaning.  Runs
+ * on `stream`; honours mla_kernel_timing.  Returns MLA_ERR_INVALID_ARG for
+ * NULL pointers (when n > 0), misalignment, bad sizes or n >= 2^31.
+ */
+int mla_gather_probe(const uint8_t* cache, int64_t cache_rows, int32_t row_bytes, const int32_t* rows,
+                     int64_t n, uint32_t* sink, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* mla_status_string(int status);
 

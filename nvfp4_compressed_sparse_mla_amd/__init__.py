@@ -412,6 +412,26 @@ def kv_unpack_blocks(staging, block_ids, pool_t, layout: str, pool_blocks: int, 
           "mla_kv_unpack_blocks")
 
 
+def gather_probe(cache: torch.Tensor, rows: torch.Tensor, sink: torch.Tensor = None) -> torch.Tensor:
+    """Read the given physical rows of a cache and nothing else (a measurement
+    aid: the HBM ceiling of a kernel that gathers those rows).  cache is
+    contiguous uint8 [rows, row_bytes]; rows is contiguous int32 [n].
+    Returns the one-word sink tensor (its contents carry no meaning)."""
+    dev = _device_of(cache, "cache")
+    if cache.dtype != torch.uint8 or cache.dim() != 2 or not cache.is_contiguous():
+        raise ValueError("cache must be contiguous uint8 [rows, row_bytes]")
+    if rows.dtype != torch.int32 or rows.dim() != 1 or not rows.is_contiguous():
+        raise ValueError("rows must be a contiguous int32 vector")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    _same_device(dev, rows=rows, sink=sink)
+    _exact(sink, "sink", (1,), torch.int32)
+    check(load().mla_gather_probe(cache.data_ptr(), cache.shape[0], cache.shape[1], rows.data_ptr(),
+                                  rows.numel(), sink.data_ptr(), _stream(cache)),
+          "mla_gather_probe")
+    return sink
+
+
 def kernel_timing(enable: bool) -> None:
     """Benchmark instrumentation: time every later library kernel with HIP events."""
     check(load().mla_kernel_timing(1 if enable else 0), "mla_kernel_timing")

@@ -51,6 +51,7 @@ SIGNATURES = {
     "mla_kv_pack_blocks": (c_int, [c_vp, c_i32, c_i64, c_i32, c_i32, c_i32, c_vp, c_i64, c_vp, c_vp]),
     "mla_kv_unpack_blocks": (c_int, [c_vp, c_i64, c_vp, c_vp, c_i32, c_i64, c_i32, c_i32, c_i32, c_vp]),
     "mla_kernel_timing": (c_int, [c_int]),
+    "mla_gather_probe": (c_int, [c_vp, c_i64, c_i32, c_vp, c_i64, c_vp, c_vp]),
     "mla_last_kernel_ms": (c_int, [ctypes.POINTER(ctypes.c_float)]),
     "mla_status_string": (ctypes.c_char_p, [c_int]),
 }

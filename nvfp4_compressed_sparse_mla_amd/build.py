@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla_nvfp4.so")
-SOURCES = ["abi.hip", "quantize.hip", "decode.hip", "staged.hip", "indexer.hip", "layout.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "decode.hip", "staged.hip", "indexer.hip", "layout.hip", "probe.hip"]
 HOST_SOURCES = ["pool.cpp"]     # host-only C++ (no device code)
 ARCH = "gfx950"
 

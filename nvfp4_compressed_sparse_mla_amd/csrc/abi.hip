@@ -511,4 +511,22 @@ int mla_nvfp4_gather_dequant_fp8(const uint8_t* cache, int64_t cache_rows, const
   return launched(mla::launch_gather_dequant_fp8(p, (hipStream_t)stream, ev), ev);
 }
 
+int mla_gather_probe(const uint8_t* cache, int64_t cache_rows, int32_t row_bytes, const int32_t* rows,
+                     int64_t n, uint32_t* sink, void* stream) {
+  if (cache_rows < 0 || n < 0 || row_bytes < 16 || row_bytes % 16) return MLA_ERR_INVALID_ARG;
+  if (n >= ((int64_t)1 << 31)) return MLA_ERR_INVALID_ARG;
+  if (n == 0) return MLA_OK;
+  if (!cache || !rows || !sink || !aligned16(cache)) return MLA_ERR_INVALID_ARG;
+  mla::GatherProbe g;
+  g.cache = cache;
+  g.cache_rows = cache_rows;
+  g.row_bytes = row_bytes;
+  g.pieces = row_bytes / 16;
+  g.rows = rows;
+  g.n = n;
+  g.sink = sink;
+  const mla::KernelEvents ev = timing_events();
+  return launched(mla::launch_gather_probe(g, (hipStream_t)stream, ev), ev);
+}
+
 }  // extern "C"

@@ -128,4 +128,16 @@ struct RegionCopy {
 hipError_t launch_region_copy(const RegionCopy& c, hipStream_t stream, const KernelEvents& ev);
 hipError_t launch_indexer(const IndexerParams& p, hipStream_t stream, const KernelEvents& ev);
 
+// Read-only gather of a row list (probe.hip; a measurement aid)
+struct GatherProbe {
+  const uint8_t* cache;
+  int64_t cache_rows;
+  int64_t row_bytes;        // a multiple of 16
+  int64_t pieces;           // row_bytes / 16
+  const int32_t* rows;      // [n] physical rows; entries outside [0, cache_rows) are skipped
+  int64_t n;
+  uint32_t* sink;           // one word, written only in a case that does not occur in practice
+};
+hipError_t launch_gather_probe(const GatherProbe& g, hipStream_t stream, const KernelEvents& ev);
+
 }  // namespace mla

@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 25, names
+    assert len(names) == 26, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -164,3 +164,17 @@ def test_indexer_rejects_bad_arguments(lib):
     need = lib.mla_indexer_workspace_size(2, 100)
     assert need == 2 * 4096 * 4 + 2 * 100 * 8
     assert lib.mla_indexer_workspace_size(3, 101) == ((3 * 4096 * 4 + 255) // 256) * 256 + 3 * 102 * 8
+
+
+def test_gather_probe_rejects_bad_arguments(lib):
+    """Host-side checks of mla_gather_probe, before any HIP call."""
+    fake = ctypes.c_void_p(1 << 20)
+
+    def call(rows_n=10, row_bytes=352, cache=fake, rows=fake, sink=fake, cache_rows=100):
+        return lib.mla_gather_probe(cache, cache_rows, row_bytes, rows, rows_n, sink, None)
+    assert call(rows_n=0) == OK
+    assert call(row_bytes=350) == INVALID and call(row_bytes=0) == INVALID
+    assert call(rows_n=-1) == INVALID and call(cache_rows=-1) == INVALID
+    assert call(rows=None) == INVALID and call(sink=None) == INVALID
+    assert call(cache=ctypes.c_void_p((1 << 20) + 8)) == INVALID     # cache not 16-byte aligned
+    assert call(rows_n=1 << 31) == INVALID
