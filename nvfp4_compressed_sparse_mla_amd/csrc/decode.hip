@@ -8,22 +8,35 @@
 // merged inside the same launch; the split count follows the token batch;
 // padded slots of the fixed-width list are masked and cost nothing.
 //
-// Workgroup = (token t, head group g of 32 heads, split s), 4 waves, one
-// workgroup per CU.  Each wave is an independent attention stream over its
-// own 16-row tiles (tiles w, w+4, w+8, ... of the split) with its own DMA
-// ring, its own FP16 V buffer and its own online-softmax state for all 32
-// heads and all 512 output columns, held in accumulation registers.  The
-// tile loop has no barrier: a wave overlaps its own DMA (the next two
-// tiles in flight) with its own MFMA and conversion work.  The four streams
-// merge once, through LDS, at the end; splits merge through the workspace
-// (the split that finishes last merges).
+// Workgroup = (token t, head group g of 32 heads, split s), 8 waves, one
+// workgroup per CU, two waves per SIMD.  The waves take two roles:
+//
+//   score waves (0..3)  each streams its own 16-row tiles (tiles w, w+4,
+//             w+8, ... of the split) through its own LDS-DMA ring, holds q
+//             of all 32 heads in registers, decodes each row once into the
+//             FP16 A operands of the score MFMAs, computes S^T[16 rows x 32
+//             heads] and its softmax P, and leaves P (FP16) and the decoded
+//             latent (the V of the tile, FP16) in LDS.
+//   value waves (4..7)  value wave j owns output columns [128j, +128) of
+//             all 32 heads (64 accumulation registers): per round it loads
+//             the four tiles' P and its columns of their V from LDS and adds
+//             P . V with 16 MFMAs (32x32x16).
+//
+// A round is one tile per score wave.  Two workgroup barriers per round
+// hand the LDS over: A(r) after the score waves wrote round r, B(r) after
+// the value waves have round r in registers.  Between B(r) and A(r+1) the
+// value waves' MFMAs for round r run beside the score waves' decode and
+// scores of round r+1 on the same SIMDs; between A(r) and B(r) the score
+// waves wait for their next tile's DMA and do its rope part.  No wave holds
+// both q and O, so each fits in 256 registers, and the output columns
+// never need merging across waves.
 //
 //   prologue  load the token's index list, translate it through the block
 //             table, drop masked / out-of-range slots and compact the valid
 //             rows into LDS (padded slots are never fetched; split
-//             boundaries balance valid rows).  Each wave loads q for all 32
-//             heads into registers in the score MFMA's B-operand layout.
-//   per tile  (16 rows, one wave)
+//             boundaries balance valid rows); stage q through LDS into the
+//             score waves' registers in the score MFMA's B-operand layout.
+//   per tile  (16 rows, one score wave)
 //     ring    global_load_lds_dwordx4 streams the tile's rows into one of
 //             the wave's LDS slots two tiles ahead; the wave waits for its
 //             oldest tile with an explicit vmcnt and reads the slot with
@@ -34,22 +47,23 @@
 //             +16) of the rope, i.e. the lane's 8 dimensions of each of the
 //             18 K-steps of a 16x16x32 MFMA A operand (q uses the same
 //             assignment).  The latent FP16 values also go to the V buffer.
-//     scores  S^T[16 rows x 32 heads]: 36 MFMAs (16x16x32, FP16 -> FP32).
-//     softmax base 2 against a lazily raised reference max: the first tile
-//             sets the reference, which then moves only when a score exceeds
-//             it by more than 15 (one ballot decides), so P = 2^(s - ref) <=
-//             2^15 stays inside FP16 (with its full 11-bit precision) and the
-//             common tile needs no cross-lane max and no O rescale.  Row sums
-//             accumulate per lane and are reduced once at the end.
-//     values  O[32 heads x 512 cols] += P . V: 16 MFMAs (32x32x16).  Each
-//             lane's P operand is 8 rows of one head: 4 of its own scores
-//             and 4 from lane ^ 16.  V's B operand comes from the V buffer
-//             through ds_read_b64_tr_b16.
-//   epilogue  the four streams are weighted by 2^(m_w - M) / L and summed
-//             through LDS; S == 1 stores the output, S > 1 stores the
-//             normalised partial (FP16) and its log2-sum-exp, and the split
-//             that finishes last for (t, g) merges all S partials.  Nothing
-//             waits on another workgroup, so no co-residency is needed.
+//     scores  36 MFMAs (16x16x32, FP16 -> FP32).
+//     softmax base 2 against a lazily raised reference max: a score wave's
+//             first tile sets its reference, which then moves only when a
+//             score exceeds it by more than 15 (one ballot decides), so
+//             P = 2^(s - ref) <= 2^15 stays inside FP16 with its full 11-bit
+//             precision.  Each tile's P goes to LDS with the reference it
+//             is relative to; row sums accumulate per lane.
+//     values  the value waves keep O relative to the largest reference seen
+//             per head: a tile whose reference is lower has its P scaled by
+//             2^(ref - M) (a power of two, exact in FP16 above its subnormal
+//             range); a higher reference first rescales O.
+//   epilogue  the value waves normalise their columns by the row sums of
+//             all score waves (weighted by 2^(m_w - M)); S == 1 stores the
+//             output, S > 1 stores the normalised partial (FP16) and its
+//             log2-sum-exp, and the split that finishes last for (t, g)
+//             merges all S partials.  Nothing waits on another workgroup, so
+//             no co-residency is needed.
 #include "mla_device.h"
 #include "mla_launch.h"
 
@@ -59,13 +73,17 @@ namespace mla {
 
 namespace {
 
-constexpr int kRowsT = 16;            // rows per tile (one wave)
+constexpr int kRowsT = 16;            // rows per tile (one score wave)
 constexpr int kHG = 32;               // heads per workgroup
-constexpr int kWaves = 4;
+constexpr int kSW = 4;                // score waves
+constexpr int kVW = 4;                // value waves
+constexpr int kWaves = kSW + kVW;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kVCols = kLatent / kVW; // output columns per value wave
 // FP16 elements per V-buffer row: a 1072-byte stride puts the 16 rows one
 // row-wise 16-byte write instruction touches in distinct banks
 constexpr int kVRow = kLatent + 24;
+constexpr int kTileV = kRowsT * kVRow;  // FP16 elements of one tile's V
 constexpr int kKSteps = 18;           // 576 key dimensions / 32
 constexpr float kLazy = 15.0f;        // P = 2^(s - reference) <= 2^15 stays inside FP16
 constexpr float kMargin = 5.0f;       // a new reference sits 2^5 above the max that set it
@@ -78,17 +96,20 @@ constexpr int row_bytes(int fmt) { return fmt == kFmtNvfp4 ? kRowBytes : kFp8Row
 // DMA instructions per tile: 4 pieces of 16 bytes of each of the 16 rows per instruction
 constexpr int dma_instr(int fmt) { return (row_bytes(fmt) / 16 + 3) / 4; }
 constexpr int slot_bytes(int fmt) { return dma_instr(fmt) * 1024; }
-// NVFP4: 3 slots (two tiles in flight while one is decoded); FP8 rows are
-// larger, so 2 slots and the refill is issued once a slot is in registers
+// Slots per score wave: a tile's bytes move to registers as the tile
+// starts, and its slot is refilled at once, so every slot holds a tile in
+// flight (NVFP4 3, FP8 rows are larger: 2)
 constexpr int ring_depth(int fmt) { return fmt == kFmtNvfp4 ? 3 : 2; }
-constexpr int kWaveRing = 18432;      // bytes of ring per wave (both formats)
+constexpr int kWaveRing = 18432;      // bytes of ring per score wave (both formats)
 static_assert(ring_depth(kFmtNvfp4) * slot_bytes(kFmtNvfp4) <= kWaveRing, "NVFP4 ring");
 static_assert(ring_depth(kFmtFp8) * slot_bytes(kFmtFp8) <= kWaveRing, "FP8 ring");
-// FP16 elements of V buffer per wave; the stream merge's exchange regions
-// (36,352 bytes per stream) reuse two waves' buffers, hence the padding
-constexpr int kWaveV = kRowsT * kVRow + 512;
-// q of the workgroup's 32 heads is staged through the V buffers before the loop
-static_assert(kHG * kQK * 2 <= kWaves * kWaveV * 2, "q staging area");
+// q of the workgroup's 32 heads is staged through the V buffer before the loop
+static_assert(kHG * kQK * 2 <= kSW * kTileV * 2, "q staging area");
+// Output exchange of a value wave (epilogue): 16 blocks (4 column blocks x 4
+// head quads) of 64 16-byte slots, padded so that both the writers' 64
+// lanes and the readers' 8 consecutive slots are free of bank conflicts
+constexpr uint32_t kXBlock = 1136, kXRegion = 16 * kXBlock;
+static_assert(2 * kXRegion <= kSW * kWaveRing && 2 * kXRegion <= kSW * kTileV * 2, "exchange regions");
 
 __device__ __forceinline__ uint32_t lds_off(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
@@ -125,14 +146,16 @@ __device__ __forceinline__ u32x4 ring_b128(uint32_t a) {
   MLA_DEVICE_ASM("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(kOff));
   return v;
 }
+template <int kOff = 0>
 __device__ __forceinline__ u32x2 ring_b64(uint32_t a) {
   u32x2 v;
-  MLA_DEVICE_ASM("ds_read_b64 %0, %1" : "=v"(v) : "v"(a));
+  MLA_DEVICE_ASM("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(kOff));
   return v;
 }
+template <int kOff = 0>
 __device__ __forceinline__ uint32_t lds_b32(uint32_t a) {
   uint32_t v;
-  MLA_DEVICE_ASM("ds_read_b32 %0, %1" : "=v"(v) : "v"(a));
+  MLA_DEVICE_ASM("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(kOff));
   return v;
 }
 
@@ -176,81 +199,28 @@ struct RingOff {
   }
 };
 
-// The row bytes are read in two parts so that the second half of the
-// latent (K-steps 8..15) occupies registers only from when it is decoded:
-// part A = latent K-steps 0..7, scales and rope; part B = latent K-steps
-// 8..15.  Each part waits for its own reads (and part A for `extra`, an LDS
-// read issued just before it).
+// All of the lane's row bytes of one slot, and `extra` (an LDS read issued
+// just before), valid on return.
 template <int kFmt>
-__device__ __forceinline__ void ring_read_a(Raw<kFmt>& r, uint32_t slot, const RingOff<kFmt>& o,
-                                            uint32_t& extra) {
+__device__ __forceinline__ void ring_read(Raw<kFmt>& r, uint32_t slot, const RingOff<kFmt>& o, uint32_t& extra) {
   if constexpr (kFmt == kFmtNvfp4) {
     r.l[0] = ring_b128<0>(slot + o.lat);
     r.l[1] = ring_b128<256>(slot + o.lat);
+    r.l[2] = ring_b128<512>(slot + o.lat);
+    r.l[3] = ring_b128<768>(slot + o.lat);
     r.sc = ring_b64(slot + o.sc);
     r.rp = ring_b128(slot + o.rope);
-    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(r.l[0]), "+v"(r.l[1]), "+v"(r.sc), "+v"(r.rp), "+v"(extra));
+    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)"
+                   : "+v"(r.l[0]), "+v"(r.l[1]), "+v"(r.l[2]), "+v"(r.l[3]), "+v"(r.sc), "+v"(r.rp), "+v"(extra));
   } else {
-    r.l[0] = ring_b128<0>(slot + o.lat);
-    r.l[1] = ring_b128<256>(slot + o.lat);
-    r.l[2] = ring_b128<512>(slot + o.lat);
-    r.l[3] = ring_b128<768>(slot + o.lat);
+    static_for<0, 8>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      r.l[i] = ring_b128<256 * i>(slot + o.lat);
+    });
     r.rp = ring_b128(slot + o.rope);
     MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)"
-                   : "+v"(r.l[0]), "+v"(r.l[1]), "+v"(r.l[2]), "+v"(r.l[3]), "+v"(r.rp), "+v"(extra));
-  }
-}
-
-// part B issued without a wait (the caller's next lgkmcnt(0) wait covers it
-// and names these registers).  FP8 rows carry twice the latent bytes: their
-// part B is read in two halves, the second (K-steps 12..15) one value group
-// later (ring_issue_b2), so that fewer row registers are live at once.
-template <int kFmt>
-__device__ __forceinline__ void ring_issue_b(Raw<kFmt>& r, uint32_t slot, const RingOff<kFmt>& o) {
-  if constexpr (kFmt == kFmtNvfp4) {
-    r.l[2] = ring_b128<512>(slot + o.lat);
-    r.l[3] = ring_b128<768>(slot + o.lat);
-  } else {
-    r.l[4] = ring_b128<1024>(slot + o.lat);
-    r.l[5] = ring_b128<1280>(slot + o.lat);
-  }
-}
-template <int kFmt>
-__device__ __forceinline__ void ring_issue_b2(Raw<kFmt>& r, uint32_t slot, const RingOff<kFmt>& o) {
-  if constexpr (kFmt == kFmtFp8) {
-    r.l[6] = ring_b128<1536>(slot + o.lat);
-    r.l[7] = ring_b128<1792>(slot + o.lat);
-  }
-}
-template <int kFmt>
-__device__ __forceinline__ void lgkm_wait_b(u32x4 (&b)[4], Raw<kFmt>& r) {
-  if constexpr (kFmt == kFmtNvfp4)
-    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(r.l[2]), "+v"(r.l[3]));
-  else
-    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(r.l[4]), "+v"(r.l[5]));
-}
-// value group 2's wait: FP8 rows' second half of part B (issued during group
-// 1, ahead of that group's four V-buffer writes) is complete as well
-template <int kFmt>
-__device__ __forceinline__ void lgkm_wait4_b2(u32x4 (&b)[4], Raw<kFmt>& r) {
-  if constexpr (kFmt == kFmtNvfp4)
-    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
-  else
-    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(r.l[6]), "+v"(r.l[7]));
-}
-
-template <int kFmt>
-__device__ __forceinline__ void ring_read_b(Raw<kFmt>& r, uint32_t slot, const RingOff<kFmt>& o) {
-  if constexpr (kFmt == kFmtNvfp4) {
-    r.l[2] = ring_b128<512>(slot + o.lat);
-    r.l[3] = ring_b128<768>(slot + o.lat);
-    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(r.l[2]), "+v"(r.l[3]));
-  } else {
-    r.l[4] = ring_b128<1024>(slot + o.lat);
-    r.l[5] = ring_b128<1280>(slot + o.lat);
-    r.l[6] = ring_b128<1536>(slot + o.lat);
-    r.l[7] = ring_b128<1792>(slot + o.lat);
-    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(r.l[4]), "+v"(r.l[5]), "+v"(r.l[6]), "+v"(r.l[7]));
+                   : "+v"(r.l[0]), "+v"(r.l[1]), "+v"(r.l[2]), "+v"(r.l[3]), "+v"(r.l[4]), "+v"(r.l[5]),
+                     "+v"(r.l[6]), "+v"(r.l[7]), "+v"(r.rp), "+v"(extra));
   }
 }
 
@@ -274,46 +244,25 @@ __device__ __forceinline__ half8_t kstep8(const Raw<kFmt>& r, int ks) {
   }
 }
 
-// A latent K-step's A operand decoded in two parts so that the conversion
-// work can be placed between MFMAs: part 1 = the conversions and half of
-// the scale multiplies, part 2 = the rest.  `sh` holds the lane's 8 group
-// scales as FP16 (group g = half g & 1 of sh[g >> 1]).
-struct KDec {
-  half2_t c[4];
-};
+// A latent K-step's A operand with the group scales already in FP16: `sh`
+// holds the lane's 8 group scales (group g = half g & 1 of sh[g >> 1]).
 template <int kFmt>
-__device__ __forceinline__ void kdec_part1(KDec& d, const Raw<kFmt>& r, const half2_t (&sh)[4], int ks) {
+__device__ __forceinline__ half8_t latent8(const Raw<kFmt>& r, const half2_t (&sh)[4], int ks) {
   if constexpr (kFmt == kFmtNvfp4) {
     const uint32_t w = r.l[ks >> 2][ks & 3];
     const half2_t s2 = sh[ks >> 2];
     const half_t sv = ((ks >> 1) & 1) ? s2.y : s2.x;
     const half2_t s = {sv, sv};
-    d.c[0] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0));
-    d.c[1] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
-    d.c[2] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
-    d.c[3] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
-    d.c[0] *= s;
-    d.c[1] *= s;
+    half2_t c[4];
+    static_for<0, 4>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      c[i] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, i)) * s;
+    });
+    return (half8_t){c[0].x, c[0].y, c[1].x, c[1].y, c[2].x, c[2].y, c[3].x, c[3].y};
   } else {
-    const uint32_t w = r.l[ks >> 1][2 * (ks & 1)];
-    d.c[0] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
-    d.c[1] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+    (void)sh;
+    return kstep8<kFmt>(r, ks);
   }
-}
-template <int kFmt>
-__device__ __forceinline__ half8_t kdec_part2(KDec& d, const Raw<kFmt>& r, const half2_t (&sh)[4], int ks) {
-  if constexpr (kFmt == kFmtNvfp4) {
-    const half2_t s2 = sh[ks >> 2];
-    const half_t sv = ((ks >> 1) & 1) ? s2.y : s2.x;
-    const half2_t s = {sv, sv};
-    d.c[2] *= s;
-    d.c[3] *= s;
-  } else {
-    const uint32_t w = r.l[ks >> 1][2 * (ks & 1) + 1];
-    d.c[2] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
-    d.c[3] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
-  }
-  return (half8_t){d.c[0].x, d.c[0].y, d.c[1].x, d.c[1].y, d.c[2].x, d.c[2].y, d.c[3].x, d.c[3].y};
 }
 // the lane's 8 NVFP4 group scales as FP16 pairs
 __device__ __forceinline__ void group_scales(half2_t (&sh)[4], const u32x2& sc) {
@@ -322,7 +271,6 @@ __device__ __forceinline__ void group_scales(half2_t (&sh)[4], const u32x2& sc) 
   sh[2] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[1], 1.0f, false));
   sh[3] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[1], 1.0f, true));
 }
-
 // Eight q elements (fp16 or bf16 bits) as the FP16 score operand: fp16 is
 // taken as is, bf16 is rounded to FP16.
 template <bool kBf16>
@@ -367,42 +315,28 @@ __device__ __forceinline__ void store8_agent(half_t* dst, const float (&v)[8]) {
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
-__device__ __forceinline__ uint32_t shfl_xor_u(uint32_t v, int m) {
-  return (uint32_t)__shfl_xor((int)v, m, 64);
-}
 
-// B operands of the 4 value MFMAs of column group q (32-column blocks q,
-// q+4, q+8, q+12) from the V buffer: ds_read_b64_tr_b16 gives each lane 4
-// consecutive rows of one column; two reads (rows 0-3 and 4-7 of the lane's
-// 8) make one operand.  In assembly so that the compiler does not make them
-// wait for the ring's DMA; the memory clobber keeps the V-buffer writes that
-// follow in program order from moving above them.
-template <int kQ>
-__device__ __forceinline__ void read_v4_group(u32x4 (&b)[4], uint32_t base) {
+// V operands of one tile for a value wave: the B operands of its 4 column
+// blocks (32x32x16 MFMA: 8 rows of one column per lane).  ds_read_b64_tr_b16
+// gives each lane 4 consecutive rows of one column; two reads (rows 0-3 and
+// 4-7 of the lane's 8) make one operand.  `base` is the lane's address for
+// column block 0 of tile 0; kTile selects the tile.
+template <int kTile>
+__device__ __forceinline__ void read_v_tile(u32x4 (&b)[4], uint32_t base) {
   static_for<0, 4>([&](auto E) {
     constexpr int e = decltype(E)::value;
-    constexpr int off = 64 * (kQ + 4 * e);
+    constexpr int off = kTile * kTileV * 2 + 64 * e;
     u32x2 lo, hi;
-    MLA_DEVICE_ASM("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(base), "i"(off) : "memory");
-    MLA_DEVICE_ASM("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(base), "i"(off + 8 * kVRow) : "memory");
+    MLA_DEVICE_ASM("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(base), "i"(off));
+    MLA_DEVICE_ASM("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(base), "i"(off + 8 * kVRow));
     b[e] = (u32x4){lo.x, lo.y, hi.x, hi.y};
   });
 }
 
-__device__ __forceinline__ void lgkm_wait(u32x4 (&b)[4]) {
-  MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
-}
-// the same, leaving the wave's last four LDS operations (V-buffer writes
-// issued after these reads) in flight: a wave's LDS operations complete in
-// issue order
-__device__ __forceinline__ void lgkm_wait4(u32x4 (&b)[4]) {
-  MLA_DEVICE_ASM("s_waitcnt lgkmcnt(4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
-}
-
 // Workgroup barrier for LDS data only: waits for this wave's LDS operations,
 // not for its outstanding global loads (__syncthreads() would also wait for
-// those, e.g. the q loads still in flight during the prologue).  The memory
-// clobber keeps the compiler from moving memory accesses across it.
+// those, e.g. the tiles' DMA in flight).  The memory clobber keeps the
+// compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() {
   MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -415,18 +349,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
-// x * a for an accumulator element that lives in an AGPR.  Written in C++
-// the multiply makes the compiler move all 256 accumulators through VGPRs
-// (and spill); in assembly the element is read, scaled and written back in
-// place.
-__device__ __forceinline__ float scale_acc(float x, float a) {
-  float tmp;
-  MLA_DEVICE_ASM("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                 : "+a"(x), "=&v"(tmp) : "v"(a));
-  (void)tmp;
-  return x;
-}
-
 // max of four MFMA results (v_max3; the compiler's fmaxf would first
 // canonicalise each input with another v_max)
 __device__ __forceinline__ float max4(float a, float b, float c, float d) {
@@ -436,9 +358,8 @@ __device__ __forceinline__ float max4(float a, float b, float c, float d) {
 }
 
 // The two score MFMAs of a K-step (16x16x32, FP16 -> FP32), in assembly so
-// that their accumulators are VGPRs: the compiler gives every MFMA of the
-// kernel an AGPR accumulator, and the 256 AGPRs already hold O.  Hazards are
-// handled here: two wait states after the VALU write of the A operand
+// that the compiler keeps their accumulators in VGPRs next to q.  Hazards
+// are handled here: two wait states after the VALU write of the A operand
 // (the first instruction), accumulation chains back to back (the hardware
 // forwards a same-size accumulator), the first K-step of a tile starts from
 // the constant 0, and score_mfma_drain() waits out the MFMA latency before
@@ -452,8 +373,8 @@ __device__ __forceinline__ void score_mfma2(float4_t (&acc)[2], const half8_t& a
     MLA_DEVICE_ASM("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %2, %3, %0\n\tv_mfma_f32_16x16x32_f16 %1, %2, %4, %1"
                    : "+v"(acc[0]), "+v"(acc[1]) : "v"(a), "v"(b0), "v"(b1));
 }
-// one score MFMA of the software-pipelined loop (its A operand was written
-// at least a slot earlier, so no wait states are needed)
+// one score MFMA of the pipelined latent K-steps (its A operand was written
+// at least two instructions earlier, so no wait states are needed)
 __device__ __forceinline__ void score_mfma1(float4_t& acc, const half8_t& a, const half8_t& b) {
   MLA_DEVICE_ASM("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
@@ -489,16 +410,18 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   constexpr int kSlot = slot_bytes(kFmt);
   constexpr int kDepth = ring_depth(kFmt);
 
-  // The DMA target and the V buffers are separate arrays so that the
-  // compiler can tell V-buffer accesses from DMA writes.  After the tile
-  // loop both hold the streams' weighted outputs for the merge.
-  __shared__ __align__(16) uint8_t ring_all[kWaves * kWaveRing];
-  __shared__ __align__(16) half_t vbuf_all[kWaves * kWaveV];
+  // The DMA target, the V buffer and the P buffer are separate arrays so
+  // that the compiler can tell their accesses from the DMA's writes.  After
+  // the loop the ring and V areas hold the value waves' output exchange.
+  __shared__ __align__(16) uint8_t ring_all[kSW * kWaveRing];
+  __shared__ __align__(16) half_t vbuf_all[kSW * kTileV];
+  __shared__ __align__(16) half_t pbuf[kSW][kHG][kRowsT];   // P of a round's tiles, [head][row]
+  __shared__ __align__(16) float ref_s[kSW][kHG];           // the reference each tile's P is relative to
   __shared__ int phys[kMaxTopk];
-  __shared__ float wm_s[kWaves][kHG];     // per-stream reference max (base 2)
-  __shared__ float wl_s[kWaves][kHG];     // per-stream row sums
-  __shared__ float alpha_s[kWaves][kHG];  // O rescale factors, then stream weights
-  __shared__ int cnt_s[8][kWaves];
+  __shared__ __align__(16) float wm_s[kSW][kHG];            // per score wave: final reference (base 2)
+  __shared__ __align__(16) float wl_s[kSW][kHG];            // per score wave: row sums
+  __shared__ __align__(16) float fac_s[kVW][kHG];           // per value wave: per-head factors
+  __shared__ int cnt_s[4][kWaves];
   __shared__ int last_s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -520,8 +443,6 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   const int g = (int)(tg32 - t32 * (uint32_t)G);
   const int64_t tg = tg32, t = t32;
   const int r16 = lane & 15, kg = lane >> 4;
-  uint8_t* ring = ring_all + wave * kWaveRing;
-  half_t* vbuf = vbuf_all + wave * kWaveV;
 
   // ------------------------------------------------ compact the valid rows
   // All index loads are issued before any is used, then all block-table
@@ -529,83 +450,84 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   // or of masked entries are clamped to valid ones and the result dropped).
   // The index loads head the longest dependent chain (index -> block table
   // -> row DMA), so they are issued first; q's loads follow while they are
-  // in flight, then the block-table loads (vector loads complete in issue
-  // order: waiting for the block-table entries also waits for q, which by
-  // then has had a round trip's head start).
-  int v8[8];
+  // in flight, then the block-table loads.
+  int v4[4];
   {
     const int32_t* ip = p.idx + t * p.idx_st;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int slot = i * kThreads + tid;
-      v8[i] = ip[slot < p.topk ? slot : p.topk - 1];
+    for (int i = 0; i < 4; ++i) {
+      const int sl = i * kThreads + tid;
+      v4[i] = ip[sl < p.topk ? sl : p.topk - 1];
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i * kThreads + tid >= p.topk) v8[i] = -1;
+    for (int i = 0; i < 4; ++i)
+      if (i * kThreads + tid >= p.topk) v4[i] = -1;
   }
   // ---------------------------------------------------------------- q
-  // q of the workgroup's 32 heads is loaded once, 9 coalesced 16-byte chunks
-  // per thread (chunk c: head c / 72, dimensions 8 (c % 72) + [0,8); heads
-  // past H repeat the last one), and later staged through the still idle V
-  // buffer, from where each wave reads the B operands of its score MFMAs.
-  constexpr int kQChunks = kHG * (kQK / 8) / kThreads;   // 9
+  // q of the workgroup's 32 heads: 2304 coalesced 16-byte chunks (chunk c:
+  // head c / 72, dimensions 8 (c % 72) + [0,8); heads past H repeat the last
+  // one), 4 or 5 per thread, later staged through the still idle V buffer,
+  // from where each score wave reads the B operands of its score MFMAs.
+  constexpr int kQChunkAll = kHG * (kQK / 8);               // 2304
+  constexpr int kQChunks = (kQChunkAll + kThreads - 1) / kThreads;   // 5
   u32x4 qstage[kQChunks];     // raw fp16 / bf16 bits
-  half8_t qreg[2][kKSteps];   // filled once the rows' DMA is issued (see below)
   {
     const uint16_t* qt = reinterpret_cast<const uint16_t*>(p.q) + t * p.q_st;
 #pragma unroll
     for (int m = 0; m < kQChunks; ++m) {
-      const int c = tid + kThreads * m, h = c / (kQK / 8), dc = c - h * (kQK / 8);
-      const int head = min(g * kHG + h, p.H - 1);
-      qstage[m] = *reinterpret_cast<const u32x4*>(qt + (int64_t)head * p.q_sh + 8 * dc);
+      const int c = tid + kThreads * m;
+      if (c < kQChunkAll) {
+        const int h = c / (kQK / 8), dc = c - h * (kQK / 8);
+        const int head = min(g * kHG + h, p.H - 1);
+        qstage[m] = *reinterpret_cast<const u32x4*>(qt + (int64_t)head * p.q_sh + 8 * dc);
+      }
     }
   }
 
-  int b8[8], pb8[8];
+  int b4[4], pb4[4];
   bool seq_ok = true;
   if (p.bt) {
     const int64_t seq = p.tok_seq[t];
     seq_ok = seq >= 0 && seq < p.bt_rows;
     const int32_t* btr = p.bt + (seq_ok ? seq : 0) * p.bt_st;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       // (a power-of-two block size, the usual case, divides by a shift)
-      const int v = v8[i] >= 0 ? v8[i] : 0;
-      b8[i] = p.bs_log2 >= 0 ? v >> p.bs_log2 : v / p.bs;
-      pb8[i] = btr[b8[i] < p.bt_cols ? b8[i] : p.bt_cols - 1];
+      const int v = v4[i] >= 0 ? v4[i] : 0;
+      b4[i] = p.bs_log2 >= 0 ? v >> p.bs_log2 : v / p.bs;
+      pb4[i] = btr[b4[i] < p.bt_cols ? b4[i] : p.bt_cols - 1];
     }
   }
 
-  int rows8[8], pre8[8];
+  int rows4[4], pre4[4];
   {
     if (p.bt) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 4; ++i) {
         int r = -1;
-        if (seq_ok && v8[i] >= 0 && b8[i] < p.bt_cols && pb8[i] >= 0) {
-          const int64_t pr = (int64_t)pb8[i] * p.bs + (v8[i] - b8[i] * p.bs);
+        if (seq_ok && v4[i] >= 0 && b4[i] < p.bt_cols && pb4[i] >= 0) {
+          const int64_t pr = (int64_t)pb4[i] * p.bs + (v4[i] - b4[i] * p.bs);
           r = pr < p.cache_rows ? (int)pr : -1;
         }
-        rows8[i] = r;
+        rows4[i] = r;
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) rows8[i] = (v8[i] >= 0 && v8[i] < p.cache_rows) ? v8[i] : -1;
+      for (int i = 0; i < 4; ++i) rows4[i] = (v4[i] >= 0 && v4[i] < p.cache_rows) ? v4[i] : -1;
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint64_t m = __ballot(rows8[i] >= 0);
-      pre8[i] = __popcll(m & ((1ull << lane) - 1ull));
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t m = __ballot(rows4[i] >= 0);
+      pre4[i] = __popcll(m & ((1ull << lane) - 1ull));
       if (lane == 0) cnt_s[i][wave] = __popcll(m);
     }
   }
   lds_barrier();
   int total = 0;
   {
-    int base[8];
+    int base[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       base[i] = total;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
@@ -614,8 +536,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
       }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (rows8[i] >= 0) phys[base[i] + pre8[i]] = rows8[i];
+    for (int i = 0; i < 4; ++i)
+      if (rows4[i] >= 0) phys[base[i] + pre4[i]] = rows4[i];
   }
   lds_barrier();
 
@@ -623,23 +545,23 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   const int r0 = S == 1 ? 0 : (int)((uint32_t)(total * s) / (uint32_t)S);
   const int n = (S == 1 ? total : (int)((uint32_t)(total * (s + 1)) / (uint32_t)S)) - r0;
   const int ntiles = (n + kRowsT - 1) / kRowsT;
-  const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+  const int rounds = (ntiles + kSW - 1) / kSW;
 
-  // ---------------------------------------------------------------- stream state
-  float16_t acc_o[16];                    // O[32 heads x 32 cols] of column block i, C layout
-  float mref[2];                          // reference of head hb*16 + r16 (base 2)
-  float lsum[2];                          // this lane's share of that head's row sum
+  // ---------------------------------------------------------------- score-wave state
+  const int sw = wave;        // (score waves only)
+  const int my_tiles = wave < kSW && ntiles > sw ? (ntiles - sw + kSW - 1) / kSW : 0;
+  uint8_t* const ring = ring_all + (wave < kSW ? wave : 0) * kWaveRing;
 
-  // DMA of one tile into ring slot `slot` (row-interleaved layout above):
+  // DMA of one tile into ring slot `sl` (row-interleaved layout above):
   // lane l moves pieces 4j + (l >> 4), j = 0 .. kInstr - 1, of the tile row
   // l & 15 (= r16), whose cache row is `row`, so every source address is the
   // lane's row address plus an immediate.  Rows past the split repeat the
   // split's last row.  NVFP4 rows have 22 pieces: in the last instruction
   // lanes 32..63 (pieces 22, 23) repeat pieces 20 and 21 of their row into
   // positions that are never read.
-  auto issue_from = [&](const uint8_t* row_base, int slot) {
+  auto issue_from = [&](const uint8_t* row_base, int sl) {
     const uint8_t* const a = row_base + 16 * kg;
-    uint8_t* const dst = ring + slot * kSlot;
+    uint8_t* const dst = ring + sl * kSlot;
     // instruction j: source a + 64j, LDS dst + 1024j (the immediate 64j
     // applies to both)
     auto one = [&](auto J) {
@@ -649,430 +571,341 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     };
     static_for<0, kInstr>(one);
   };
-  auto issue = [&](uint32_t row, int slot) { issue_from(p.cache + (uint64_t)row * kRB, slot); };
-  // cache row of this lane's DMA row in the wave's k-th tile
-  auto tile_row_addr = [&](int k) -> uint32_t {
-    int i = (wave + kWaves * k) * kRowsT + r16;
-    i = i < n ? i : n - 1;
-    return lds_off(&phys[r0 + i]);
-  };
-  const RingOff<kFmt> ro(r16, kg);
-
-  // V-buffer addresses: this lane's ds_read_b64_tr_b16 base for column
-  // block 0 (block b is 64 bytes further) and its row for the V writes.
-  const int vgrp = lane >> 4, vsl = lane & 15;
-  const uint32_t vb = lds_off(vbuf + (8 * (vgrp >> 1) + (vsl >> 2)) * kVRow + 16 * (vgrp & 1) + 4 * (vsl & 3));
-  half_t* const vrow = vbuf + r16 * kVRow + 128 * kg;
-
-  // Per tile (16 rows, this wave): wait for the tile's DMA, read the row
-  // bytes from the ring, decode them (A operands of the score MFMAs, and the
-  // latent also into the V buffer), scores, softmax, then the values.  The
-  // next two tiles' DMA is in flight throughout.
-  //
-  // Software pipeline: the value MFMAs of tile k-1 run interleaved with the
-  // decode and score MFMAs of tile k, so the conversion work issues while
-  // the matrix core is busy.  Both use the one V buffer: value group j
-  // (column blocks j, j+4, j+8, j+12) reads tile k-1's V before latent
-  // K-steps 4j..4j+3 of tile k overwrite exactly those columns, and a wave's
-  // LDS operations execute in issue order.
-  //
-  // Softmax reference (base 2): the first tile sets it to its max + kMargin
-  // (P <= 2^-kMargin there); afterwards it moves only when a score exceeds
-  // it by more than kLazy (P would leave FP16), one ballot deciding; then O
-  // and the row sums are rescaled in place.
-  const float sm = p.sm_log2;
-  const bool two_level = kFmt == kFmtNvfp4 && p.lat_scale != 1.0f;
-#pragma unroll
-  for (int nb = 0; nb < 16; ++nb)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc_o[nb][j] = 0.0f;
-  mref[0] = mref[1] = kNegInf;
-  lsum[0] = lsum[1] = 0.0f;
-
-  Raw<kFmt> raw;
-  float4_t sacc[2];
-  uint32_t next_row = 0;
-  // wait for tile k's DMA and read part A of its rows (and the cache row of
-  // this lane's DMA row two tiles ahead)
-  auto tile_start = [&](int k) -> uint32_t {
-    if (k + 1 < my_tiles) wait_vmcnt<kInstr>();
-    else wait_vmcnt<0>();
-    const uint32_t slot = lds_off(ring + (k % kDepth) * kSlot);
-    next_row = lds_b32(tile_row_addr(k + 2));
-    ring_read_a<kFmt>(raw, slot, ro, next_row);
-    return slot;
-  };
-  // one K-step of tile k's scores (latent K-steps also go to the V buffer)
-  auto score_step = [&](int k, int ks, uint32_t slot) {
-    if (ks == 8) {
-      ring_read_b<kFmt>(raw, slot, ro);
-      // the slot of tile k + 2 held tile k - 1 (3 slots) or tile k (2
-      // slots), both now in registers
-      if (k + 2 < my_tiles) issue(next_row, (k + 2) % kDepth);
-    }
-    const half8_t kop = kstep8<kFmt>(raw, ks);
-    if (ks < 16) *reinterpret_cast<half8_t*>(vrow + 8 * ks) = kop;
-    score_mfma2(sacc, kop, qreg[0][ks], qreg[1][ks], ks == 16);
-  };
-  // value group j of the tile whose P is `pa` (its V is in the V buffer)
-  auto value_group = [&](const u32x4 (&bv)[4], const half8_t& pa, auto J) {
-    constexpr int j = decltype(J)::value;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      acc_o[j + 4 * e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-          pa, __builtin_bit_cast(half8_t, bv[e]), acc_o[j + 4 * e], 0, 0, 0);
-  };
-  // Softmax of tile k (scores in sacc), first part: the reference.  Returns
-  // whether O must be rescaled by alpha_s before tile k's values are added.
-  // The lane holds rows 4kg + j (j = 0..3) of head hb*16 + r16; sm >= 0,
-  // so the scaled max is the max scaled.  Only the split's last tile can
-  // hold rows past its end; they get P = 0.
-  auto softmax_ref = [&](int k) -> bool {
-    const int row0 = (wave + kWaves * k) * kRowsT + 4 * kg;
-    const bool ragged = (wave + kWaves * k + 1) * kRowsT > n;
-    score_mfma_drain(sacc);
-    float tmax[2];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float m = max4(sacc[hb][0], sacc[hb][1], sacc[hb][2], sacc[hb][3]);
-      if (ragged) {
-        m = kNegInf;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (row0 + j < n) m = __builtin_fmaxf(m, sacc[hb][j]);
-      }
-      // (-inf * 0 is NaN; the max with -inf maps it back to -inf)
-      tmax[hb] = __builtin_fmaxf(m * sm, kNegInf);
-    }
-    const bool first = k == 0;
-    const bool raise = tmax[0] > mref[0] + kLazy || tmax[1] > mref[1] + kLazy;
-    if (first || __ballot(raise) != 0) {
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        float m = tmax[hb];
-        m = __builtin_fmaxf(m, shfl_xor_f(m, 16));
-        m = __builtin_fmaxf(m, shfl_xor_f(m, 32));
-        const float mnew = __builtin_fmaxf(mref[hb], m) + kMargin;
-        const float al = first ? 0.0f : __builtin_amdgcn_exp2f(mref[hb] - mnew);
-        lsum[hb] *= al;
-        mref[hb] = mnew;
-        if (kg == 0) alpha_s[wave][hb * 16 + r16] = al;
-      }
-      return !first;
-    }
-    return false;
-  };
-  // second part: P of tile k against the reference, as the value MFMA's A
-  // operand
-  auto softmax_p = [&](int k) -> half8_t {
-    const int row0 = (wave + kWaves * k) * kRowsT + 4 * kg;
-    const bool ragged = (wave + kWaves * k + 1) * kRowsT > n;
-    float pv[2][4];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const float nm = -mref[hb];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pv[hb][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[hb][j], sm, nm));
-      if (ragged) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (row0 + j >= n) pv[hb][j] = 0.0f;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) lsum[hb] += pv[hb][j];
-    }
-    // A operand of the value MFMA: lane L = head block (L >> 4) & 1, head
-    // L & 15, rows 8(L >> 5) + [0,8).  d[hb][x] = P of head hb*16 + r16,
-    // rows 4kg + 2x, +1 (FP16 pair).  permlane16_swap exchanges the odd
-    // 16-lane rows of its first operand with the even rows of its second;
-    // afterwards d[0] holds rows 8(kg >> 1) + [0,4) and d[1] rows + [4,8) of
-    // head block kg & 1 (the lane ^ 16 neighbour holds the other 4 rows).
-    uint32_t d[2][2];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-        d[hb][x] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
-                                                    (float2_t){pv[hb][2 * x], pv[hb][2 * x + 1]}, half2_t));
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const auto sw = __builtin_amdgcn_permlane16_swap(d[0][x], d[1][x], false, false);
-      d[0][x] = sw[0];
-      d[1][x] = sw[1];
-    }
-    return __builtin_bit_cast(half8_t, (u32x4){d[0][0], d[0][1], d[1][0], d[1][1]});
+  auto issue = [&](uint32_t row, int sl) { issue_from(p.cache + (uint64_t)row * kRB, sl); };
+  // LDS address of the cache row of this lane's DMA row in the wave's i-th tile
+  auto tile_row_addr = [&](int i) -> uint32_t {
+    int e = (sw + kSW * i) * kRowsT + r16;
+    e = e < n ? e : n - 1;
+    return lds_off(&phys[r0 + e]);
   };
 
-  // The first two tiles' DMA.  Missing tiles re-read a valid row (or q,
-  // with an empty cache) into slots that are never read.
-  // q's loads (issued before the compaction) are complete by now; waiting
-  // for them here, where nothing else is in flight, keeps the compiler from
-  // waiting for the tiles' DMA before q is staged
+  // The first kDepth tiles' DMA (score waves).  Missing tiles re-read a
+  // valid row (or q, with an empty cache) into slots that are never read.  q's
+  // loads (issued before the compaction) are complete by now; waiting for
+  // them here, where nothing else is in flight, keeps the compiler from
+  // waiting for the tiles' DMA before q is staged.
   wait_vmcnt<0>();
-  {
+  if (wave < kSW) {
     const uint8_t* const spare = p.cache_rows > 0 ? p.cache : static_cast<const uint8_t*>(p.q);
-    const uint8_t* b0 = spare;
-    const uint8_t* b1 = spare;
-    if (my_tiles > 0) b0 = p.cache + (uint64_t)(uint32_t)phys[r0 + min(wave * kRowsT + r16, n - 1)] * kRB;
-    if (my_tiles > 1) b1 = p.cache + (uint64_t)(uint32_t)phys[r0 + min((wave + kWaves) * kRowsT + r16, n - 1)] * kRB;
-    issue_from(b0, 0);
-    issue_from(b1, 1 % kDepth);
+    static_for<0, kDepth>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      const uint8_t* b = spare;
+      if (my_tiles > i) b = p.cache + (uint64_t)(uint32_t)phys[r0 + min((sw + kSW * i) * kRowsT + r16, n - 1)] * kRB;
+      issue_from(b, i);
+    });
   }
-  // q into LDS in B-operand order, then into registers (while the first
-  // tiles' DMA is in flight).  B operand of K-step ks for head block hb,
-  // lane (r16, kg): q[hb*16 + r16][d] with d(ks < 16) = 128kg + 8ks + [0,8)
-  // and d(16 + i) = 512 + 16kg + 8i + [0,8), at 16-byte slot
-  // (hb * 18 + ks) * 64 + 16kg + r16.  A negative softmax scale flips q's
-  // signs here (exact), so sm_log2 >= 0.
+  // q into LDS in B-operand order, then into the score waves' registers
+  // (while the first tiles' DMA is in flight).  B operand of K-step ks for
+  // head block hb, lane (r16, kg): q[hb*16 + r16][d] with d(ks < 16) =
+  // 128kg + 8ks + [0,8) and d(16 + i) = 512 + 16kg + 8i + [0,8), at 16-byte
+  // slot (hb * 18 + ks) * 64 + 16kg + r16.  A negative softmax scale flips
+  // q's signs here (exact), so sm_log2 >= 0.
   {
     // LDS accesses in assembly: the compiler would make them wait for the
-    // tiles' DMA (it cannot tell the V buffer from the ring)
+    // tiles' DMA (it cannot tell the staging area from the ring)
     const uint32_t qs = lds_off(vbuf_all);
 #pragma unroll
     for (int m = 0; m < kQChunks; ++m) {
-      const int c = tid + kThreads * m, h = c / (kQK / 8), d = 8 * (c - h * (kQK / 8));
-      int kgq, ks;
-      if (d < kLatent) {
-        kgq = d >> 7;
-        ks = (d >> 3) & 15;
-      } else {
-        kgq = (d - kLatent) >> 4;
-        ks = 16 + (((d - kLatent) >> 3) & 1);
+      const int c = tid + kThreads * m;
+      if (c < kQChunkAll) {
+        const int h = c / (kQK / 8), d = 8 * (c - h * (kQK / 8));
+        int kgq, ks;
+        if (d < kLatent) {
+          kgq = d >> 7;
+          ks = (d >> 3) & 15;
+        } else {
+          kgq = (d - kLatent) >> 4;
+          ks = 16 + (((d - kLatent) >> 3) & 1);
+        }
+        u32x4 u = q8_operand<kBf16>(qstage[m]);
+        if (p.q_neg) u ^= 0x80008000u;
+        const uint32_t a = qs + 16 * (((h >> 4) * kKSteps + ks) * 64 + 16 * kgq + (h & 15));
+        MLA_DEVICE_ASM("ds_write_b128 %0, %1" :: "v"(a), "v"(u) : "memory");
       }
-      u32x4 u = q8_operand<kBf16>(qstage[m]);
-      if (p.q_neg) u ^= 0x80008000u;
-      const uint32_t a = qs + 16 * (((h >> 4) * kKSteps + ks) * 64 + 16 * kgq + (h & 15));
-      MLA_DEVICE_ASM("ds_write_b128 %0, %1" :: "v"(a), "v"(u) : "memory");
     }
     lds_barrier();   // (not __syncthreads: that would also wait for the tiles' DMA)
-    const uint32_t qa = qs + 16 * lane;
-    static_for<0, 2 * kKSteps>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      qreg[i / kKSteps][i % kKSteps] = __builtin_bit_cast(half8_t, ring_b128<1024 * i>(qa));
-    });
-    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) MLA_DEVICE_ASM("" : "+v"(qreg[hb][ks]));
-    lds_barrier();   // every wave has its q before the V buffer is written
   }
-  if (my_tiles > 0) {
 
-    // tile 0: scores only
-    {
-      const uint32_t slot = tile_start(0);
-#pragma unroll
-      for (int ks = 16; ks < kKSteps; ++ks) score_step(0, ks, slot);   // rope first: its bytes are then dead
-      if (two_level) scale_rope_scores(sacc, p.inv_lat_scale);
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) score_step(0, ks, slot);
-    }
-    (void)softmax_ref(0);
-    half8_t pa = softmax_p(0);
-
-    // tiles 1 .. my_tiles-1: values of tile k-1 with the scores of tile k.
-    // A raised reference rescales O lazily: each value group first scales
-    // its four column blocks (the register allocator keeps O in place only
-    // when every rescale sits next to the MFMAs that consume it).
-    bool pending = false;   // O is still to be rescaled by alv before its next value MFMA
-    float16_t alv = {};     // the rescale factors of this lane's 16 accumulator rows
-    auto rescale_group = [&](auto J) {
-      constexpr int j = decltype(J)::value;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc_o[j + 4 * e][i] = scale_acc(acc_o[j + 4 * e][i], alv[i]);
-    };
-    for (int k = 1; k < my_tiles; ++k) {
-      const uint32_t slot = tile_start(k);
-      half2_t sh[4];
-      if constexpr (kFmt == kFmtNvfp4) group_scales(sh, raw.sc);
-#pragma unroll
-      for (int ks = 16; ks < kKSteps; ++ks) {   // rope
-        const half8_t kop = kstep8<kFmt>(raw, ks);
-        score_mfma2(sacc, kop, qreg[0][ks], qreg[1][ks], ks == 16);
-      }
-      if (two_level) scale_rope_scores(sacc, p.inv_lat_scale);
-      // Slot t (latent K-step t): the value MFMA of one column block of
-      // tile k-1, the conversions of K-step t+1 split around the two score
-      // MFMAs of K-step t, then the V write of K-step t+1.  The order is
-      // pinned (sched_barrier) so that every conversion issues while an MFMA
-      // runs.
-      half8_t kop;
-      {
-        KDec d;
-        kdec_part1<kFmt>(d, raw, sh, 0);
-        kop = kdec_part2<kFmt>(d, raw, sh, 0);
-      }
-      // value groups read one unit ahead (two buffers): group j + 1 is read
-      // during unit j, before K-step 4(j+1) overwrites it at unit j + 1
-      u32x4 bvb[2][4];
-      read_v4_group<0>(bvb[0], vb);
-      ring_issue_b<kFmt>(raw, slot, ro);   // latent K-steps 8..15 (FP8: 8..11), waited for with group 1
-      // the slot of tile k + 2 held tile k - 1 (NVFP4, 3 slots), now in
-      // registers; FP8 rows (2 slots) refill the slot of tile k itself once
-      // the last of its bytes are read, in value group 1
-      if constexpr (kFmt == kFmtNvfp4)
-        if (k + 2 < my_tiles) issue(next_row, (k + 2) % kDepth);
-      static_for<0, 4>([&](auto J) {
-        constexpr int j = decltype(J)::value;
-        u32x4 (&bv)[4] = bvb[j & 1];
-        // group j's reads were issued one unit earlier, followed by that
-        // unit's four V-buffer writes (unit 0: by the ring's part B reads,
-        // which it waits for as well)
-        if constexpr (j == 0) lgkm_wait(bv);
-        else if constexpr (j == 1) lgkm_wait_b<kFmt>(bv, raw);
-        else if constexpr (j == 2) lgkm_wait4_b2<kFmt>(bv, raw);
-        else lgkm_wait4(bv);
-        if constexpr (j < 3) read_v4_group<j + 1>(bvb[(j + 1) & 1], vb);
-        if constexpr (j == 1 && kFmt == kFmtFp8) {
-          ring_issue_b2<kFmt>(raw, slot, ro);   // K-steps 12..15
-          if (k + 2 < my_tiles) issue(next_row, (k + 2) % kDepth);
-        }
-        *reinterpret_cast<half8_t*>(vrow + 8 * (4 * j)) = kop;   // after group j's reads
-        if (pending) rescale_group(J);
-        static_for<0, 4>([&](auto E) {
-          constexpr int e = decltype(E)::value;
-          constexpr int t = 4 * j + e;
-          KDec d;
-          __builtin_amdgcn_sched_barrier(0);
-          acc_o[j + 4 * e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              pa, __builtin_bit_cast(half8_t, bv[e]), acc_o[j + 4 * e], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-          if constexpr (t < 15) kdec_part1<kFmt>(d, raw, sh, t + 1);
-          __builtin_amdgcn_sched_barrier(0);
-          score_mfma1(sacc[0], kop, qreg[0][t]);
-          __builtin_amdgcn_sched_barrier(0);
-          half8_t nx;
-          if constexpr (t < 15) nx = kdec_part2<kFmt>(d, raw, sh, t + 1);
-          __builtin_amdgcn_sched_barrier(0);
-          score_mfma1(sacc[1], kop, qreg[1][t]);
-          __builtin_amdgcn_sched_barrier(0);
-          if constexpr (t < 15) {
-            kop = nx;
-            if constexpr ((t + 1) % 4 != 0) *reinterpret_cast<half8_t*>(vrow + 8 * (t + 1)) = kop;
-          }
-        });
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      pending = softmax_ref(k);
-      if (pending) {   // (LDS keeps this wave's order for alpha_s)
-        MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-        for (int i = 0; i < 16; ++i) alv[i] = alpha_s[wave][c_head(i, lane)];
-      }
-      pa = softmax_p(k);
-    }
-
-    // values of the last tile
-    static_for<0, 4>([&](auto J) {
-      constexpr int j = decltype(J)::value;
-      u32x4 bv[4];
-      read_v4_group<j>(bv, vb);
-      if (pending) rescale_group(J);
-      lgkm_wait(bv);
-      value_group(bv, pa, J);
-    });
-  }
-  wait_vmcnt<0>();   // no DMA may still be writing this workgroup's LDS
-
-  // ---------------------------------------------------------------- merge the streams
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    lsum[hb] += shfl_xor_f(lsum[hb], 16);
-    lsum[hb] += shfl_xor_f(lsum[hb], 32);
-  }
-  if (kg == 0) {
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      wm_s[wave][hb * 16 + r16] = mref[hb];
-      wl_s[wave][hb * 16 + r16] = lsum[hb];
-    }
-  }
-  __syncthreads();   // every stream's state is visible and the rings are idle
-  // weight of stream w for head hd: 2^(m_w - M) / L with
-  // M = max_w m_w and L = sum_w 2^(m_w - M) l_w; log2-sum-exp = M + log2 L
-  if (tid < kWaves * kHG) {
-    const int w = tid >> 5, hd = tid & 31;
-    float M = kNegInf;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = __builtin_fmaxf(M, wm_s[v][hd]);
-    float L = 0.0f;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int v = 0; v < kWaves; ++v)
-        L += wm_s[v][hd] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(wm_s[v][hd] - M) * wl_s[v][hd];
-    }
-    const float mw = wm_s[w][hd];
-    alpha_s[w][hd] = (L > 0.0f && mw != kNegInf) ? __builtin_amdgcn_exp2f(mw - M) / L : 0.0f;
-    if (w == 0) {
-      const float lse2 = L > 0.0f ? M + __log2f(L) : kNegInf;
-      const int head = g * kHG + hd;
-      if (S > 1) __hip_atomic_store(p.part_lse + (tg * S + s) * kHG + hd, lse2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else if (head < p.H && p.lse) p.lse[t * p.H + head] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
-    }
-  }
-  __syncthreads();
-  // Stream merge in two rounds of 256 columns.  Each wave writes its FP32
-  // O for 8 column blocks straight from the accumulation registers into its
-  // exchange region (waves 0, 1 in the ring area, 2, 3 in the V area; the
-  // rings are idle), then every thread sums the four streams for 4 heads x 8
-  // columns with the stream weights and stores them (16-byte stores).
-  // Exchange layout: 16-byte slot s (the lane of the MFMA C layout) of block
-  // b (column block within the round x 4 + element quad) sits at byte
-  // 1136 b + 16 s + 32 (s >> 4): the writers' 64 lanes and the readers' 8
-  // consecutive slots (8 columns of 4 heads) are both free of bank conflicts.
+  const float sm = p.sm_log2;
   const float out_mul = p.kv_scale * p.lat_scale;  // values carry the cache's per-tensor scale
   const int64_t H = p.H;
-  {
-    constexpr uint32_t kXBlock = 1136, kXRegion = 32 * kXBlock;
-    static_assert(2 * kXRegion <= kWaves * kWaveRing && 2 * kXRegion <= kWaves * kWaveV * 2, "exchange regions");
-    uint8_t* const x01 = ring_all;
-    uint8_t* const x23 = reinterpret_cast<uint8_t*>(vbuf_all);
-    uint8_t* const xw = (wave < 2 ? x01 : x23) + (wave & 1) * kXRegion + 16 * lane + 32 * (lane >> 4);
-    // reader: heads 4 hq + [0,4), columns 256 hh + 8 co + [0,8)
-    const int hq = tid & 7, co = tid >> 3;
-    const uint32_t rslot = 32 * (hq & 1) + 8 * (co & 3);
-    const uint32_t rofs = ((co >> 2) * 4 + (hq >> 1)) * kXBlock + 16 * rslot + 32 * (rslot >> 4);
-    const uint8_t* const r01 = x01 + rofs;
-    const uint8_t* const r23 = x23 + rofs;
-    const float mul = S > 1 ? 1.0f : out_mul;
-    float wgt[kWaves][4];
+  // exchange region of value wave j (epilogue): j = 0, 1 in the ring area,
+  // 2, 3 in the V area
+  auto xregion = [&](int j) -> uint8_t* {
+    return (j < 2 ? ring_all : reinterpret_cast<uint8_t*>(vbuf_all)) + (j & 1) * kXRegion;
+  };
+
+  if (wave < kSW) {
+    // ============================================================ score wave
+    // q's B operands into registers (inside this branch, so that they take
+    // no registers on the value waves' path)
+    half8_t qreg[2][kKSteps];
+    {
+      const uint32_t qa = lds_off(vbuf_all) + 16 * lane;
+      static_for<0, 2 * kKSteps>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        qreg[i / kKSteps][i % kKSteps] = __builtin_bit_cast(half8_t, ring_b128<1024 * i>(qa));
+      });
+      MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
+      for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int h = 0; h < 4; ++h) wgt[w][h] = alpha_s[w][4 * hq + h] * mul;
+        for (int ks = 0; ks < kKSteps; ++ks) MLA_DEVICE_ASM("" : "+v"(qreg[hb][ks]));
+    }
+    lds_barrier();   // every score wave has its q before the V buffer is written
+    const bool two_level = kFmt == kFmtNvfp4 && p.lat_scale != 1.0f;
+    const RingOff<kFmt> ro(r16, kg);
+    half_t* const vrow = vbuf_all + sw * kTileV + r16 * kVRow + 128 * kg;
+    float mref[2] = {kNegInf, kNegInf};   // reference of head hb*16 + r16 (base 2)
+    float lsum[2] = {0.0f, 0.0f};         // this lane's share of that head's row sum
+    Raw<kFmt> raw;
+    float4_t sacc[2];
+    for (int i = 0; i < rounds; ++i) {
+      const bool have = i < my_tiles;     // (only the last round can miss a tile)
+      const int k = sw + kSW * i;         // tile index within the split
+      if (have) {
+        // wait for this tile's DMA (the later tiles' stays in flight: a
+        // wave's vector memory operations complete in issue order), read
+        // its rows, then refill its slot with tile i + kDepth
+        const int later = my_tiles - 1 - i;   // tiles issued after this one
+        if (kDepth > 2 && later >= 2) wait_vmcnt<(kDepth > 2 ? 2 : 0) * kInstr>();
+        else if (later >= 1) wait_vmcnt<kInstr>();
+        else wait_vmcnt<0>();
+        const uint32_t sl = lds_off(ring + (i % kDepth) * kSlot);
+        uint32_t next_row = lds_b32(tile_row_addr(i + kDepth));
+        ring_read<kFmt>(raw, sl, ro, next_row);
+        if (i + kDepth < my_tiles) issue(next_row, i % kDepth);
+        // rope first: its scores need no V-buffer space
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      if (hh == 1) __syncthreads();   // the first round's reads are done
+        for (int ks = 16; ks < kKSteps; ++ks)
+          score_mfma2(sacc, kstep8<kFmt>(raw, ks), qreg[0][ks], qreg[1][ks], ks == 16);
+        if (two_level) scale_rope_scores(sacc, p.inv_lat_scale);
+      }
+      if (i > 0) lds_barrier();   // B(i-1): the value waves hold round i-1 in registers
+      if (have) {
+        // latent K-steps: the A operand of K-step t+1 is converted while
+        // K-step t's two MFMAs run; each goes to the V buffer as well
+        half2_t sh[4];
+        if constexpr (kFmt == kFmtNvfp4) group_scales(sh, raw.sc);
+        half8_t kop = latent8<kFmt>(raw, sh, 0);
+        MLA_DEVICE_ASM("s_nop 1" : "+v"(kop));
+        static_for<0, 16>([&](auto T) {
+          constexpr int tt = decltype(T)::value;
+          *reinterpret_cast<half8_t*>(vrow + 8 * tt) = kop;
+          __builtin_amdgcn_sched_barrier(0);
+          score_mfma1(sacc[0], kop, qreg[0][tt]);
+          __builtin_amdgcn_sched_barrier(0);
+          half8_t nx;
+          if constexpr (tt < 15) nx = latent8<kFmt>(raw, sh, tt + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          score_mfma1(sacc[1], kop, qreg[1][tt]);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (tt < 15) kop = nx;
+        });
+
+        // softmax: the lane holds rows 4kg + j (j = 0..3) of head
+        // hb*16 + r16; sm >= 0, so the scaled max is the max scaled.  Only
+        // the split's last tile can hold rows past its end; they get P = 0.
+        const int row0 = k * kRowsT + 4 * kg;
+        const bool ragged = (k + 1) * kRowsT > n;
+        score_mfma_drain(sacc);
+        float tmax[2];
 #pragma unroll
-      for (int nbl = 0; nbl < 8; ++nbl)
+        for (int hb = 0; hb < 2; ++hb) {
+          float m = max4(sacc[hb][0], sacc[hb][1], sacc[hb][2], sacc[hb][3]);
+          if (ragged) {
+            m = kNegInf;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<float4_t*>(xw + (nbl * 4 + q) * kXBlock) =
-              (float4_t){acc_o[8 * hh + nbl][4 * q], acc_o[8 * hh + nbl][4 * q + 1], acc_o[8 * hh + nbl][4 * q + 2],
-                         acc_o[8 * hh + nbl][4 * q + 3]};
-      __syncthreads();
+            for (int j = 0; j < 4; ++j)
+              if (row0 + j < n) m = __builtin_fmaxf(m, sacc[hb][j]);
+          }
+          // (-inf * 0 is NaN; the max with -inf maps it back to -inf)
+          tmax[hb] = __builtin_fmaxf(m * sm, kNegInf);
+        }
+        const bool first = i == 0;
+        const bool raise = tmax[0] > mref[0] + kLazy || tmax[1] > mref[1] + kLazy;
+        if (first || __ballot(raise) != 0) {
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            float m = tmax[hb];
+            m = __builtin_fmaxf(m, shfl_xor_f(m, 16));
+            m = __builtin_fmaxf(m, shfl_xor_f(m, 32));
+            const float mnew = __builtin_fmaxf(mref[hb], m) + kMargin;
+            lsum[hb] *= first ? 0.0f : __builtin_amdgcn_exp2f(mref[hb] - mnew);
+            mref[hb] = mnew;
+          }
+        }
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const float nm = -mref[hb];
+          float pv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[hb][j], sm, nm));
+          if (ragged) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (row0 + j >= n) pv[j] = 0.0f;
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) lsum[hb] += pv[j];
+          const u32x2 d = {as_u32(__builtin_convertvector((float2_t){pv[0], pv[1]}, half2_t)),
+                           as_u32(__builtin_convertvector((float2_t){pv[2], pv[3]}, half2_t))};
+          *reinterpret_cast<u32x2*>(&pbuf[sw][hb * 16 + r16][4 * kg]) = d;
+          if (kg == 0) ref_s[sw][hb * 16 + r16] = mref[hb];
+        }
+      }
+      lds_barrier();   // A(i): round i's P, references and V are in LDS
+    }
+    if (rounds > 0) lds_barrier();   // B(rounds-1)
+    wait_vmcnt<0>();   // no DMA may still be writing this workgroup's LDS
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      lsum[hb] += shfl_xor_f(lsum[hb], 16);
+      lsum[hb] += shfl_xor_f(lsum[hb], 32);
+    }
+    if (kg == 0) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        wm_s[sw][hb * 16 + r16] = mref[hb];
+        wl_s[sw][hb * 16 + r16] = lsum[hb];
+      }
+    }
+    lds_barrier();   // E: every score wave's (reference, row sum) is in LDS
+    lds_barrier();   // F: the value waves have read them
+  } else {
+    // ============================================================ value wave
+    lds_barrier();   // (the score waves' q reads)
+    const int j = wave - kSW;
+    const int hl = lane & 31;               // head of this lane's P operand
+    float16_t acc[4];                       // O[32 heads x 32 cols] of column block 32c + [0,32), C layout
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[c][e] = 0.0f;
+    float M = kNegInf;                      // reference of O for head hl
+    // V operand address (column block 0 of tile 0 of this wave's columns):
+    // the ds_read_b64_tr_b16 pattern gives lane L rows 8 (L >> 5) + [0,4)
+    // (and + [4,8) from the second read) of column L & 31
+    const int vgrp = lane >> 4, vsl = lane & 15;
+    const uint32_t vb = lds_off(vbuf_all + (8 * (vgrp >> 1) + (vsl >> 2)) * kVRow + 16 * (vgrp & 1) +
+                                4 * (vsl & 3) + kVCols * j);
+    const uint32_t pa_addr = lds_off(&pbuf[0][hl][8 * (lane >> 5)]);
+    const uint32_t ref_addr = lds_off(&ref_s[0][hl]);
+    const uint32_t fac_w = lds_off(&fac_s[j][hl]);
+    const uint32_t fac_r = lds_off(&fac_s[j][4 * (lane >> 5)]);
+    // factors of this lane's 16 accumulator heads (c_head) from fac_s[j]
+    auto read_factors = [&](float (&f)[16]) {
+      MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" ::: "memory");
+      static_for<0, 4>([&](auto Q) {
+        constexpr int q = decltype(Q)::value;
+        u32x4 v;
+        MLA_DEVICE_ASM("ds_read_b128 %0, %1 offset:%2\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(fac_r), "i"(32 * q));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[4 * q + e] = __uint_as_float(v[e]);
+      });
+    };
+    for (int i = 0; i < rounds; ++i) {
+      const int nt = ntiles - kSW * i < kSW ? ntiles - kSW * i : kSW;   // tiles in this round
+      lds_barrier();   // A(i)
+      half8_t pa[kSW];
+      float mr[kSW];
+      u32x4 bv[kSW][4];
+      static_for<0, kSW>([&](auto W) {
+        constexpr int w = decltype(W)::value;
+        pa[w] = __builtin_bit_cast(half8_t, ring_b128<w * kHG * kRowsT * 2>(pa_addr));
+        mr[w] = __uint_as_float(lds_b32<w * kHG * 4>(ref_addr));
+        read_v_tile<w>(bv[w], vb);
+      });
+      lds_barrier();   // B(i): waits for this wave's reads, then releases the buffers
+#pragma unroll
+      for (int w = 0; w < kSW; ++w)
+        MLA_DEVICE_ASM("" : "+v"(pa[w]), "+v"(mr[w]), "+v"(bv[w][0]), "+v"(bv[w][1]), "+v"(bv[w][2]), "+v"(bv[w][3]));
+      // O follows the largest reference of the round's tiles (per head)
+      float mx = M;
+#pragma unroll
+      for (int w = 0; w < kSW; ++w)
+        if (w < nt) mx = __builtin_fmaxf(mx, mr[w]);
+      if (__ballot(mx > M) != 0) {
+        const float f = mx > M ? (M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - mx)) : 1.0f;
+        if (lane < 32) *reinterpret_cast<float*>(&fac_s[j][hl]) = f;
+        float fo[16];
+        read_factors(fo);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[c][e] *= fo[e];
+        M = mx;
+      }
+      static_for<0, kSW>([&](auto W) {
+        constexpr int w = decltype(W)::value;
+        if (w < nt) {
+          // P relative to M: a power of two, exact in FP16 above its subnormals
+          const float f = __builtin_amdgcn_exp2f(mr[w] - M);
+          if (__ballot(f != 1.0f) != 0) pa[w] = pa[w] * (half_t)f;
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[w], __builtin_bit_cast(half8_t, bv[w][c]), acc[c],
+                                                             0, 0, 0);
+        }
+      });
+    }
+    (void)fac_w;
+    lds_barrier();   // E
+    // weight of head h: 1 / L with L = sum_w 2^(m_w - M) l_w over the score
+    // waves (whose references are all <= M); log2-sum-exp = M + log2 L
+    float inv = 0.0f, lse2 = kNegInf;
+    {
+      float L = 0.0f;
+      if (M != kNegInf) {
+#pragma unroll
+        for (int w = 0; w < kSW; ++w)
+          L += wm_s[w][hl] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(wm_s[w][hl] - M) * wl_s[w][hl];
+      }
+      if (L > 0.0f) {
+        inv = 1.0f / L;
+        lse2 = M + __log2f(L);
+      }
+    }
+    lds_barrier();   // F
+    if (j == 0 && lane < 32) {
+      const int head = g * kHG + hl;
+      if (S > 1) __hip_atomic_store(p.part_lse + (tg * S + s) * kHG + hl, lse2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else if (head < p.H && p.lse) p.lse[t * H + head] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
+    }
+    // normalise this wave's columns, then store them through its exchange
+    // region: block (c * 4 + q) holds, in slot L, heads 8q + 4(L >> 5) +
+    // [0,4) of column 32c + (L & 31); a reader takes heads 4hq + [0,4) x
+    // columns 8co + [0,8) (8 consecutive slots of one block) and stores
+    // 16-byte rows of 8 columns per head.
+    if (lane < 32) fac_s[j][hl] = inv * (S > 1 ? 1.0f : out_mul);
+    float fo[16];
+    read_factors(fo);
+    uint8_t* const xr = xregion(j);
+    uint8_t* const xw = xr + 16 * lane + 32 * (lane >> 4);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4_t*>(xw + (c * 4 + q) * kXBlock) =
+            (float4_t){acc[c][4 * q] * fo[4 * q], acc[c][4 * q + 1] * fo[4 * q + 1],
+                       acc[c][4 * q + 2] * fo[4 * q + 2], acc[c][4 * q + 3] * fo[4 * q + 3]};
+    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int hq = lane & 7, co = (lane >> 3) + 8 * u;
+      const uint32_t rslot = 32 * (hq & 1) + 8 * (co & 3);
+      const uint8_t* const src = xr + ((co >> 2) * 4 + (hq >> 1)) * kXBlock + 16 * rslot + 32 * (rslot >> 4);
       float o[4][8];
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
+      for (int x = 0; x < 8; ++x) {
+        const float4_t v = *reinterpret_cast<const float4_t*>(src + 16 * x);
 #pragma unroll
-        for (int x = 0; x < 8; ++x) o[h][x] = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const uint8_t* const src = (w < 2 ? r01 : r23) + (w & 1) * kXRegion;
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const float4_t v = *reinterpret_cast<const float4_t*>(src + 16 * x);
-#pragma unroll
-          for (int h = 0; h < 4; ++h) o[h][x] = __builtin_fmaf(wgt[w][h], v[h], o[h][x]);
-        }
+        for (int h = 0; h < 4; ++h) o[h][x] = v[h];
       }
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const int hd = 4 * hq + h, head = g * kHG + hd;
-        const int col = 256 * hh + 8 * co;
+        const int col = kVCols * j + 8 * co;
         if (S > 1) store8_agent(p.part_o + ((tg * S + s) * kHG + hd) * kLatent + col, o[h]);
         else if (head < p.H)
           store8<kBf16>(reinterpret_cast<uint16_t*>(p.out) + (t * H + head) * kLatent + col, o[h]);
@@ -1101,40 +934,41 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   __syncthreads();
   if (!last_s) return;
 
-  // Chunks of 8 consecutive columns, 32 heads x 64 chunks: chunk tid + 256 m
-  // (m = 0..7) is head (tid >> 6) + 4 m, columns 8 (tid & 63).  Splits are
+  // Chunks of 8 consecutive columns, 32 heads x 64 chunks: chunk tid + 512 m
+  // (m = 0..3) is head (tid >> 6) + 8 m, columns 8 (tid & 63).  Splits are
   // summed in index order, two per round, and the next round's 16-byte
   // loads are in flight while a round is summed (an odd count adds split s0
   // again with weight 0).  The log2-sum-exps are loaded first (lane x of
   // wave 0 reads split x's), then the first round's partials, so that the
   // merge weights wait only for the former.
+  constexpr int kMH = kHG * 64 / kThreads;   // heads per thread
   float* lse_sh = reinterpret_cast<float*>(ring_all);   // [S][32]
   float* wsh = lse_sh + 64 * kHG;                        // [S][32]
   const int cc = 8 * (tid & 63);
   const half_t* pp = p.part_o + (tg * S) * kHG * kLatent + (tid >> 6) * kLatent + cc;
-  auto load_split = [&](int x, half8_t (&v)[8]) {
+  auto load_split = [&](int x, half8_t (&v)[kMH]) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) v[m] = *reinterpret_cast<const half8_t*>(pp + (x * kHG + 4 * m) * kLatent);
+    for (int m = 0; m < kMH; ++m) v[m] = *reinterpret_cast<const half8_t*>(pp + (x * kHG + kWaves * m) * kLatent);
   };
-  float a[8][8];
+  float a[kMH][8];
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
+  for (int m = 0; m < kMH; ++m)
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[m][i] = 0.0f;
-  auto add_pair = [&](const half8_t (&v0)[8], const half8_t (&v1)[8], int s0) {
+  auto add_pair = [&](const half8_t (&v0)[kMH], const half8_t (&v1)[kMH], int s0) {
     const bool has1 = s0 + 1 < S;
     const int s1 = has1 ? s0 + 1 : s0;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const float w0 = wsh[s0 * kHG + (tid >> 6) + 4 * m];
-      const float w1 = has1 ? wsh[s1 * kHG + (tid >> 6) + 4 * m] : 0.0f;
+    for (int m = 0; m < kMH; ++m) {
+      const float w0 = wsh[s0 * kHG + (tid >> 6) + kWaves * m];
+      const float w1 = has1 ? wsh[s1 * kHG + (tid >> 6) + kWaves * m] : 0.0f;
       // (two fused multiply-adds per element, each taking its FP16 operand
       // as is: v_fma_mix)
 #pragma unroll
       for (int i = 0; i < 8; ++i) a[m][i] = __builtin_fmaf(w1, (float)v1[m][i], __builtin_fmaf(w0, (float)v0[m][i], a[m][i]));
     }
   };
-  half8_t A0[8], A1[8], B0[8], B1[8];
+  half8_t A0[kMH], A1[kMH], B0[kMH], B1[kMH];
   float4_t lx[8];
   if (wave == 0) {
     const float4_t* src = reinterpret_cast<const float4_t*>(p.part_lse + (tg * S + (lane < S ? lane : 0)) * kHG);
@@ -1181,8 +1015,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     }
   }
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int hd = (tid >> 6) + 4 * m, head = g * kHG + hd;
+  for (int m = 0; m < kMH; ++m) {
+    const int hd = (tid >> 6) + kWaves * m, head = g * kHG + hd;
     if (head >= p.H) continue;
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[m][i] *= out_mul;
@@ -1226,8 +1060,8 @@ int decode_auto_splits(int64_t T, int H, int topk) {
   const int cus = device_cus() > 0 ? device_cus() : 256;
   // One workgroup per CU is resident at a time: fill the CUs once (more
   // splits than that would start a second, mostly idle round).  A split
-  // keeps at least 256 valid rows (four tiles per stream) so its fixed
-  // costs (index compaction, q load, stream and split merges) stay small.
+  // keeps at least 256 valid rows (four rounds of tiles) so its fixed costs
+  // (index compaction, q staging, split merge) stay small.
   int64_t s = cus / groups;
   int64_t max_by_rows = topk / 256;
   if (max_by_rows < 1) max_by_rows = 1;
