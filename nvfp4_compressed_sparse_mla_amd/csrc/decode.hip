@@ -935,54 +935,60 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   if (!last_s) return;
 
   // Chunks of 8 consecutive columns, 32 heads x 64 chunks: chunk tid + 512 m
-  // (m = 0..3) is head (tid >> 6) + 8 m, columns 8 (tid & 63).  Splits are
-  // summed in index order, two per round, and the next round's 16-byte
-  // loads are in flight while a round is summed (an odd count adds split s0
-  // again with weight 0).  The log2-sum-exps are loaded first (lane x of
-  // wave 0 reads split x's), then the first round's partials, so that the
-  // merge weights wait only for the former.
+  // (m = 0..3) is head (tid >> 6) + 8 m, columns 8 (tid & 63).  The
+  // log2-sum-exps are loaded first (lane x of wave 0 reads split x's), then
+  // the partials of up to kBatch splits at once, so that the merge waits
+  // for one memory round trip per batch; the merge weights are computed
+  // while the partials are in flight.  Splits are summed in index order.
   constexpr int kMH = kHG * 64 / kThreads;   // heads per thread
+  constexpr int kBatch = 8;                  // splits whose partials are in flight together
   float* lse_sh = reinterpret_cast<float*>(ring_all);   // [S][32]
   float* wsh = lse_sh + 64 * kHG;                        // [S][32]
   const int cc = 8 * (tid & 63);
   const half_t* pp = p.part_o + (tg * S) * kHG * kLatent + (tid >> 6) * kLatent + cc;
-  auto load_split = [&](int x, half8_t (&v)[kMH]) {
+  half8_t part[kBatch][kMH];
+  auto load_batch = [&](int x0) {
+    static_for<0, kBatch>([&](auto X) {
+      constexpr int x = decltype(X)::value;
+      if (x0 + x < S) {
 #pragma unroll
-    for (int m = 0; m < kMH; ++m) v[m] = *reinterpret_cast<const half8_t*>(pp + (x * kHG + kWaves * m) * kLatent);
+        for (int m = 0; m < kMH; ++m)
+          part[x][m] = *reinterpret_cast<const half8_t*>(pp + ((x0 + x) * kHG + kWaves * m) * kLatent);
+      }
+    });
   };
   float a[kMH][8];
 #pragma unroll
   for (int m = 0; m < kMH; ++m)
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[m][i] = 0.0f;
-  auto add_pair = [&](const half8_t (&v0)[kMH], const half8_t (&v1)[kMH], int s0) {
-    const bool has1 = s0 + 1 < S;
-    const int s1 = has1 ? s0 + 1 : s0;
+  auto add_batch = [&](int x0) {
+    static_for<0, kBatch>([&](auto X) {
+      constexpr int x = decltype(X)::value;
+      if (x0 + x < S) {
 #pragma unroll
-    for (int m = 0; m < kMH; ++m) {
-      const float w0 = wsh[s0 * kHG + (tid >> 6) + kWaves * m];
-      const float w1 = has1 ? wsh[s1 * kHG + (tid >> 6) + kWaves * m] : 0.0f;
-      // (two fused multiply-adds per element, each taking its FP16 operand
-      // as is: v_fma_mix)
+        for (int m = 0; m < kMH; ++m) {
+          const float w = wsh[(x0 + x) * kHG + (tid >> 6) + kWaves * m];
+          // (a fused multiply-add per element taking its FP16 operand as is: v_fma_mix)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a[m][i] = __builtin_fmaf(w1, (float)v1[m][i], __builtin_fmaf(w0, (float)v0[m][i], a[m][i]));
-    }
+          for (int i = 0; i < 8; ++i) a[m][i] = __builtin_fmaf(w, (float)part[x][m][i], a[m][i]);
+        }
+      }
+    });
   };
-  half8_t A0[kMH], A1[kMH], B0[kMH], B1[kMH];
   float4_t lx[8];
   if (wave == 0) {
     const float4_t* src = reinterpret_cast<const float4_t*>(p.part_lse + (tg * S + (lane < S ? lane : 0)) * kHG);
 #pragma unroll
     for (int i = 0; i < 8; ++i) lx[i] = src[i];
   }
-  load_split(0, A0);
-  load_split(1 < S ? 1 : 0, A1);
+  load_batch(0);
   if (wave == 0 && lane < S) {
     float4_t* dst = reinterpret_cast<float4_t*>(lse_sh + lane * kHG);
 #pragma unroll
     for (int i = 0; i < 8; ++i) dst[i] = lx[i];
   }
-  __syncthreads();
+  lds_barrier();   // (not __syncthreads: the partials' loads stay in flight)
   if (tid < kHG) {
     float mx = kNegInf;
     for (int ss = 0; ss < S; ++ss) mx = __builtin_fmaxf(mx, lse_sh[ss * kHG + tid]);
@@ -995,24 +1001,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     const int head = g * kHG + tid;
     if (head < p.H && p.lse) p.lse[t * H + head] = mx != kNegInf ? (mx + __log2f(sum)) * kLn2 : kNegInf;
   }
-  __syncthreads();
-  {
-    for (int s0 = 0; s0 < S; s0 += 4) {
-      const bool more = s0 + 2 < S;
-      if (more) {
-        load_split(s0 + 2, B0);
-        load_split(s0 + 3 < S ? s0 + 3 : s0 + 2, B1);
-      }
-      add_pair(A0, A1, s0);
-      if (!more) break;
-      const bool more2 = s0 + 4 < S;
-      if (more2) {
-        load_split(s0 + 4, A0);
-        load_split(s0 + 5 < S ? s0 + 5 : s0 + 4, A1);
-      }
-      add_pair(B0, B1, s0 + 2);
-      if (!more2) break;
-    }
+  lds_barrier();
+  for (int x0 = 0; x0 < S; x0 += kBatch) {
+    if (x0 > 0) load_batch(x0);
+    add_batch(x0);
   }
 #pragma unroll
   for (int m = 0; m < kMH; ++m) {
