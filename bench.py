@@ -339,7 +339,7 @@ def _two_level(torch, mla, c: Case, n: int):
 
 def _indexer(torch, mla, c: Case, n: int):
     """The sparse indexer over every token's visible positions (kernel time of
-    its two kernels, from the first one's start to the second one's end)."""
+    its three kernels, from the first one's start to the last one's end)."""
     from synth import indexer_inputs
 
     w = c.w

@@ -330,7 +330,11 @@ int mla_nvfp4_gather_dequant_fp8(const uint8_t* cache, int64_t cache_rows,
  *                     out_stride_t >= topk.
  *   workspace         device, >= mla_indexer_workspace_size(T, max_ctx)
  *                     bytes, 16-byte aligned, zero-filled before first use
- *                     (every completed call leaves its histogram part zero).
+ *                     (every completed call leaves its histogram and
+ *                     candidate-count parts zero).  It holds, per token,
+ *                     a 4096-bin histogram, a candidate count, max_ctx
+ *                     score keys, candidate keys and positions, and two
+ *                     max_ctx-bit maps: about 20.5 bytes per position.
  * The result is deterministic.  Calls that overlap in time must not share a
  * workspace.  Non-finite E4M3 codes (0x7F, 0xFF) are outside the contract.
  */

@@ -348,7 +348,7 @@ int mla_indexer_topk(const uint8_t* q_idx, int64_t q_stride_t, const uint8_t* ke
   } else if (!key_base) {
     return MLA_ERR_INVALID_ARG;
   }
-  const int64_t nchunks = ((int64_t)max_ctx + 1023) / 1024;
+  const int64_t nchunks = ((int64_t)max_ctx + 1023) / 1024;   // score-kernel chunks (the finer grid)
   if (num_tokens * nchunks >= ((int64_t)1 << 31) || num_tokens >= ((int64_t)1 << 31)) return MLA_ERR_INVALID_ARG;
   const size_t need = mla::indexer_workspace_bytes(num_tokens, max_ctx);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
@@ -372,9 +372,7 @@ int mla_indexer_topk(const uint8_t* q_idx, int64_t q_stride_t, const uint8_t* ke
   p.topk = topk;
   p.out = out;
   p.out_st = out_stride_t;
-  const size_t hist = ((size_t)num_tokens * 4096 * sizeof(uint32_t) + 255) & ~(size_t)255;
-  p.hist = reinterpret_cast<uint32_t*>(workspace);
-  p.keys_ws = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(workspace) + hist);
+  mla::indexer_workspace_layout(p, workspace, num_tokens, max_ctx);
   p.nchunks = 0;
   const mla::KernelEvents ev = timing_events();
   return launched(mla::launch_indexer(p, (hipStream_t)stream, ev), ev);

@@ -19,15 +19,32 @@
 //                  products and sums, a 3-step lane reduction.  The score
 //                  becomes a 64-bit key whose unsigned order is the score's
 //                  order (0 marks a position that is not a candidate); its
-//                  top 12 bits are counted in a per-token histogram.
-//   select kernel  one workgroup per token: radix select on the keys.  The
-//                  histogram names the 12-bit bucket that holds the k-th
-//                  best key; while that bucket holds more keys than are still
-//                  needed, one pass over the token's keys histograms the next
-//                  12 bits of the keys in it.  A last pass over the positions
-//                  in order writes every key above the bucket and the first
-//                  still-needed keys inside it (equal keys are equal scores,
-//                  so the smaller positions come first), then pads.
+//                  top 12 bits (the score's sign and exponent) are counted
+//                  in a per-token histogram.
+//   Contexts up to 32768 positions take the select kernel, longer ones the
+//   compact and finish kernels; both give the same lists.
+//   select kernel  one workgroup per token: radix select on all its keys.
+//                  The histogram names the 12-bit bucket that holds the k-th
+//                  best key; while that bucket holds more keys than are
+//                  still needed, one pass over the token's keys histograms
+//                  the next 12 bits of the keys in it.  A last pass over the
+//                  positions in order writes every key above the bucket and
+//                  the first still-needed keys inside it, then pads.
+//   compact kernel workgroup = (token, chunk of 8192 positions).  From the
+//                  histogram it finds the 12-bit bucket b that holds the
+//                  k-th best key (every workgroup of the token finds the same
+//                  one).  Each thread takes 32 consecutive positions: keys
+//                  above b set their bit in the token's selection bitmap (one
+//                  word per thread, plain stores); keys inside b are appended
+//                  to the token's candidate list (one atomic per workgroup).
+//   finish kernel  one workgroup per token: a radix select over the
+//                  candidates only (12 more bits per pass, through all 64 if
+//                  ties demand) marks the ones that make the list; keys equal
+//                  to the k-th best one are marked in a tie bitmap and the
+//                  first still-needed of them in position order are taken
+//                  (equal keys are equal scores, so the smaller positions come
+//                  first).  A last pass over the bitmaps in word order writes
+//                  the selected positions in ascending order, then pads.
 #include "mla_device.h"
 #include "mla_launch.h"
 
@@ -39,6 +56,7 @@ constexpr int kIdxDim = 128;
 constexpr int kChunk = 1024;              // positions per score workgroup
 constexpr int kBins = 1 << kIdxHistBits;  // 4096
 constexpr int kSelThreads = 1024;
+constexpr int kShortCtx = 32768;      // contexts up to this use the one-workgroup select
 
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
@@ -49,6 +67,12 @@ __device__ __forceinline__ uint64_t score_key(double s) {
   const uint64_t b = (uint64_t)__double_as_longlong(s);
   return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
+
+// First-level bucket of a key: its top 12 bits (the score's sign and
+// exponent), so that the keys of one bucket share those 12 bits.
+constexpr int kPrefixBits = kIdxHistBits;
+__device__ __forceinline__ uint32_t key_bucket(uint64_t key) { return (uint32_t)(key >> (64 - kPrefixBits)); }
+__device__ __forceinline__ uint64_t bucket_prefix(uint32_t b) { return b; }
 
 // Key row of position pos of token t, or -1 if it names none.
 __device__ __forceinline__ int64_t key_row(const IndexerParams& p, int64_t base, int64_t seq, int pos) {
@@ -83,8 +107,9 @@ __device__ __forceinline__ void e4m3x16_to_f64(const u32x4& w, double (&d)[16]) 
   }
 }
 
-// Inclusive prefix sum over the 1024 threads of the select workgroup in
-// thread order.  `ws` holds 16 words of scratch; all threads must call.
+// Inclusive prefix sum over the NT threads of a workgroup in thread order.
+// `ws` holds NT / 64 words of scratch; all threads must call.
+template <int NT = kSelThreads>
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* ws) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 #pragma unroll
@@ -96,10 +121,42 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* ws) {
   __syncthreads();
   uint32_t add = 0;
 #pragma unroll
-  for (int i = 0; i < kSelThreads / 64; ++i)
+  for (int i = 0; i < NT / 64; ++i)
     if (i < w) add += ws[i];
   __syncthreads();
   return v + add;
+}
+
+// The bucket of a histogram (nbins <= 4096 bins in LDS, larger bins hold
+// larger keys) that holds the need_in-th largest key, need_in >= 1 and at
+// most the histogram's total: out[0] = the bucket, out[1] = keys in the
+// buckets above it, out[2] = keys in it.  Thread i owns the bins
+// nbins - 1 - (per i + j), j = 0 .. per-1, so the scan in thread order counts
+// keys from the top.  All threads must call; out is valid on return.
+template <int NT>
+__device__ __forceinline__ void top_bucket(const uint32_t* hist, int nbins, uint32_t need_in, uint32_t* ws,
+                                           uint32_t* out) {
+  constexpr int kPer = kBins / NT;
+  const int hi = nbins - 1 - kPer * (int)threadIdx.x;
+  uint32_t v = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) v += (hi - j >= 0) ? hist[hi - j] : 0u;
+  const uint32_t incl = block_scan<NT>(v, ws);
+  uint32_t excl = incl - v;
+  if (excl < need_in && need_in <= incl) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t h = (hi - j >= 0) ? hist[hi - j] : 0u;
+      if (excl + h >= need_in) {
+        out[0] = (uint32_t)(hi - j);
+        out[1] = excl;
+        out[2] = h;
+        break;
+      }
+      excl += h;
+    }
+  }
+  __syncthreads();
 }
 
 // N consecutive keys from position i (a multiple of N, N even; the keys
@@ -140,15 +197,16 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerParams p) {
   uint64_t* const kout = p.keys_ws + t * p.key_stride;
   __syncthreads();
 
-  // wave w takes positions p0 + 256 w + 8 i + (lane >> 3), i = 0 .. 31, four at a time
+  // wave w takes positions p0 + kWavePos w + 8 i + (lane >> 3), four i at a time
+  constexpr int kWavePos = kChunk / 4;
   constexpr int kUnroll = 4;
-  for (int i0 = 0; i0 < 32; i0 += kUnroll) {
+  for (int i0 = 0; i0 < kWavePos / 8; i0 += kUnroll) {
     u32x4 raw[kUnroll];
     bool ok[kUnroll];
     int pos[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      pos[u] = p0 + 256 * wave + 8 * (i0 + u) + (lane >> 3);
+      pos[u] = p0 + kWavePos * wave + 8 * (i0 + u) + (lane >> 3);
       const int64_t r = pos[u] < ctx ? key_row(p, base, seq, pos[u]) : -1;
       ok[u] = r >= 0;
       raw[u] = ok[u] ? *reinterpret_cast<const u32x4*>(p.keys + r * kIdxDim + 16 * sub) : (u32x4){0, 0, 0, 0};
@@ -166,7 +224,7 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerParams p) {
       if (sub == 0 && pos[u] < ctx) {
         const uint64_t key = ok[u] ? score_key(s) : 0ull;
         kout[pos[u]] = key;
-        if (key) atomicAdd(&hist[key >> (64 - kIdxHistBits)], 1u);
+        if (key) atomicAdd(&hist[key_bucket(key)], 1u);
       }
     }
   }
@@ -233,8 +291,8 @@ __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerPara
   uint32_t need_in = need;
   if (!all) {
     find_bin(need_in, kBins);
-    prefix = sh_bin;
-    pbits = kIdxHistBits;
+    prefix = bucket_prefix(sh_bin);
+    pbits = kPrefixBits;
     need_in -= sh_above;
     uint32_t cnt = sh_cnt;
     // refine while the bucket holds more keys than are still needed
@@ -312,25 +370,281 @@ __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerPara
   for (int i = (int)need + tid; i < p.topk; i += kSelThreads) out[i] = -1;
 }
 
+constexpr int kCT = 256;              // compact kernel threads
+constexpr int kCPos = 32 * kCT;       // positions per compact workgroup (one bitmap word per thread)
+
+// The k-th best key's 12-bit bucket from the token's histogram (in LDS):
+// sh[0] = bucket, sh[1] = keys above it, sh[3] = all candidate keys.  `all`
+// when every candidate makes the list (then no bucket is needed).
+template <int NT>
+__device__ __forceinline__ void threshold_bucket(const uint32_t* hist, uint32_t* ws, uint32_t* sh, int topk,
+                                                 uint32_t& need, bool& all) {
+  constexpr int kPer = kBins / NT;
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) mine += hist[kPer * (int)threadIdx.x + j];
+  const uint32_t total = block_scan<NT>(mine, ws);
+  if ((int)threadIdx.x == NT - 1) sh[3] = total;
+  __syncthreads();
+  const uint32_t n_cand = sh[3];
+  need = n_cand < (uint32_t)topk ? n_cand : (uint32_t)topk;
+  all = need == n_cand;
+  if (!all) top_bucket<NT>(hist, kBins, need, ws, sh);
+}
+
+__global__ __launch_bounds__(kCT) void indexer_compact_kernel(IndexerParams p) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t ws[kCT / 64];
+  __shared__ uint32_t sh[4];
+  __shared__ uint32_t base_s;
+  const uint32_t ncc = (uint32_t)p.cchunks;
+  const uint32_t t32 = blockIdx.x / ncc;
+  const int c = (int)(blockIdx.x - t32 * ncc);
+  const int64_t t = t32;
+  const int ctx = token_ctx(p, t);
+  const int p0 = c * kCPos;
+  if (p0 >= ctx) return;
+  const int tid = threadIdx.x;
+  // 32 consecutive positions per thread (one selection-bitmap word); their
+  // keys are loaded while the histogram is scanned
+  const int pp = p0 + 32 * tid;
+  const uint64_t* const keys = p.keys_ws + t * p.key_stride;
+  uint64_t k[32];
+  load_keys<32>(keys, pp, ctx, k);
+  const uint32_t* const g = p.hist + t * kBins;
+  for (int i = tid; i < kBins; i += kCT) hist[i] = g[i];
+  __syncthreads();
+  uint32_t need;
+  bool all;
+  threshold_bucket<kCT>(hist, ws, sh, p.topk, need, all);
+  // keys of bucket b share their top bits: compare those with b's
+  const uint64_t pstar = all ? 0 : bucket_prefix(sh[0]);
+
+  uint32_t sel = 0, cm = 0;   // selected / candidate bits of the 32 positions
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const uint64_t top = k[j] >> (64 - kPrefixBits);
+    if (k[j] && (all || top > pstar)) sel |= 1u << j;
+    if (k[j] && !all && top == pstar) cm |= 1u << j;
+  }
+  const uint32_t nc = __popc(cm);
+  if (pp < ctx) {
+    p.sel_bits[t * p.word_stride + (pp >> 5)] = sel;
+    p.tie_bits[t * p.word_stride + (pp >> 5)] = 0u;
+  }
+  // the bucket's keys join the token's candidate list
+  const uint32_t incl = block_scan<kCT>(nc, ws);
+  if (tid == kCT - 1) base_s = incl ? atomicAdd(&p.cand_n[t], incl) : 0u;
+  __syncthreads();
+  if (nc) {
+    uint32_t o = base_s + incl - nc;
+    uint64_t* const ck = p.cand_key + t * p.key_stride;
+    uint32_t* const cp = p.cand_pos + t * p.key_stride;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if ((cm >> j) & 1u) {
+        ck[o] = k[j];
+        cp[o] = (uint32_t)(pp + j);
+        ++o;
+      }
+    }
+  }
+}
+
+// a bitmap word written by an earlier kernel or by this kernel's atomics,
+// read at the device-coherent level
+__device__ __forceinline__ uint32_t word_at(const uint32_t* w) {
+  return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kCandCache = 8192;      // candidates the finish kernel keeps in LDS
+
+__global__ __launch_bounds__(kSelThreads) void indexer_finish_kernel(IndexerParams p) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint64_t ck_s[kCandCache];
+  __shared__ uint32_t cp_s[kCandCache];
+  __shared__ uint32_t ws[kSelThreads / 64];
+  __shared__ uint32_t sh[4];
+  const int tid = threadIdx.x;
+  const int64_t t = blockIdx.x;
+  const int ctx = token_ctx(p, t);
+  int32_t* const out = p.out + t * p.out_st;
+  const int64_t out_base = p.bt ? 0 : p.base[t];
+
+  // the token's histogram, zeroed for the next call
+  uint32_t* const g = p.hist + t * kBins;
+  for (int i = tid; i < kBins; i += kSelThreads) {
+    hist[i] = g[i];
+    g[i] = 0u;
+  }
+  const uint32_t n_c = p.cand_n[t];
+  __syncthreads();
+  if (tid == 0) p.cand_n[t] = 0u;
+  uint32_t need;
+  bool all;
+  threshold_bucket<kSelThreads>(hist, ws, sh, p.topk, need, all);
+
+  // Radix select among the candidates (the keys of bucket b): refine while
+  // the bucket holds more keys than are still needed.  Up to kCandCache
+  // candidates are read once into LDS; more are read from the workspace
+  // in every pass.
+  const uint64_t* const gk = p.cand_key + t * p.key_stride;
+  const uint32_t* const gp = p.cand_pos + t * p.key_stride;
+  const bool cached = n_c <= (uint32_t)kCandCache;
+  if (cached && !all)
+    for (uint32_t i = tid; i < n_c; i += kSelThreads) {
+      ck_s[i] = gk[i];
+      cp_s[i] = gp[i];
+    }
+  __syncthreads();
+  auto cand_key = [&](uint32_t i) -> uint64_t { return cached ? ck_s[i] : gk[i]; };
+  auto cand_pos = [&](uint32_t i) -> uint32_t { return cached ? cp_s[i] : gp[i]; };
+  uint64_t prefix = 0;
+  int pbits = kPrefixBits;
+  uint32_t need_in = 0, cnt = 0;
+  if (!all) {
+    prefix = bucket_prefix(sh[0]);
+    need_in = need - sh[1];
+    cnt = sh[2];
+    while (cnt > need_in && pbits < 64) {
+      const int d = 64 - pbits < kIdxHistBits ? 64 - pbits : kIdxHistBits;
+      for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0u;
+      __syncthreads();
+      for (uint32_t i = tid; i < n_c; i += kSelThreads) {
+        const uint64_t k = cand_key(i);
+        if ((k >> (64 - pbits)) == prefix)
+          atomicAdd(&hist[(uint32_t)(k >> (64 - pbits - d)) & ((1u << d) - 1u)], 1u);
+      }
+      __syncthreads();
+      top_bucket<kSelThreads>(hist, 1 << d, need_in, ws, sh);
+      prefix = (prefix << d) | sh[0];
+      pbits += d;
+      need_in -= sh[1];
+      cnt = sh[2];
+    }
+  }
+  // Keys above the final bucket are in; so is the whole bucket if it holds
+  // exactly the keys still needed; otherwise (all 64 bits equal) its keys
+  // are ties, of which the need_in first in position order are in.
+  const bool ties = !all && cnt > need_in;
+  uint32_t* const sb = p.sel_bits + t * p.word_stride;
+  uint32_t* const tb = p.tie_bits + t * p.word_stride;
+  if (!all) {
+    for (uint32_t i = tid; i < n_c; i += kSelThreads) {
+      const uint64_t k = cand_key(i);
+      const uint64_t top = pbits == 64 ? k : k >> (64 - pbits);
+      const uint32_t pos = cand_pos(i);
+      if (top > prefix || (top == prefix && !ties)) atomicOr(&sb[pos >> 5], 1u << (pos & 31));
+      else if (top == prefix) atomicOr(&tb[pos >> 5], 1u << (pos & 31));
+    }
+  }
+  __threadfence();
+  __syncthreads();
+
+  // Ordered emit: thread i takes words [per i, per (i+1)) of the bitmaps.
+  const int nw = (ctx + 31) >> 5;
+  const int per = (nw + kSelThreads - 1) / kSelThreads;
+  const int w0 = per * tid, w1 = min(w0 + per, nw);
+  uint32_t my_ties = 0;
+  if (ties)
+    for (int w = w0; w < w1; ++w) my_ties += __popc(word_at(&tb[w]));
+  const uint32_t tie_incl = ties ? block_scan<kSelThreads>(my_ties, ws) : 0u;
+  const uint32_t tie_rank0 = tie_incl - my_ties;   // ties in earlier threads' words
+  // word w's selected positions: its selection bits and, of its tie bits,
+  // the lowest (need_in - rank) ones (rank = ties in earlier words)
+  auto selected = [&](int w, uint32_t& rank) -> uint32_t {
+    uint32_t s = word_at(&sb[w]);
+    if (ties) {
+      uint32_t tw = word_at(&tb[w]);
+      uint32_t take = rank < need_in ? need_in - rank : 0u;
+      rank += __popc(tw);
+      while (tw && take) {
+        const uint32_t lo = tw & (0u - tw);
+        s |= lo;
+        tw ^= lo;
+        --take;
+      }
+    }
+    return s;
+  };
+  uint32_t my_sel = 0;
+  {
+    uint32_t rank = tie_rank0;
+    for (int w = w0; w < w1; ++w) my_sel += __popc(selected(w, rank));
+  }
+  const uint32_t sel_incl = block_scan<kSelThreads>(my_sel, ws);
+  {
+    uint32_t o = sel_incl - my_sel, rank = tie_rank0;
+    for (int w = w0; w < w1; ++w) {
+      uint32_t s = selected(w, rank);
+      while (s) {
+        const int bit = __ffs((int)s) - 1;
+        s &= s - 1u;
+        if (o < (uint32_t)p.topk) out[o] = (int32_t)(out_base + 32 * w + bit);
+        ++o;
+      }
+    }
+  }
+  for (int i = (int)need + tid; i < p.topk; i += kSelThreads) out[i] = -1;
+}
+
+namespace {
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+}  // namespace
+
+void indexer_workspace_layout(IndexerParams& p, void* ws, int64_t T, int max_ctx) {
+  char* b = static_cast<char*>(ws);
+  const int64_t ks = (max_ctx + 1) & ~1;
+  const int64_t wsd = (((int64_t)max_ctx + 31) / 32 + 3) & ~(int64_t)3;
+  p.hist = reinterpret_cast<uint32_t*>(b);
+  b += round256((size_t)T * kBins * sizeof(uint32_t));
+  p.cand_n = reinterpret_cast<uint32_t*>(b);
+  b += round256((size_t)T * sizeof(uint32_t));
+  p.keys_ws = reinterpret_cast<uint64_t*>(b);
+  b += round256((size_t)T * ks * sizeof(uint64_t));
+  p.cand_key = reinterpret_cast<uint64_t*>(b);
+  b += round256((size_t)T * ks * sizeof(uint64_t));
+  p.cand_pos = reinterpret_cast<uint32_t*>(b);
+  b += round256((size_t)T * ks * sizeof(uint32_t));
+  p.sel_bits = reinterpret_cast<uint32_t*>(b);
+  b += round256((size_t)T * wsd * sizeof(uint32_t));
+  p.tie_bits = reinterpret_cast<uint32_t*>(b);
+  p.key_stride = ks;
+  p.word_stride = wsd;
+}
+
 size_t indexer_workspace_bytes(int64_t T, int max_ctx) {
-  const size_t hist = ((size_t)T * kBins * sizeof(uint32_t) + 255) & ~(size_t)255;
-  return hist + (size_t)T * (size_t)((max_ctx + 1) & ~1) * sizeof(uint64_t);
+  const int64_t ks = (max_ctx + 1) & ~1;
+  const int64_t wsd = (((int64_t)max_ctx + 31) / 32 + 3) & ~(int64_t)3;
+  return round256((size_t)T * kBins * sizeof(uint32_t)) + round256((size_t)T * sizeof(uint32_t)) +
+         round256((size_t)T * ks * sizeof(uint64_t)) * 2 + round256((size_t)T * ks * sizeof(uint32_t)) +
+         round256((size_t)T * wsd * sizeof(uint32_t)) + (size_t)T * wsd * sizeof(uint32_t);
 }
 
 hipError_t launch_indexer(const IndexerParams& p, hipStream_t stream, const KernelEvents& ev) {
   IndexerParams a = p;
   a.nchunks = (p.max_ctx + kChunk - 1) / kChunk;
+  a.cchunks = (p.max_ctx + kCPos - 1) / kCPos;
   void* args[] = {&a};
   hipError_t e = hipSuccess;
-  // the benchmark events (if any) bracket both kernels: start at the first
-  // kernel's start, stop at the second's end
+  // the benchmark events (if any) bracket all the kernels: start at the
+  // first kernel's start, stop at the last one's end
   if (a.nchunks > 0) {
     e = launch_kernel((const void*)indexer_score_kernel, dim3((unsigned)(p.T * a.nchunks)), dim3(256), args,
                       stream, {ev.start, nullptr});
     if (e != hipSuccess) return e;
   }
-  return launch_kernel((const void*)indexer_select_kernel, dim3((unsigned)p.T), dim3(kSelThreads), args,
-                       stream, {a.nchunks > 0 ? nullptr : ev.start, ev.stop});
+  // Short contexts: one workgroup per token selects over all its keys.
+  // Long ones: many workgroups per token compact the candidates first.
+  // Both give the same lists.
+  if (p.max_ctx <= kShortCtx)
+    return launch_kernel((const void*)indexer_select_kernel, dim3((unsigned)p.T), dim3(kSelThreads), args,
+                         stream, {a.nchunks > 0 ? nullptr : ev.start, ev.stop});
+  e = launch_kernel((const void*)indexer_compact_kernel, dim3((unsigned)(p.T * a.cchunks)), dim3(kCT), args,
+                    stream, {});
+  if (e != hipSuccess) return e;
+  return launch_kernel((const void*)indexer_finish_kernel, dim3((unsigned)p.T), dim3(kSelThreads), args,
+                       stream, {nullptr, ev.stop});
 }
 
 }  // namespace mla

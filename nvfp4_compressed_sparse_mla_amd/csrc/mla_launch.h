@@ -107,9 +107,18 @@ struct IndexerParams {
   int64_t out_st;
   uint64_t* keys_ws;        // [T][key_stride] order-preserving score keys
   uint32_t* hist;           // [T][4096] histogram of the keys' top 12 bits (zero between calls)
-  int nchunks;              // set by launch_indexer
+  uint32_t* cand_n;         // [T] candidates found (zero between calls)
+  uint64_t* cand_key;       // [T][key_stride] keys of the candidates (the k-th best key's bucket)
+  uint32_t* cand_pos;       // [T][key_stride] their positions
+  uint32_t* sel_bits;       // [T][word_stride] positions certainly selected, one bit each
+  uint32_t* tie_bits;       // [T][word_stride] positions whose key equals the k-th best one
+  int64_t word_stride;      // bitmap words per token
+  int nchunks;              // set by launch_indexer: score chunks per token
+  int cchunks;              // set by launch_indexer: compact chunks per token
 };
 size_t indexer_workspace_bytes(int64_t T, int max_ctx);
+// the workspace's parts (the layout indexer_workspace_bytes sizes)
+void indexer_workspace_layout(IndexerParams& p, void* ws, int64_t T, int max_ctx);
 
 // Copies of (layer, block) regions (layout.hip): region l of entry i moves
 // from src + sid * src_block_stride + l * src_layer_stride to the same form

@@ -161,9 +161,14 @@ def test_indexer_rejects_bad_arguments(lib):
     assert call(base=None, bt=fake) == INVALID                          # a table needs token_seq
     assert call(max_ctx=-1) == INVALID
     assert call(ws_bytes=16) == WORKSPACE
+    r = lambda x: (x + 255) // 256 * 256
+
+    def layout(T, max_ctx):   # histograms, candidate counts, keys, candidate keys and positions, two bitmaps
+        ks, wsd = (max_ctx + 1) // 2 * 2, ((max_ctx + 31) // 32 + 3) // 4 * 4
+        return r(T * 4096 * 4) + r(T * 4) + 2 * r(T * ks * 8) + r(T * ks * 4) + r(T * wsd * 4) + T * wsd * 4
     need = lib.mla_indexer_workspace_size(2, 100)
-    assert need == 2 * 4096 * 4 + 2 * 100 * 8
-    assert lib.mla_indexer_workspace_size(3, 101) == ((3 * 4096 * 4 + 255) // 256) * 256 + 3 * 102 * 8
+    assert need == layout(2, 100)
+    assert lib.mla_indexer_workspace_size(3, 101) == layout(3, 101)
 
 
 def test_gather_probe_rejects_bad_arguments(lib):

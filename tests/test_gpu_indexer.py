@@ -103,6 +103,28 @@ def test_workspace_reuse_and_determinism():
     hist_bytes = 6 * 4096 * 4
     torch.cuda.synchronize()
     assert torch.all(ws[:hist_bytes] == 0)              # the histograms are left at zero
+    assert torch.all(ws[hist_bytes:hist_bytes + 6 * 4] == 0)   # and so are the candidate counts
+
+
+def test_long_contexts_of_equal_scores():
+    """100K positions whose keys are all one row: every score ties, so the
+    list is the first topk positions; several bitmap words per thread of the
+    ordered emit, tie ranks running across threads.  A second token mixes
+    two distinct keys, so its threshold falls inside a run of ties."""
+    one = fp8_values((2, 128), 11, 0, DEV)
+    n = 100_000
+    keys = one[torch.zeros(n, dtype=torch.long, device=DEV)].contiguous()
+    keys[::3] = one[1]
+    q = fp8_values((3, 128), 11, 1, DEV)
+    ctx = torch.tensor([n, n, 70_001], dtype=torch.int32, device=DEV)
+    base = torch.zeros(3, dtype=torch.int64, device=DEV)
+    same = keys.clone()
+    same[:] = one[0]
+    for kk in (same, keys):
+        for topk in (2048, 777):
+            out = mla.indexer_topk(q, kk, ctx, topk, n, key_base=base)
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy(), _oracle(q, kk, ctx, topk, base=base)), topk
 
 
 def test_decode15_full_size_every_token():
