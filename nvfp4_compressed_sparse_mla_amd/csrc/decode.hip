@@ -79,6 +79,8 @@ constexpr int kSW = 4;                // score waves
 constexpr int kVW = 4;                // value waves
 constexpr int kWaves = kSW + kVW;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kSlices = kMaxTopk / (64 * kSW);   // index-list slots per score-wave thread
+static_assert(kSlices * 64 * kSW == kMaxTopk, "index slots per score-wave thread");
 constexpr int kVCols = kLatent / kVW; // output columns per value wave
 // FP16 elements per V-buffer row: a 1072-byte stride puts the 16 rows one
 // row-wise 16-byte write instruction touches in distinct banks
@@ -421,10 +423,21 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   __shared__ __align__(16) float wm_s[kSW][kHG];            // per score wave: final reference (base 2)
   __shared__ __align__(16) float wl_s[kSW][kHG];            // per score wave: row sums
   __shared__ __align__(16) float fac_s[kVW][kHG];           // per value wave: per-head factors
-  __shared__ int cnt_s[4][kWaves];
+  __shared__ __align__(16) int cnt_s[kSlices][kVW];   // valid slots per (slice, value wave)
   __shared__ int last_s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Every kernel argument the prologue uses, in registers before anything
+  // else: left to the compiler, each group would be loaded at its first use,
+  // one dependent scalar round trip after another ahead of the index ->
+  // block table -> row chain.  One statement, whose outputs (S, G and the
+  // XCD shift) the block index arithmetic takes, so that nothing is
+  // scheduled between the loads and their single wait.
+  int S = p.S, G = p.G, xsh_arg = p.xcd_shift;
+  MLA_DEVICE_ASM("" : "+s"(S), "+s"(G), "+s"(xsh_arg)
+                 : "s"(p.q), "s"(p.q_st), "s"(p.q_sh), "s"(p.T), "s"(p.H), "s"(p.cache), "s"(p.cache_rows),
+                   "s"(p.idx), "s"(p.topk), "s"(p.idx_st), "s"(p.q_neg), "s"(p.bt), "s"(p.bs), "s"(p.bt_rows),
+                   "s"(p.bt_cols), "s"(p.bs_log2), "s"(p.bt_st), "s"(p.tok_seq));
   // Block index arithmetic in 32 bits (a 64-bit division is a long chain
   // of dependent scalar instructions ahead of the first memory access).
   // Workgroups are dealt to the 8 XCDs in turn (workgroup b runs on XCD
@@ -433,8 +446,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   // merging split reads the others' partials (and all read the same q and
   // index list) through one L2; the grid is then rounded up to a multiple
   // of 8 S.  With xcd_shift = 0 split s of unit k is workgroup S k + s.
-  const int S = p.S, G = p.G;
-  const uint32_t xsh = (uint32_t)p.xcd_shift;
+  const uint32_t xsh = (uint32_t)xsh_arg;
   const uint32_t slot = blockIdx.x >> xsh, kx = slot / (uint32_t)S;
   const int s = (int)(slot - kx * (uint32_t)S);
   const uint32_t tg32 = (kx << xsh) + (blockIdx.x & ((1u << xsh) - 1u));
@@ -444,112 +456,23 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   const int64_t tg = tg32, t = t32;
   const int r16 = lane & 15, kg = lane >> 4;
 
-  // ------------------------------------------------ compact the valid rows
-  // All index loads are issued before any is used, then all block-table
-  // loads: two dependent memory round trips (addresses of slots past topk
-  // or of masked entries are clamped to valid ones and the result dropped).
-  // The index loads head the longest dependent chain (index -> block table
-  // -> row DMA), so they are issued first; q's loads follow while they are
-  // in flight, then the block-table loads.
-  int v4[4];
-  {
-    const int32_t* ip = p.idx + t * p.idx_st;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sl = i * kThreads + tid;
-      v4[i] = ip[sl < p.topk ? sl : p.topk - 1];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (i * kThreads + tid >= p.topk) v4[i] = -1;
-  }
-  // ---------------------------------------------------------------- q
-  // q of the workgroup's 32 heads: 2304 coalesced 16-byte chunks (chunk c:
-  // head c / 72, dimensions 8 (c % 72) + [0,8); heads past H repeat the last
-  // one), 4 or 5 per thread, later staged through the still idle V buffer,
-  // from where each score wave reads the B operands of its score MFMAs.
-  constexpr int kQChunkAll = kHG * (kQK / 8);               // 2304
-  constexpr int kQChunks = (kQChunkAll + kThreads - 1) / kThreads;   // 5
-  u32x4 qstage[kQChunks];     // raw fp16 / bf16 bits
-  {
-    const uint16_t* qt = reinterpret_cast<const uint16_t*>(p.q) + t * p.q_st;
-#pragma unroll
-    for (int m = 0; m < kQChunks; ++m) {
-      const int c = tid + kThreads * m;
-      if (c < kQChunkAll) {
-        const int h = c / (kQK / 8), dc = c - h * (kQK / 8);
-        const int head = min(g * kHG + h, p.H - 1);
-        qstage[m] = *reinterpret_cast<const u32x4*>(qt + (int64_t)head * p.q_sh + 8 * dc);
-      }
-    }
-  }
-
-  int b4[4], pb4[4];
-  bool seq_ok = true;
-  if (p.bt) {
-    const int64_t seq = p.tok_seq[t];
-    seq_ok = seq >= 0 && seq < p.bt_rows;
-    const int32_t* btr = p.bt + (seq_ok ? seq : 0) * p.bt_st;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // (a power-of-two block size, the usual case, divides by a shift)
-      const int v = v4[i] >= 0 ? v4[i] : 0;
-      b4[i] = p.bs_log2 >= 0 ? v >> p.bs_log2 : v / p.bs;
-      pb4[i] = btr[b4[i] < p.bt_cols ? b4[i] : p.bt_cols - 1];
-    }
-  }
-
-  int rows4[4], pre4[4];
-  {
-    if (p.bt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int r = -1;
-        if (seq_ok && v4[i] >= 0 && b4[i] < p.bt_cols && pb4[i] >= 0) {
-          const int64_t pr = (int64_t)pb4[i] * p.bs + (v4[i] - b4[i] * p.bs);
-          r = pr < p.cache_rows ? (int)pr : -1;
-        }
-        rows4[i] = r;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rows4[i] = (v4[i] >= 0 && v4[i] < p.cache_rows) ? v4[i] : -1;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint64_t m = __ballot(rows4[i] >= 0);
-      pre4[i] = __popcll(m & ((1ull << lane) - 1ull));
-      if (lane == 0) cnt_s[i][wave] = __popcll(m);
-    }
-  }
-  lds_barrier();
-  int total = 0;
-  {
-    int base[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      base[i] = total;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        if (w < wave) base[i] += cnt_s[i][w];
-        total += cnt_s[i][w];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (rows4[i] >= 0) phys[base[i] + pre4[i]] = rows4[i];
-  }
-  lds_barrier();
-
-  // (total <= 2048 and S <= 64: the products fit in 32 bits)
-  const int r0 = S == 1 ? 0 : (int)((uint32_t)(total * s) / (uint32_t)S);
-  const int n = (S == 1 ? total : (int)((uint32_t)(total * (s + 1)) / (uint32_t)S)) - r0;
-  const int ntiles = (n + kRowsT - 1) / kRowsT;
-  const int rounds = (ntiles + kSW - 1) / kSW;
-
-  // ---------------------------------------------------------------- score-wave state
+  // ---------------------------------------------------------------- prologue
+  // The longest chain of the prologue is index list -> block table -> row
+  // DMA; everything else is arranged around it.
+  //  * Score waves: while every slot of the list names a row, the compacted
+  //    row list is the slot list itself, so each lane loads the index and
+  //    block-table entries of its own rows of the first kDepth tiles and
+  //    issues their DMA at once ("speculative" first tiles).  A wave does so
+  //    only if those rows and the list's last slot are valid (a list padded
+  //    at its end does not speculate); if the compaction then finds masked
+  //    slots, the wave waits for that DMA and issues the tiles again from the
+  //    compacted list.
+  //  * Value waves: compact the valid rows of the whole list (slot
+  //    i * 256 + v of value-wave thread v), and stage q in LDS.
+  // Loads and their uses stay inside each role's branch: loads left in flight
+  // past it would, for the compiler, also be in flight on the other role's
+  // path.
   const int sw = wave;        // (score waves only)
-  const int my_tiles = wave < kSW && ntiles > sw ? (ntiles - sw + kSW - 1) / kSW : 0;
   uint8_t* const ring = ring_all + (wave < kSW ? wave : 0) * kWaveRing;
 
   // DMA of one tile into ring slot `sl` (row-interleaved layout above):
@@ -572,6 +495,210 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     static_for<0, kInstr>(one);
   };
   auto issue = [&](uint32_t row, int sl) { issue_from(p.cache + (uint64_t)row * kRB, sl); };
+  // missing tiles re-read a valid row (or q, with an empty cache) into slots
+  // that are never read
+  const uint8_t* const spare = p.cache_rows > 0 ? p.cache : static_cast<const uint8_t*>(p.q);
+
+  const int32_t* const ip = p.idx + t * p.idx_st;
+  // the token's block-table row number (from the index list itself when
+  // there is no table, so that the load needs no branch)
+  const int32_t* const seq_p = p.bt ? p.tok_seq + t : ip;
+
+  int rows8[kSlices], pre8[kSlices];   // (value waves)
+  bool spec = false;                   // (score waves) first tiles issued before the compaction
+  if (wave < kSW) {
+    const int topk = p.topk;
+    const int r0s = S == 1 ? 0 : (int)((uint32_t)(topk * s) / (uint32_t)S);
+    const int ns = (S == 1 ? topk : (int)((uint32_t)(topk * (s + 1)) / (uint32_t)S)) - r0s;
+    const int nts = (ns + kRowsT - 1) / kRowsT;
+    const int myts = nts > sw ? (nts - sw + kSW - 1) / kSW : 0;
+    const int seq_raw = *seq_p;
+    const int last = ip[topk - 1];
+    int vs[kDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) {
+      const int e = min((sw + kSW * i) * kRowsT + r16, ns - 1);
+      vs[i] = ip[r0s + (e > 0 ? e : 0)];   // (r0s < topk for every split)
+    }
+    MLA_DEVICE_ASM("" :: "v"(seq_raw));   // (loaded with the index entries, not sunk behind them)
+    int rs[kDepth];
+    if (p.bt) {
+      const bool seq_ok = seq_raw >= 0 && seq_raw < p.bt_rows;
+      const int32_t* btr = p.bt + (int64_t)(seq_ok ? seq_raw : 0) * p.bt_st;
+      int bs[kDepth], pbs[kDepth];
+#pragma unroll
+      for (int i = 0; i < kDepth; ++i) {
+        const int v = vs[i] >= 0 ? vs[i] : 0;
+        bs[i] = p.bs_log2 >= 0 ? v >> p.bs_log2 : v / p.bs;
+        pbs[i] = btr[bs[i] < p.bt_cols ? bs[i] : p.bt_cols - 1];
+      }
+#pragma unroll
+      for (int i = 0; i < kDepth; ++i) {
+        int r = -1;
+        if (seq_ok && vs[i] >= 0 && bs[i] < p.bt_cols && pbs[i] >= 0) {
+          const int64_t pr = (int64_t)pbs[i] * p.bs + (vs[i] - bs[i] * p.bs);
+          r = pr < p.cache_rows ? (int)pr : -1;
+        }
+        rs[i] = r;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kDepth; ++i) rs[i] = (vs[i] >= 0 && vs[i] < p.cache_rows) ? vs[i] : -1;
+    }
+    // Every load of this branch is complete here.  An explicit wait: the
+    // compiler's own waits, placed per use inside lane-masked blocks, leave
+    // loads in flight in its model, and where their registers are reused
+    // after the branch it would wait for all vector memory, the DMA included.
+    wait_vmcnt<0>();
+    bool ok = last >= 0;
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i)
+      if (myts > i && rs[i] < 0) ok = false;
+    spec = __ballot(!ok) == 0;
+    // P0: the DMA is issued only once the value waves have issued all their
+    // prologue loads, which would otherwise queue behind it
+    lds_barrier();
+    if (spec) {
+      static_for<0, kDepth>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        issue_from(myts > i ? p.cache + (uint64_t)(uint32_t)rs[i] * kRB : spare, i);
+      });
+    }
+  } else {
+    constexpr int kVT = kVW * 64;                               // 256 threads
+    const int vt = tid - kSW * 64;
+    int v8[kSlices];
+    const int seq_raw = *seq_p;
+#pragma unroll
+    for (int i = 0; i < kSlices; ++i) {
+      const int sl = i * kVT + vt;
+      v8[i] = ip[sl < p.topk ? sl : p.topk - 1];
+    }
+    MLA_DEVICE_ASM("" :: "v"(seq_raw));   // (loaded with the index entries, not sunk behind them)
+    // q of the workgroup's 32 heads: 2304 coalesced 16-byte chunks (chunk c:
+    // head c / 72, dimensions 8 (c % 72) + [0,8); heads past H repeat the
+    // last one), 9 per thread, loaded now (any later, the loads would queue
+    // behind the first tiles' DMA) and staged in the still idle V buffer
+    // below.
+    constexpr int kQChunkAll = kHG * (kQK / 8);               // 2304
+    constexpr int kQChunks = kQChunkAll / kVT;                // 9
+    static_assert(kQChunks * kVT == kQChunkAll, "q chunks per value-wave thread");
+    u32x4 qstage[kQChunks];     // raw fp16 / bf16 bits
+    {
+      const uint16_t* qt = reinterpret_cast<const uint16_t*>(p.q) + t * p.q_st;
+#pragma unroll
+      for (int m = 0; m < kQChunks; ++m) {
+        const int c = vt + kVT * m;
+        const int h = c / (kQK / 8), dc = c - h * (kQK / 8);
+        const int head = min(g * kHG + h, p.H - 1);
+        qstage[m] = *reinterpret_cast<const u32x4*>(qt + (int64_t)head * p.q_sh + 8 * dc);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kSlices; ++i)
+      if (i * kVT + vt >= p.topk) v8[i] = -1;
+
+    int b8[kSlices], pb8[kSlices];
+    const bool seq_ok = seq_raw >= 0 && seq_raw < p.bt_rows;
+    if (p.bt) {
+      const int32_t* btr = p.bt + (int64_t)(seq_ok ? seq_raw : 0) * p.bt_st;
+      // (a power-of-two block size, the usual case, divides by a shift; one
+      // uniform branch for all slots)
+      if (p.bs_log2 >= 0) {
+#pragma unroll
+        for (int i = 0; i < kSlices; ++i) b8[i] = (v8[i] >= 0 ? v8[i] : 0) >> p.bs_log2;
+      } else {
+#pragma unroll
+        for (int i = 0; i < kSlices; ++i) b8[i] = (v8[i] >= 0 ? v8[i] : 0) / p.bs;
+      }
+#pragma unroll
+      for (int i = 0; i < kSlices; ++i) pb8[i] = btr[b8[i] < p.bt_cols ? b8[i] : p.bt_cols - 1];
+    }
+    lds_barrier();   // P0: this wave's prologue loads are issued (the score waves' DMA follows them)
+    if (p.bt) {
+#pragma unroll
+      for (int i = 0; i < kSlices; ++i) {
+        int r = -1;
+        if (seq_ok && v8[i] >= 0 && b8[i] < p.bt_cols && pb8[i] >= 0) {
+          const int64_t pr = (int64_t)pb8[i] * p.bs + (v8[i] - b8[i] * p.bs);
+          r = pr < p.cache_rows ? (int)pr : -1;
+        }
+        rows8[i] = r;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kSlices; ++i) rows8[i] = (v8[i] >= 0 && v8[i] < p.cache_rows) ? v8[i] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kSlices; ++i) {
+      const uint64_t m = __ballot(rows8[i] >= 0);
+      pre8[i] = __popcll(m & ((1ull << lane) - 1ull));
+      if (lane == 0) cnt_s[i][wave - kSW] = __popcll(m);
+    }
+    // q into LDS in B-operand order, for the score waves' registers.  B
+    // operand of K-step ks for head block hb, lane (r16, kg): q[hb*16 +
+    // r16][d] with d(ks < 16) = 128kg + 8ks + [0,8) and d(16 + i) = 512 +
+    // 16kg + 8i + [0,8), at 16-byte slot (hb * 18 + ks) * 64 + 16kg + r16.  A
+    // negative softmax scale flips q's signs here (exact), so sm_log2 >= 0.
+    const uint32_t qs = lds_off(vbuf_all);
+#pragma unroll
+    for (int m = 0; m < kQChunks; ++m) {
+      const int c = vt + kVT * m;
+      const int h = c / (kQK / 8), d = 8 * (c - h * (kQK / 8));
+      int kgq, ks;
+      if (d < kLatent) {
+        kgq = d >> 7;
+        ks = (d >> 3) & 15;
+      } else {
+        kgq = (d - kLatent) >> 4;
+        ks = 16 + (((d - kLatent) >> 3) & 1);
+      }
+      u32x4 u = q8_operand<kBf16>(qstage[m]);
+      if (p.q_neg) u ^= 0x80008000u;
+      const uint32_t a = qs + 16 * (((h >> 4) * kKSteps + ks) * 64 + 16 * kgq + (h & 15));
+      MLA_DEVICE_ASM("ds_write_b128 %0, %1" :: "v"(a), "v"(u) : "memory");
+    }
+    wait_vmcnt<0>();   // (as in the score waves' branch)
+  }
+  lds_barrier();   // the slices' counts and the staged q are in LDS
+  // Valid rows in slot order: slice i of value wave w starts after all of
+  // slices 0 .. i-1 and slice i of value waves 0 .. w-1.  The counts are read
+  // in assembly: the compiler cannot tell these reads from the speculative
+  // DMA's LDS writes and would wait for that DMA first.
+  int total = 0;
+  {
+    static_assert(kSlices == 8 && kVW == 4, "count reads below");
+    u32x4 c[kSlices];
+    MLA_DEVICE_ASM("ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:16\n\tds_read_b128 %2, %8 offset:32\n\t"
+                   "ds_read_b128 %3, %8 offset:48\n\tds_read_b128 %4, %8 offset:64\n\tds_read_b128 %5, %8 offset:80\n\t"
+                   "ds_read_b128 %6, %8 offset:96\n\tds_read_b128 %7, %8 offset:112\n\ts_waitcnt lgkmcnt(0)"
+                   : "=v"(c[0]), "=v"(c[1]), "=v"(c[2]), "=v"(c[3]), "=v"(c[4]), "=v"(c[5]), "=v"(c[6]), "=v"(c[7])
+                   : "v"(lds_off(&cnt_s[0][0])));
+    int base[kSlices];
+#pragma unroll
+    for (int i = 0; i < kSlices; ++i) {
+      base[i] = total;
+#pragma unroll
+      for (int w = 0; w < kVW; ++w) {
+        if (w + kSW < wave) base[i] += (int)c[i][w];
+        total += (int)c[i][w];
+      }
+    }
+    if (wave >= kSW) {
+#pragma unroll
+      for (int i = 0; i < kSlices; ++i)
+        if (rows8[i] >= 0) phys[base[i] + pre8[i]] = rows8[i];
+    }
+  }
+  lds_barrier();
+
+  // (total <= 2048 and S <= 64: the products fit in 32 bits)
+  const int r0 = S == 1 ? 0 : (int)((uint32_t)(total * s) / (uint32_t)S);
+  const int n = (S == 1 ? total : (int)((uint32_t)(total * (s + 1)) / (uint32_t)S)) - r0;
+  const int ntiles = (n + kRowsT - 1) / kRowsT;
+  const int rounds = (ntiles + kSW - 1) / kSW;
+  const int my_tiles = wave < kSW && ntiles > sw ? (ntiles - sw + kSW - 1) / kSW : 0;
+
   // LDS address of the cache row of this lane's DMA row in the wave's i-th tile
   auto tile_row_addr = [&](int i) -> uint32_t {
     int e = (sw + kSW * i) * kRowsT + r16;
@@ -579,51 +706,18 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     return lds_off(&phys[r0 + e]);
   };
 
-  // The first kDepth tiles' DMA (score waves).  Missing tiles re-read a
-  // valid row (or q, with an empty cache) into slots that are never read.  q's
-  // loads (issued before the compaction) are complete by now; waiting for
-  // them here, where nothing else is in flight, keeps the compiler from
-  // waiting for the tiles' DMA before q is staged.
-  wait_vmcnt<0>();
-  if (wave < kSW) {
-    const uint8_t* const spare = p.cache_rows > 0 ? p.cache : static_cast<const uint8_t*>(p.q);
+  // The first kDepth tiles' DMA from the compacted list, unless the
+  // speculative DMA already holds them (every slot named a row: then the
+  // compacted list is the slot list and r0, n are the speculated ones).  A
+  // speculative DMA into the same slots completes first.
+  if (wave < kSW && !(spec && total == p.topk)) {
+    if (spec) wait_vmcnt<0>();
     static_for<0, kDepth>([&](auto I) {
       constexpr int i = decltype(I)::value;
       const uint8_t* b = spare;
       if (my_tiles > i) b = p.cache + (uint64_t)(uint32_t)phys[r0 + min((sw + kSW * i) * kRowsT + r16, n - 1)] * kRB;
       issue_from(b, i);
     });
-  }
-  // q into LDS in B-operand order, then into the score waves' registers
-  // (while the first tiles' DMA is in flight).  B operand of K-step ks for
-  // head block hb, lane (r16, kg): q[hb*16 + r16][d] with d(ks < 16) =
-  // 128kg + 8ks + [0,8) and d(16 + i) = 512 + 16kg + 8i + [0,8), at 16-byte
-  // slot (hb * 18 + ks) * 64 + 16kg + r16.  A negative softmax scale flips
-  // q's signs here (exact), so sm_log2 >= 0.
-  {
-    // LDS accesses in assembly: the compiler would make them wait for the
-    // tiles' DMA (it cannot tell the staging area from the ring)
-    const uint32_t qs = lds_off(vbuf_all);
-#pragma unroll
-    for (int m = 0; m < kQChunks; ++m) {
-      const int c = tid + kThreads * m;
-      if (c < kQChunkAll) {
-        const int h = c / (kQK / 8), d = 8 * (c - h * (kQK / 8));
-        int kgq, ks;
-        if (d < kLatent) {
-          kgq = d >> 7;
-          ks = (d >> 3) & 15;
-        } else {
-          kgq = (d - kLatent) >> 4;
-          ks = 16 + (((d - kLatent) >> 3) & 1);
-        }
-        u32x4 u = q8_operand<kBf16>(qstage[m]);
-        if (p.q_neg) u ^= 0x80008000u;
-        const uint32_t a = qs + 16 * (((h >> 4) * kKSteps + ks) * 64 + 16 * kgq + (h & 15));
-        MLA_DEVICE_ASM("ds_write_b128 %0, %1" :: "v"(a), "v"(u) : "memory");
-      }
-    }
-    lds_barrier();   // (not __syncthreads: that would also wait for the tiles' DMA)
   }
 
   const float sm = p.sm_log2;
