@@ -411,6 +411,13 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   constexpr int kInstr = dma_instr(kFmt);
   constexpr int kSlot = slot_bytes(kFmt);
   constexpr int kDepth = ring_depth(kFmt);
+  // NVFP4 rows: the value waves issue the ring refills (value wave j for
+  // score wave j's slot, right after the score wave has read it), which
+  // keeps the DMA issue off the score waves' path to the next barrier.
+  // FP8 rows keep the score waves' own refills (their two-slot ring leaves
+  // a refill issued one round later too little time).
+  constexpr bool kVRefill = kFmt == kFmtNvfp4;
+  static_assert(!kVRefill || kDepth == 3, "value-wave refills assume a three-slot ring");
 
   // The DMA target, the V buffer and the P buffer are separate arrays so
   // that the compiler can tell their accesses from the DMA's writes.  After
@@ -482,9 +489,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   // split's last row.  NVFP4 rows have 22 pieces: in the last instruction
   // lanes 32..63 (pieces 22, 23) repeat pieces 20 and 21 of their row into
   // positions that are never read.
-  auto issue_from = [&](const uint8_t* row_base, int sl) {
+  auto dma_tile = [&](const uint8_t* row_base, uint8_t* const dst) {
     const uint8_t* const a = row_base + 16 * kg;
-    uint8_t* const dst = ring + sl * kSlot;
     // instruction j: source a + 64j, LDS dst + 1024j (the immediate 64j
     // applies to both)
     auto one = [&](auto J) {
@@ -494,6 +500,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     };
     static_for<0, kInstr>(one);
   };
+  auto issue_from = [&](const uint8_t* row_base, int sl) { dma_tile(row_base, ring + sl * kSlot); };
   auto issue = [&](uint32_t row, int sl) { issue_from(p.cache + (uint64_t)row * kRB, sl); };
   // missing tiles re-read a valid row (or q, with an empty cache) into slots
   // that are never read
@@ -760,15 +767,25 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
       if (have) {
         // wait for this tile's DMA (the later tiles' stays in flight: a
         // wave's vector memory operations complete in issue order), read
-        // its rows, then refill its slot with tile i + kDepth
-        const int later = my_tiles - 1 - i;   // tiles issued after this one
-        if (kDepth > 2 && later >= 2) wait_vmcnt<(kDepth > 2 ? 2 : 0) * kInstr>();
-        else if (later >= 1) wait_vmcnt<kInstr>();
-        else wait_vmcnt<0>();
+        // its rows, then (FP8 rows) refill its slot with tile i + kDepth.
+        // With value-wave refills, tiles 0 .. kDepth-1 come from this wave's
+        // prologue DMA (always kDepth tiles, spare ones included) and later
+        // ones are complete before the barrier that ended the last round.
+        if constexpr (kVRefill) {
+          if (i == 0) wait_vmcnt<(kDepth - 1) * kInstr>();
+          else if (i == 1 && kDepth > 2) wait_vmcnt<(kDepth > 2 ? kDepth - 2 : 0) * kInstr>();
+          else if (i < kDepth) wait_vmcnt<0>();
+        } else {
+          const int later = my_tiles - 1 - i;   // tiles issued after this one
+          if (kDepth > 2 && later >= 2) wait_vmcnt<(kDepth > 2 ? 2 : 0) * kInstr>();
+          else if (later >= 1) wait_vmcnt<kInstr>();
+          else wait_vmcnt<0>();
+        }
         const uint32_t sl = lds_off(ring + (i % kDepth) * kSlot);
         uint32_t next_row = lds_b32(tile_row_addr(i + kDepth));
         ring_read<kFmt>(raw, sl, ro, next_row);
-        if (i + kDepth < my_tiles) issue(next_row, i % kDepth);
+        if constexpr (!kVRefill)
+          if (i + kDepth < my_tiles) issue(next_row, i % kDepth);
         // rope first: its scores need no V-buffer space
 #pragma unroll
         for (int ks = 16; ks < kKSteps; ++ks)
@@ -898,8 +915,30 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
         for (int e = 0; e < 4; ++e) f[4 * q + e] = __uint_as_float(v[e]);
       });
     };
+    // Refill R(m) (value-wave refills): tile j + kSW (m + kDepth) of score
+    // wave j into its slot m % kDepth, issued right after A(m) (the score
+    // wave read that slot in round m); the score wave reads it in round
+    // m + kDepth, after A(m + kDepth - 1), before which this wave waits for it.
+    const int mt_j = ntiles > j ? (ntiles - j + kSW - 1) / kSW : 0;   // score wave j's tiles
+    uint8_t* const ring_j = ring_all + j * kWaveRing;
+    auto refill_row_addr = [&](int m) -> uint32_t {
+      const int e = (j + kSW * (m + kDepth)) * kRowsT + r16;
+      return lds_off(&phys[r0 + (e < n ? e : n - 1)]);
+    };
     for (int i = 0; i < rounds; ++i) {
       const int nt = ntiles - kSW * i < kSW ? ntiles - kSW * i : kSW;   // tiles in this round
+      uint32_t refill_row = 0;
+      if constexpr (kVRefill) {
+        // R(i - 2) complete before A(i) (R(i - 1) may stay in flight)
+        if (i >= 2) {
+          if (i - 1 + kDepth < mt_j) wait_vmcnt<kInstr>();
+          else wait_vmcnt<0>();
+        }
+        if (i + kDepth < mt_j) {
+          refill_row = lds_b32(refill_row_addr(i));
+          MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(refill_row));
+        }
+      }
       lds_barrier();   // A(i)
       half8_t pa[kSW];
       float mr[kSW];
@@ -911,6 +950,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
         read_v_tile<w>(bv[w], vb);
       });
       lds_barrier();   // B(i): waits for this wave's reads, then releases the buffers
+      // (issued after B(i), in this wave's slack before A(i + 1))
+      if constexpr (kVRefill)
+        if (i + kDepth < mt_j) dma_tile(p.cache + (uint64_t)refill_row * kRB, ring_j + (i % kDepth) * kSlot);
 #pragma unroll
       for (int w = 0; w < kSW; ++w)
         MLA_DEVICE_ASM("" : "+v"(pa[w]), "+v"(mr[w]), "+v"(bv[w][0]), "+v"(bv[w][1]), "+v"(bv[w][2]), "+v"(bv[w][3]));
@@ -921,7 +963,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
         if (w < nt) mx = __builtin_fmaxf(mx, mr[w]);
       if (__ballot(mx > M) != 0) {
         const float f = mx > M ? (M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - mx)) : 1.0f;
-        if (lane < 32) *reinterpret_cast<float*>(&fac_s[j][hl]) = f;
+        // (an assembly store: the compiler would make a plain LDS store wait
+        // for this wave's refill DMA)
+        if (lane < 32) MLA_DEVICE_ASM("ds_write_b32 %0, %1" :: "v"(fac_w), "v"(f) : "memory");
         float fo[16];
         read_factors(fo);
 #pragma unroll
@@ -943,7 +987,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
         }
       });
     }
-    (void)fac_w;
+    wait_vmcnt<0>();   // no refill DMA may still be writing this workgroup's LDS
     lds_barrier();   // E
     // weight of head h: 1 / L with L = sum_w 2^(m_w - M) l_w over the score
     // waves (whose references are all <= M); log2-sum-exp = M + log2 L
