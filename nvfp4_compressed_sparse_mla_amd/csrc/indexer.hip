@@ -393,7 +393,7 @@ __device__ __forceinline__ void threshold_bucket(const uint32_t* hist, uint32_t*
 }
 
 __global__ __launch_bounds__(kCT) void indexer_compact_kernel(IndexerParams p) {
-  __shared__ uint32_t hist[kBins];
+  __shared__ __align__(16) uint32_t hist[kBins];
   __shared__ uint32_t ws[kCT / 64];
   __shared__ uint32_t sh[4];
   __shared__ uint32_t base_s;
@@ -411,8 +411,18 @@ __global__ __launch_bounds__(kCT) void indexer_compact_kernel(IndexerParams p) {
   const uint64_t* const keys = p.keys_ws + t * p.key_stride;
   uint64_t k[32];
   load_keys<32>(keys, pp, ctx, k);
-  const uint32_t* const g = p.hist + t * kBins;
-  for (int i = tid; i < kBins; i += kCT) hist[i] = g[i];
+  // the token's histogram: 16-byte loads, all issued before any is used
+  // (one at a time, each would be a dependent round trip to memory)
+  {
+    constexpr int kPer = kBins / (4 * kCT);
+    static_assert(kPer * 4 * kCT == kBins, "histogram words per thread");
+    const u32x4* const g = reinterpret_cast<const u32x4*>(p.hist + t * kBins);
+    u32x4 hv[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) hv[j] = g[tid + kCT * j];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) reinterpret_cast<u32x4*>(hist)[tid + kCT * j] = hv[j];
+  }
   __syncthreads();
   uint32_t need;
   bool all;
@@ -457,10 +467,11 @@ __device__ __forceinline__ uint32_t word_at(const uint32_t* w) {
   return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-constexpr int kCandCache = 8192;      // candidates the finish kernel keeps in LDS
+constexpr int kCandCache = 11776;     // candidates the finish kernel keeps in LDS (with the histogram, < 160 KB)
+constexpr int kEmitWords = 8;         // bitmap words per thread held in registers by the ordered emit
 
 __global__ __launch_bounds__(kSelThreads) void indexer_finish_kernel(IndexerParams p) {
-  __shared__ uint32_t hist[kBins];
+  __shared__ __align__(16) uint32_t hist[kBins];
   __shared__ uint64_t ck_s[kCandCache];
   __shared__ uint32_t cp_s[kCandCache];
   __shared__ uint32_t ws[kSelThreads / 64];
@@ -471,11 +482,15 @@ __global__ __launch_bounds__(kSelThreads) void indexer_finish_kernel(IndexerPara
   int32_t* const out = p.out + t * p.out_st;
   const int64_t out_base = p.bt ? 0 : p.base[t];
 
-  // the token's histogram, zeroed for the next call
-  uint32_t* const g = p.hist + t * kBins;
-  for (int i = tid; i < kBins; i += kSelThreads) {
-    hist[i] = g[i];
-    g[i] = 0u;
+  // The token's histogram (one 16-byte load per thread), zeroed for the
+  // next call.  Every global read of this kernel is issued in batches:
+  // one at a time, each would be a dependent round trip to memory.
+  static_assert(kBins == 4 * kSelThreads, "histogram words per thread");
+  {
+    u32x4* const g = reinterpret_cast<u32x4*>(p.hist + t * kBins);
+    const u32x4 h = g[tid];
+    g[tid] = (u32x4){0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4*>(hist)[tid] = h;
   }
   const uint32_t n_c = p.cand_n[t];
   __syncthreads();
@@ -491,14 +506,50 @@ __global__ __launch_bounds__(kSelThreads) void indexer_finish_kernel(IndexerPara
   const uint64_t* const gk = p.cand_key + t * p.key_stride;
   const uint32_t* const gp = p.cand_pos + t * p.key_stride;
   const bool cached = n_c <= (uint32_t)kCandCache;
+  constexpr int kU = 8;                 // candidates per thread per batch
+  // (indices past the list are clamped to its last entry, so that every
+  // load of a batch is issued unconditionally; their results are dropped)
+  auto cand_index = [&](uint32_t i) -> uint32_t { return i < n_c ? i : n_c - 1u; };
   if (cached && !all)
-    for (uint32_t i = tid; i < n_c; i += kSelThreads) {
-      ck_s[i] = gk[i];
-      cp_s[i] = gp[i];
+    for (uint32_t i0 = 0; i0 < n_c; i0 += kU * kSelThreads) {
+      uint64_t kk[kU];
+      uint32_t pp[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const uint32_t i = cand_index(i0 + u * kSelThreads + tid);
+        kk[u] = gk[i];
+        pp[u] = gp[i];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const uint32_t i = i0 + u * kSelThreads + tid;
+        if (i < n_c) {
+          ck_s[i] = kk[u];
+          cp_s[i] = pp[u];
+        }
+      }
     }
   __syncthreads();
-  auto cand_key = [&](uint32_t i) -> uint64_t { return cached ? ck_s[i] : gk[i]; };
-  auto cand_pos = [&](uint32_t i) -> uint32_t { return cached ? cp_s[i] : gp[i]; };
+  // f(key, position) for every candidate, in batches
+  auto for_candidates = [&](auto&& f) {
+    if (cached) {
+      for (uint32_t i = tid; i < n_c; i += kSelThreads) f(ck_s[i], cp_s[i]);
+    } else {
+      for (uint32_t i0 = 0; i0 < n_c; i0 += kU * kSelThreads) {
+        uint64_t kk[kU];
+        uint32_t pp[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const uint32_t i = cand_index(i0 + u * kSelThreads + tid);
+          kk[u] = gk[i];
+          pp[u] = gp[i];
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          if (i0 + u * kSelThreads + tid < n_c) f(kk[u], pp[u]);
+      }
+    }
+  };
   uint64_t prefix = 0;
   int pbits = kPrefixBits;
   uint32_t need_in = 0, cnt = 0;
@@ -510,11 +561,10 @@ __global__ __launch_bounds__(kSelThreads) void indexer_finish_kernel(IndexerPara
       const int d = 64 - pbits < kIdxHistBits ? 64 - pbits : kIdxHistBits;
       for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0u;
       __syncthreads();
-      for (uint32_t i = tid; i < n_c; i += kSelThreads) {
-        const uint64_t k = cand_key(i);
+      for_candidates([&](uint64_t k, uint32_t) {
         if ((k >> (64 - pbits)) == prefix)
           atomicAdd(&hist[(uint32_t)(k >> (64 - pbits - d)) & ((1u << d) - 1u)], 1u);
-      }
+      });
       __syncthreads();
       top_bucket<kSelThreads>(hist, 1 << d, need_in, ws, sh);
       prefix = (prefix << d) | sh[0];
@@ -529,33 +579,28 @@ __global__ __launch_bounds__(kSelThreads) void indexer_finish_kernel(IndexerPara
   const bool ties = !all && cnt > need_in;
   uint32_t* const sb = p.sel_bits + t * p.word_stride;
   uint32_t* const tb = p.tie_bits + t * p.word_stride;
-  if (!all) {
-    for (uint32_t i = tid; i < n_c; i += kSelThreads) {
-      const uint64_t k = cand_key(i);
+  if (!all)
+    for_candidates([&](uint64_t k, uint32_t pos) {
       const uint64_t top = pbits == 64 ? k : k >> (64 - pbits);
-      const uint32_t pos = cand_pos(i);
       if (top > prefix || (top == prefix && !ties)) atomicOr(&sb[pos >> 5], 1u << (pos & 31));
       else if (top == prefix) atomicOr(&tb[pos >> 5], 1u << (pos & 31));
-    }
-  }
-  __threadfence();
+    });
+  // Every reader of the bitmaps is in this workgroup: the barrier's wait for
+  // this workgroup's atomics suffices (a device-scope fence would also write
+  // back this XCD's L2)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
 
-  // Ordered emit: thread i takes words [per i, per (i+1)) of the bitmaps.
+  // Ordered emit: thread i takes words [per i, per (i+1)) of the bitmaps,
+  // read once (kEmitWords at a time) for its tie count, its selected count
+  // and the writes.  Word w's selected positions: its selection bits and,
+  // of its tie bits, the lowest (need_in - rank) ones (rank = ties in
+  // earlier words).
   const int nw = (ctx + 31) >> 5;
   const int per = (nw + kSelThreads - 1) / kSelThreads;
   const int w0 = per * tid, w1 = min(w0 + per, nw);
-  uint32_t my_ties = 0;
-  if (ties)
-    for (int w = w0; w < w1; ++w) my_ties += __popc(word_at(&tb[w]));
-  const uint32_t tie_incl = ties ? block_scan<kSelThreads>(my_ties, ws) : 0u;
-  const uint32_t tie_rank0 = tie_incl - my_ties;   // ties in earlier threads' words
-  // word w's selected positions: its selection bits and, of its tie bits,
-  // the lowest (need_in - rank) ones (rank = ties in earlier words)
-  auto selected = [&](int w, uint32_t& rank) -> uint32_t {
-    uint32_t s = word_at(&sb[w]);
+  auto selected = [&](uint32_t s, uint32_t tw, uint32_t& rank) -> uint32_t {
     if (ties) {
-      uint32_t tw = word_at(&tb[w]);
       uint32_t take = rank < need_in ? need_in - rank : 0u;
       rank += __popc(tw);
       while (tw && take) {
@@ -567,21 +612,61 @@ __global__ __launch_bounds__(kSelThreads) void indexer_finish_kernel(IndexerPara
     }
     return s;
   };
+  uint32_t sw_r[kEmitWords], tw_r[kEmitWords];
+  // (words past the thread's range are read at a clamped address and
+  // dropped, so that every load is issued unconditionally; nw >= 1 here)
+  auto load_words = [&](int wa) {
+#pragma unroll
+    for (int u = 0; u < kEmitWords; ++u) {
+      const int w = wa + u;
+      const int wc = w < nw ? w : nw - 1;
+      sw_r[u] = word_at(&sb[wc]);
+      tw_r[u] = ties ? word_at(&tb[wc]) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kEmitWords; ++u)
+      if (wa + u >= w1) sw_r[u] = tw_r[u] = 0u;
+  };
+  const bool in_regs = per <= kEmitWords;   // (contexts up to 8 * 32 * 1024 positions)
+  if (in_regs && nw > 0) load_words(w0);
+  uint32_t my_ties = 0;
+  if (ties) {
+    if (in_regs) {
+#pragma unroll
+      for (int u = 0; u < kEmitWords; ++u) my_ties += __popc(tw_r[u]);
+    } else {
+      for (int wa = w0; wa < w1; wa += kEmitWords) {
+        load_words(wa);
+#pragma unroll
+        for (int u = 0; u < kEmitWords; ++u) my_ties += __popc(tw_r[u]);
+      }
+    }
+  }
+  const uint32_t tie_incl = ties ? block_scan<kSelThreads>(my_ties, ws) : 0u;
+  const uint32_t tie_rank0 = tie_incl - my_ties;   // ties in earlier threads' words
   uint32_t my_sel = 0;
   {
     uint32_t rank = tie_rank0;
-    for (int w = w0; w < w1; ++w) my_sel += __popc(selected(w, rank));
+    for (int wa = w0; wa < w1; wa += kEmitWords) {
+      if (!in_regs) load_words(wa);
+#pragma unroll
+      for (int u = 0; u < kEmitWords; ++u) my_sel += __popc(selected(sw_r[u], tw_r[u], rank));
+    }
   }
   const uint32_t sel_incl = block_scan<kSelThreads>(my_sel, ws);
   {
     uint32_t o = sel_incl - my_sel, rank = tie_rank0;
-    for (int w = w0; w < w1; ++w) {
-      uint32_t s = selected(w, rank);
-      while (s) {
-        const int bit = __ffs((int)s) - 1;
-        s &= s - 1u;
-        if (o < (uint32_t)p.topk) out[o] = (int32_t)(out_base + 32 * w + bit);
-        ++o;
+    for (int wa = w0; wa < w1; wa += kEmitWords) {
+      if (!in_regs) load_words(wa);
+#pragma unroll
+      for (int u = 0; u < kEmitWords; ++u) {
+        uint32_t s = selected(sw_r[u], tw_r[u], rank);
+        while (s) {
+          const int bit = __ffs((int)s) - 1;
+          s &= s - 1u;
+          if (o < (uint32_t)p.topk) out[o] = (int32_t)(out_base + 32 * (wa + u) + bit);
+          ++o;
+        }
       }
     }
   }
