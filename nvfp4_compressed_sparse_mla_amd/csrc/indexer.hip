@@ -180,6 +180,7 @@ __device__ __forceinline__ void load_keys(const uint64_t* keys, int i, int ctx, 
 
 __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerParams p) {
   __shared__ uint32_t hist[kBins];
+  __shared__ int64_t rows_s[kChunk];   // key row of each position of the chunk (-1: none)
   const uint32_t nch = (uint32_t)p.nchunks;
   const uint32_t t32 = blockIdx.x / nch;
   const int c = (int)(blockIdx.x - t32 * nch);
@@ -191,39 +192,92 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerParams p) {
   for (int i = tid; i < kBins; i += 256) hist[i] = 0;
 
   double q[16];
-  e4m3x16_to_f64(*reinterpret_cast<const u32x4*>(p.q + t * p.q_st + 16 * sub), q);
+  const uint8_t* const qrow = p.q + t * p.q_st + 16 * sub;
+  e4m3x16_to_f64(*reinterpret_cast<const u32x4*>(qrow), q);
   const int64_t base = p.bt ? 0 : p.base[t];
   const int64_t seq = p.bt ? (int64_t)p.tok_seq[t] : 0;
   uint64_t* const kout = p.keys_ws + t * p.key_stride;
-  __syncthreads();
 
-  // wave w takes positions p0 + kWavePos w + 8 i + (lane >> 3), four i at a time
-  constexpr int kWavePos = kChunk / 4;
-  constexpr int kUnroll = 4;
-  for (int i0 = 0; i0 < kWavePos / 8; i0 += kUnroll) {
-    u32x4 raw[kUnroll];
-    bool ok[kUnroll];
-    int pos[kUnroll];
+  // The key row of every position of the chunk, 4 per thread, their
+  // block-table loads issued together (the keys' loads below then depend on
+  // no other global load).
+  {
+    constexpr int kPer = kChunk / 256;
+    int64_t rr[kPer];
+    if (p.bt) {
+      const bool seq_ok = seq >= 0 && seq < p.bt_rows;
+      const int32_t* const btr = p.bt + (seq_ok ? seq : 0) * p.bt_st;
+      int blk[kPer], e[kPer];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      pos[u] = p0 + kWavePos * wave + 8 * (i0 + u) + (lane >> 3);
-      const int64_t r = pos[u] < ctx ? key_row(p, base, seq, pos[u]) : -1;
-      ok[u] = r >= 0;
-      raw[u] = ok[u] ? *reinterpret_cast<const u32x4*>(p.keys + r * kIdxDim + 16 * sub) : (u32x4){0, 0, 0, 0};
+      for (int m = 0; m < kPer; ++m) {
+        const int pos = p0 + tid + 256 * m;
+        blk[m] = p.bs_log2 >= 0 ? pos >> p.bs_log2 : pos / p.bs;
+        e[m] = btr[blk[m] < p.bt_cols ? blk[m] : p.bt_cols - 1];
+      }
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        const int pos = p0 + tid + 256 * m;
+        int64_t r = -1;
+        if (pos < ctx && seq_ok && blk[m] < p.bt_cols && e[m] >= 0) {
+          r = (int64_t)e[m] * p.bs + (pos - blk[m] * p.bs);
+          if (r >= p.key_rows) r = -1;
+        }
+        rr[m] = r;
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        const int pos = p0 + tid + 256 * m;
+        const int64_t r = base + pos;
+        rr[m] = (pos < ctx && r >= 0 && r < p.key_rows) ? r : -1;
+      }
     }
 #pragma unroll
+    for (int m = 0; m < kPer; ++m) rows_s[tid + 256 * m] = rr[m];
+  }
+  __syncthreads();
+
+  // wave w takes positions p0 + kWavePos w + 8 i + (lane >> 3), four i at a
+  // time; the next four's keys are loaded while these are scored
+  constexpr int kWavePos = kChunk / 4;
+  constexpr int kUnroll = 4;
+  constexpr int kIters = kWavePos / 8 / kUnroll;
+  auto fetch = [&](int it, u32x4 (&raw)[kUnroll], bool (&ok)[kUnroll]) {
+#pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
+      const int off = kWavePos * wave + 8 * (it * kUnroll + u) + (lane >> 3);
+      const int64_t r = rows_s[off];
+      ok[u] = r >= 0;
+      // (a position without a key reads q's row, a valid address, and drops it)
+      raw[u] = *reinterpret_cast<const u32x4*>(ok[u] ? p.keys + r * kIdxDim + 16 * sub : qrow);
+    }
+  };
+  u32x4 nraw[kUnroll];
+  bool nok[kUnroll];
+  fetch(0, nraw, nok);
+  for (int it = 0; it < kIters; ++it) {
+    u32x4 raw[kUnroll];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      raw[u] = nraw[u];
+      ok[u] = nok[u];
+    }
+    if (it + 1 < kIters) fetch(it + 1, nraw, nok);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int pos = p0 + kWavePos * wave + 8 * (it * kUnroll + u) + (lane >> 3);
       double k[16];
-      e4m3x16_to_f64(raw[u], k);
+      e4m3x16_to_f64(ok[u] ? raw[u] : (u32x4){0, 0, 0, 0}, k);
       double s = 0.0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) s = __builtin_fma(q[j], k[j], s);   // exact (see above)
       s += __shfl_xor(s, 1, 64);
       s += __shfl_xor(s, 2, 64);
       s += __shfl_xor(s, 4, 64);
-      if (sub == 0 && pos[u] < ctx) {
+      if (sub == 0 && pos < ctx) {
         const uint64_t key = ok[u] ? score_key(s) : 0ull;
-        kout[pos[u]] = key;
+        kout[pos] = key;
         if (key) atomicAdd(&hist[key_bucket(key)], 1u);
       }
     }
@@ -235,7 +289,7 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerParams p) {
 }
 
 __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerParams p) {
-  __shared__ uint32_t hist[kBins];
+  __shared__ __align__(16) uint32_t hist[kBins];
   __shared__ uint32_t ws[kSelThreads / 64];
   __shared__ uint32_t sh_bin, sh_above, sh_cnt, sh_tot;
   const int tid = threadIdx.x;
@@ -245,13 +299,16 @@ __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerPara
   int32_t* const out = p.out + t * p.out_st;
   const int64_t out_base = p.bt ? 0 : p.base[t];
 
-  // the score kernel's histogram of the top 12 bits; zero it for the next call
-  uint32_t* const g = p.hist + t * kBins;
+  // the score kernel's histogram of the top 12 bits (one 16-byte load per
+  // thread); zero it for the next call
+  static_assert(kBins == 4 * kSelThreads, "histogram words per thread");
   uint32_t mine = 0;
-  for (int i = tid; i < kBins; i += kSelThreads) {
-    hist[i] = g[i];
-    mine += hist[i];
-    g[i] = 0u;
+  {
+    u32x4* const g = reinterpret_cast<u32x4*>(p.hist + t * kBins);
+    const u32x4 h = g[tid];
+    g[tid] = (u32x4){0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4*>(hist)[tid] = h;
+    mine = h[0] + h[1] + h[2] + h[3];
   }
   const uint32_t total = block_scan(mine, ws);
   if (tid == kSelThreads - 1) sh_tot = total;
