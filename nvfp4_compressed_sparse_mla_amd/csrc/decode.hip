@@ -93,6 +93,7 @@ constexpr int kVCols = kLatent / kVW; // output columns per value wave
 constexpr int kVRow = kLatent;
 constexpr int kTileV = kRowsT * kVRow;  // FP16 elements of one tile's V
 __device__ __forceinline__ uint32_t vswz(uint32_t r) { return 4 * (r & 3) + ((r >> 1) & 3); }
+constexpr int kPRow = kRowsT + 8;       // FP16 elements per head in the P buffer (16 rows + padding)
 constexpr int kKSteps = 18;           // 576 key dimensions / 32
 constexpr float kLazy = 15.0f;        // P = 2^(s - reference) <= 2^15 stays inside FP16
 constexpr float kMargin = 5.0f;       // a new reference sits 2^5 above the max that set it
@@ -436,7 +437,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   // the loop the ring and V areas hold the value waves' output exchange.
   __shared__ __align__(16) uint8_t ring_all[kSW * kWaveRing];
   __shared__ __align__(256) half_t vbuf_all[kSW * kTileV];   // (256-byte aligned: see read_v_tile)
-  __shared__ __align__(16) half_t pbuf[kSW][kHG][kRowsT];   // P of a round's tiles, [head][row]
+  // P of a round's tiles, [head][row]; heads 48 bytes apart, so that 16
+  // consecutive heads (the value waves' 16-byte reads, the score waves'
+  // 8-byte writes) fall in distinct banks
+  __shared__ __align__(16) half_t pbuf[kSW][kHG][kPRow];
   __shared__ __align__(16) float ref_s[kSW][kHG];           // the reference each tile's P is relative to
   __shared__ int phys[kMaxTopk];
   __shared__ __align__(16) float wm_s[kSW][kHG];            // per score wave: final reference (base 2)
@@ -960,7 +964,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
       u32x4 bv[kSW][4];
       static_for<0, kSW>([&](auto W) {
         constexpr int w = decltype(W)::value;
-        pa[w] = __builtin_bit_cast(half8_t, ring_b128<w * kHG * kRowsT * 2>(pa_addr));
+        pa[w] = __builtin_bit_cast(half8_t, ring_b128<w * kHG * kPRow * 2>(pa_addr));
         mr[w] = __uint_as_float(lds_b32<w * kHG * 4>(ref_addr));
         read_v_tile<w>(bv[w], vb);
       });
