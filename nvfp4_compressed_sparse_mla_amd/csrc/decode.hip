@@ -772,9 +772,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     lds_barrier();   // every score wave has its q before the V buffer is written
     const bool two_level = kFmt == kFmtNvfp4 && p.lat_scale != 1.0f;
     const RingOff<kFmt> ro(r16, kg);
-    // this lane's V row (r16) and its 16 chunks from 16 kg, swizzled by vswz(r16)
-    half_t* const vrow = vbuf_all + sw * kTileV + r16 * kVRow + 128 * kg;
-    const int vsw = (int)vswz((uint32_t)r16);
+    // this lane's V row (r16) and its 16 chunks from 16 kg: chunk tt at
+    // byte vx ^ 16 tt (the row group is 256-byte aligned, and the swizzle
+    // XORs the chunk index with vswz(r16)).  The writes are inline
+    // ds_write_b128: as plain stores, the compiler could not tell them from
+    // the ring DMA's LDS writes and would wait for that DMA first.
+    const uint32_t vx = lds_off(vbuf_all + sw * kTileV + r16 * kVRow + 128 * kg) ^ (16u * vswz((uint32_t)r16));
     float mref[2] = {kNegInf, kNegInf};   // reference of head hb*16 + r16 (base 2)
     float lsum[2] = {0.0f, 0.0f};         // this lane's share of that head's row sum
     Raw<kFmt> raw;
@@ -820,7 +823,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
         MLA_DEVICE_ASM("s_nop 1" : "+v"(kop));
         static_for<0, 16>([&](auto T) {
           constexpr int tt = decltype(T)::value;
-          *reinterpret_cast<half8_t*>(vrow + 8 * (tt ^ vsw)) = kop;
+          MLA_DEVICE_ASM("ds_write_b128 %0, %1" :: "v"(vx ^ (16u * tt)), "v"(kop) : "memory");
           __builtin_amdgcn_sched_barrier(0);
           score_mfma1(sacc[0], kop, qreg[0][tt]);
           __builtin_amdgcn_sched_barrier(0);
