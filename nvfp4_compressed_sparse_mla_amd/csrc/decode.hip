@@ -1076,7 +1076,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
 
   // Count arrivals once every wave's partial stores are complete (each wave
   // waits for its own; the barrier orders them before the count); the last
-  // arrival merges.
+  // arrival merges.  Why a relaxed count suffices (AMDGPU memory model,
+  // GFX942/GFX950): an agent-scope release is "buffer_wbl2 sc1" (write back
+  // the L2 lines that plain stores left dirty) followed by "s_waitcnt
+  // vmcnt(0)".  Everything this protocol publishes (partials and
+  // log2-sum-exps) is stored with the agent-scope policy sc1, the one the
+  // model uses for agent-scope atomic stores, so nothing of it is dirty in
+  // L2; the vmcnt wait below completes those stores before the count, which
+  // is all that remains of the release.  The merging split's acquire is the
+  // fence after its count.
   MLA_DEVICE_ASM("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   uint32_t* ctr = p.counters + tg;
