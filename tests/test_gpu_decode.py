@@ -168,6 +168,43 @@ def test_duplicates_and_out_of_range_indices():
     _check(w, cache, out, lse, what="dups")
 
 
+@pytest.mark.parametrize("splits", [1, 2, 5, 8])
+@pytest.mark.parametrize("kind", ["negative", "past_pool", "unmapped_block"])
+def test_masked_middle_slots_after_speculated_first_tiles(kind, splits):
+    # Every list ends in a valid slot and its first tiles' rows are valid, so
+    # the score waves issue their first tiles' DMA from the slot list before
+    # the compaction; the masked slots further in then shift the compacted
+    # rows and the split boundaries, and the waves must replace that DMA.
+    bs, nblk, topk = 64, 48, 2048
+    w = make_custom(bs * nblk, 3, 32, topk, seed=31, device=DEV)
+    rng = np.random.default_rng(31)
+    bt = np.stack([rng.permutation(nblk) for _ in range(3)]).astype(np.int32)
+    idx = np.stack([rng.choice(bs * nblk, topk, replace=False) for _ in range(3)]).astype(np.int64)
+    ref = idx.copy()
+    # masked slots: a few in the middle and one just past the first tiles
+    for t, cols in enumerate([[700], [300, 301, 1500], [64 * 4 + 1, 1024, 2000]]):
+        for c in cols:
+            if kind == "negative":
+                idx[t, c] = -1
+            elif kind == "past_pool":
+                idx[t, c] = 2**31 - 1
+            else:
+                # a position in a block whose table entry is unmapped
+                blk = int(idx[t, c]) // bs
+                bt[t, blk] = -1
+                ref[t, idx[t] // bs == blk] = -1          # every slot in that block is masked
+            ref[t, c] = -1
+    assert (idx[:, -1] >= 0).all() and (ref[:, -1] >= 0).all() or kind == "unmapped_block"
+    w.indices = torch.from_numpy(idx.astype(np.int32)).to(DEV)
+    w.block_table = torch.from_numpy(bt).to(DEV)
+    w.token_seq = torch.arange(3, dtype=torch.int32, device=DEV)
+    w.block_size = bs
+    cache = _fill(w)
+    out, lse = _run(w, cache, num_splits=splits)
+    w.indices = torch.from_numpy(np.where(ref < 0, -1, ref).astype(np.int32)).to(DEV)
+    _check(w, cache, out, lse, what=f"masked-{kind}-S{splits}")
+
+
 @pytest.mark.parametrize("bs", [64, 48, 16])
 def test_block_table_small(bs):
     # power-of-two block sizes take the shift path, others the division
