@@ -127,6 +127,26 @@ def test_long_contexts_of_equal_scores():
             assert np.array_equal(out.cpu().numpy(), _oracle(q, kk, ctx, topk, base=base)), topk
 
 
+def test_contexts_past_the_emit_registers():
+    """Contexts longer than 8 x 32 x 1024 positions take the ordered emit's
+    chunked path (more than 8 bitmap words per thread).  With random keys
+    ~8% of 300K positions share the threshold bucket, more than the finish
+    kernel's LDS candidate cache holds; a long run of one key puts the
+    threshold inside ties spread over many words."""
+    n = 300_000
+    keys = fp8_values((n, 128), 12, 0, DEV)
+    q = fp8_values((3, 128), 12, 1, DEV)
+    runs = keys.clone()
+    runs[100_000:280_000] = keys[5]
+    ctx = torch.tensor([n, 270_001, n - 31], dtype=torch.int32, device=DEV)
+    base = torch.zeros(3, dtype=torch.int64, device=DEV)
+    for kk in (keys, runs):
+        for topk in (2048, 513):
+            out = mla.indexer_topk(q, kk, ctx, topk, n, key_base=base)
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy(), _oracle(q, kk, ctx, topk, base=base)), topk
+
+
 def test_decode15_full_size_every_token():
     w = make_workload("decode15", DEV)
     ix = indexer_inputs(w)
