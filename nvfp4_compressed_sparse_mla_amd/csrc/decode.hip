@@ -316,12 +316,31 @@ __device__ __forceinline__ void store8(T* dst, const float (&v)[8]) {
 // uses), which writes through this XCD's L2, so the writer needs no
 // L2-wide writeback before counting its arrival.  One 16-byte store; in
 // assembly, so the caller waits for it itself (s_waitcnt vmcnt(0) right
-// after its last store).
+// after its last store).  A store of more than 8 bytes reads its data
+// registers after it issues, and a VALU write to them needs wait states
+// after it (the store-data hazard); the compiler does not see this store,
+// so the wait states are part of the statement: without them the next
+// instruction may reuse the data registers while the late lanes' data is
+// still being read.
 __device__ __forceinline__ void store8_agent(half_t* dst, const float (&v)[8]) {
   u32x4 w;
 #pragma unroll
   for (int i = 0; i < 4; ++i) w[i] = as_u32((half2_t){(half_t)v[2 * i], (half_t)v[2 * i + 1]});
-  MLA_DEVICE_ASM("global_store_dwordx4 %0, %1, off sc1" :: "v"(dst), "v"(w) : "memory");
+  MLA_DEVICE_ASM("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" :: "v"(dst), "v"(w) : "memory");
+}
+
+// The merge's reads of the other splits' results: 16-byte loads with the
+// agent-scope policy (sc1, what an agent-scope atomic load uses), coherent
+// at agent scope by themselves, so no cache invalidation is needed before
+// them.  In assembly (the caller waits with vmcnt and ties the registers).
+__device__ __forceinline__ u32x4 load16_agent(const void* src) {
+  u32x4 v;
+  MLA_DEVICE_ASM("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(src) : "memory");
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ void tie4(T& a, T& b, T& c, T& d) {
+  MLA_DEVICE_ASM("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
@@ -443,8 +462,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   __shared__ __align__(16) half_t pbuf[kSW][kHG][kPRow];
   __shared__ __align__(16) float ref_s[kSW][kHG];           // the reference each tile's P is relative to
   __shared__ int phys[kMaxTopk];
-  __shared__ __align__(16) float wm_s[kSW][kHG];            // per score wave: final reference (base 2)
-  __shared__ __align__(16) float wl_s[kSW][kHG];            // per score wave: row sums
+  // per head: the score waves' final references (base 2), then their row sums
+  __shared__ __align__(16) float wml_s[kHG][2 * kSW];
   __shared__ __align__(16) float fac_s[kVW][kHG];           // per value wave: per-head factors
   __shared__ __align__(16) int cnt_s[kSlices][kVW];   // valid slots per (slice, value wave)
   __shared__ int last_s;
@@ -751,6 +770,13 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   auto xregion = [&](int j) -> uint8_t* {
     return (j < 2 ? ring_all : reinterpret_cast<uint8_t*>(vbuf_all)) + (j & 1) * kXRegion;
   };
+  // A split's partial is kept in the order its value waves' lanes hold it
+  // after the exchange (value wave j, pass u, head 4hq + h of the lane's
+  // quad: 64 lanes x 16 bytes), so that every store and every merge load is
+  // one contiguous kilobyte per wave
+  auto part_slice = [&](int x, int j, int u, int h) -> half_t* {
+    return p.part_o + ((((tg * S + x) * kVW + j) * 2 + u) * 4 + h) * (64 * 8) + 8 * lane;
+  };
 
   if (wave < kSW) {
     // ============================================================ score wave
@@ -898,12 +924,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     if (kg == 0) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        wm_s[sw][hb * 16 + r16] = mref[hb];
-        wl_s[sw][hb * 16 + r16] = lsum[hb];
+        wml_s[hb * 16 + r16][sw] = mref[hb];
+        wml_s[hb * 16 + r16][kSW + sw] = lsum[hb];
       }
     }
     lds_barrier();   // E: every score wave's (reference, row sum) is in LDS
-    lds_barrier();   // F: the value waves have read them
   } else {
     // ============================================================ value wave
     lds_barrier();   // (the score waves' q reads)
@@ -929,13 +954,16 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     // factors of this lane's 16 accumulator heads (c_head) from fac_s[j]
     auto read_factors = [&](float (&f)[16]) {
       MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" ::: "memory");
-      static_for<0, 4>([&](auto Q) {
-        constexpr int q = decltype(Q)::value;
-        u32x4 v;
-        MLA_DEVICE_ASM("ds_read_b128 %0, %1 offset:%2\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(fac_r), "i"(32 * q));
+      u32x4 v[4];
+      MLA_DEVICE_ASM("ds_read_b128 %0, %1" : "=v"(v[0]) : "v"(fac_r));
+      MLA_DEVICE_ASM("ds_read_b128 %0, %1 offset:32" : "=v"(v[1]) : "v"(fac_r));
+      MLA_DEVICE_ASM("ds_read_b128 %0, %1 offset:64" : "=v"(v[2]) : "v"(fac_r));
+      MLA_DEVICE_ASM("ds_read_b128 %0, %1 offset:96" : "=v"(v[3]) : "v"(fac_r));
+      MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) f[4 * q + e] = __uint_as_float(v[e]);
-      });
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[4 * q + e] = __uint_as_float(v[q][e]);
     };
     // Refill R(m) (value-wave refills): tile j + kSW (m + kDepth) of score
     // wave j into its slot m % kDepth, issued right after A(m) (the score
@@ -1015,18 +1043,17 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     // waves (whose references are all <= M); log2-sum-exp = M + log2 L
     float inv = 0.0f, lse2 = kNegInf;
     {
+      const float4_t wm = *reinterpret_cast<const float4_t*>(&wml_s[hl][0]);
+      const float4_t wl = *reinterpret_cast<const float4_t*>(&wml_s[hl][kSW]);
       float L = 0.0f;
-      if (M != kNegInf) {
 #pragma unroll
-        for (int w = 0; w < kSW; ++w)
-          L += wm_s[w][hl] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(wm_s[w][hl] - M) * wl_s[w][hl];
-      }
-      if (L > 0.0f) {
+      for (int w = 0; w < kSW; ++w)
+        L += wm[w] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(wm[w] - M) * wl[w];
+      if (M != kNegInf && L > 0.0f) {
         inv = 1.0f / L;
         lse2 = M + __log2f(L);
       }
     }
-    lds_barrier();   // F
     if (j == 0 && lane < 32) {
       const int head = g * kHG + hl;
       if (S > 1) __hip_atomic_store(p.part_lse + (tg * S + s) * kHG + hl, lse2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1066,7 +1093,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
       for (int h = 0; h < 4; ++h) {
         const int hd = 4 * hq + h, head = g * kHG + hd;
         const int col = kVCols * j + 8 * co;
-        if (S > 1) store8_agent(p.part_o + ((tg * S + s) * kHG + hd) * kLatent + col, o[h]);
+        if (S > 1) store8_agent(part_slice(s, j, u, h), o[h]);
         else if (head < p.H)
           store8<kBf16>(reinterpret_cast<uint16_t*>(p.out) + (t * H + head) * kLatent + col, o[h]);
       }
@@ -1083,104 +1110,165 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   // log2-sum-exps) is stored with the agent-scope policy sc1, the one the
   // model uses for agent-scope atomic stores, so nothing of it is dirty in
   // L2; the vmcnt wait below completes those stores before the count, which
-  // is all that remains of the release.  The merging split's acquire is the
-  // fence after its count.
+  // is all that remains of the release.  The merging split reads the
+  // results with agent-scope loads (sc1), which see them without an acquire
+  // fence's cache invalidation: these loads are issued only after its count
+  // has returned, and that count follows every other split's count.
   MLA_DEVICE_ASM("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   uint32_t* ctr = p.counters + tg;
   if (tid == 0) {
     const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int last = old == (uint32_t)S - 1u;
-    if (last) {
-      // the partials were written through (agent-scope stores) before their
-      // counts; invalidate this XCD's caches so that plain loads see them
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
-    }
+    if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
     last_s = last;
   }
   __syncthreads();
   if (!last_s) return;
 
-  // Chunks of 8 consecutive columns, 32 heads x 64 chunks: chunk tid + 512 m
-  // (m = 0..3) is head (tid >> 6) + 8 m, columns 8 (tid & 63).  The
-  // log2-sum-exps are loaded first (lane x of wave 0 reads split x's), then
-  // the partials of up to kBatch splits at once, so that the merge waits
-  // for one memory round trip per batch; the merge weights are computed
-  // while the partials are in flight.  Splits are summed in index order.
-  constexpr int kMH = kHG * 64 / kThreads;   // heads per thread
+  // The merge, by all eight waves: wave w takes the slice that value wave
+  // j = w / 2 stored in its pass u = w mod 2 (heads 4hq + [0,4) x columns
+  // 128j + 8co + [0,8), hq = lane mod 8, co = lane / 8 + 8u), so that this
+  // split's own partial comes from j's exchange region in LDS (rounded to
+  // FP16 as it was stored) and only the other splits' partials are read
+  // from memory.  Per batch of up to kBatch splits a lane loads its heads'
+  // log2-sum-exps (one 16-byte load per split) and then the partials, so
+  // that a batch waits for one memory round trip, and it derives the merge
+  // weights itself (no barrier).  Splits are summed in index order.
   constexpr int kBatch = 8;                  // splits whose partials are in flight together
-  float* lse_sh = reinterpret_cast<float*>(ring_all);   // [S][32]
-  float* wsh = lse_sh + 64 * kHG;                        // [S][32]
-  const int cc = 8 * (tid & 63);
-  const half_t* pp = p.part_o + (tg * S) * kHG * kLatent + (tid >> 6) * kLatent + cc;
-  half8_t part[kBatch][kMH];
-  auto load_batch = [&](int x0) {
+  const int mj = wave >> 1, hq = lane & 7, co = (lane >> 3) + 8 * (wave & 1);
+  const int col = kVCols * mj + 8 * co;
+  const float* pl = p.part_lse + tg * S * kHG + 4 * hq;                    // split x: + x kHG
+  float4_t lb[kBatch];
+  half8_t part[kBatch][4];
+  auto load_lse = [&](int x0) {
     static_for<0, kBatch>([&](auto X) {
       constexpr int x = decltype(X)::value;
-      if (x0 + x < S) {
+      if (x0 + x < S) lb[x] = __builtin_bit_cast(float4_t, load16_agent(pl + (x0 + x) * kHG));
+    });
+  };
+  auto load_parts = [&](int x0) {
+    static_for<0, kBatch>([&](auto X) {
+      constexpr int x = decltype(X)::value;
+      if (x0 + x < S && x0 + x != s) {
 #pragma unroll
-        for (int m = 0; m < kMH; ++m)
-          part[x][m] = *reinterpret_cast<const half8_t*>(pp + ((x0 + x) * kHG + kWaves * m) * kLatent);
+        for (int h = 0; h < 4; ++h)
+          part[x][h] = __builtin_bit_cast(half8_t, load16_agent(part_slice(x0 + x, mj, wave & 1, h)));
       }
     });
   };
-  float a[kMH][8];
+  // (all of a batch's loads complete; the ties keep every use of their
+  // registers behind the wait)
+  auto wait_loads = [&]() {
+    MLA_DEVICE_ASM("s_waitcnt vmcnt(0)" ::: "memory");
+    tie4(lb[0], lb[1], lb[2], lb[3]);
+    tie4(lb[4], lb[5], lb[6], lb[7]);
+    static_for<0, kBatch>([&](auto X) {
+      constexpr int x = decltype(X)::value;
+      tie4(part[x][0], part[x][1], part[x][2], part[x][3]);
+    });
+  };
+  // log2 of sum_x 2^lse_x per head, against the running maximum (in split
+  // order; 2^(-inf - finite) is 0, so an empty split adds nothing)
+  float mx[4], sum[4];
 #pragma unroll
-  for (int m = 0; m < kMH; ++m)
+  for (int h = 0; h < 4; ++h) {
+    mx[h] = kNegInf;
+    sum[h] = 0.0f;
+  }
+  auto lse_batch = [&](int x0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[m][i] = 0.0f;
-  auto add_batch = [&](int x0) {
+    for (int h = 0; h < 4; ++h) {
+      float bm = mx[h];
+#pragma unroll
+      for (int x = 0; x < kBatch; ++x)
+        if (x0 + x < S) bm = __builtin_fmaxf(bm, lb[x][h]);
+      if (bm != kNegInf) {
+        float sx = mx[h] == kNegInf ? 0.0f : sum[h] * __builtin_amdgcn_exp2f(mx[h] - bm);
+#pragma unroll
+        for (int x = 0; x < kBatch; ++x)
+          if (x0 + x < S) sx += __builtin_amdgcn_exp2f(lb[x][h] - bm);
+        sum[h] = sx;
+      }
+      mx[h] = bm;
+    }
+  };
+  if (S <= kBatch) {
+    load_lse(0);
+    load_parts(0);
+  } else {
+    for (int x0 = 0; x0 < S; x0 += kBatch) {
+      load_lse(x0);
+      wait_loads();
+      lse_batch(x0);
+    }
+    load_lse(0);
+    load_parts(0);
+  }
+  // this split's own partial, as stored (the exchange region's reader
+  // layout of the epilogue); an assembly read, so that no wait for the
+  // loads above is added in front of it
+  half8_t own[4];
+  {
+    const uint32_t rslot = 32 * (hq & 1) + 8 * (co & 3);
+    const uint32_t src = lds_off(xregion(mj) + ((co >> 2) * 4 + (hq >> 1)) * kXBlock + 16 * rslot + 32 * (rslot >> 4));
+    u32x4 v[8];
+    static_for<0, 8>([&](auto X) {
+      constexpr int x = decltype(X)::value;
+      v[x] = ring_b128<16 * x>(src);
+    });
+    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                   "+v"(v[6]), "+v"(v[7]));
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int x = 0; x < 8; ++x) own[h][x] = (half_t)__uint_as_float(v[x][h]);
+  }
+  wait_loads();
+  if (S <= kBatch) lse_batch(0);
+  float inv[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) inv[h] = mx[h] != kNegInf ? 1.0f / sum[h] : 0.0f;
+  float a[4][8];
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[h][i] = 0.0f;
+  for (int x0 = 0; x0 < S; x0 += kBatch) {
+    if (x0 > 0) {
+      load_lse(x0);
+      load_parts(x0);
+      wait_loads();
+    }
     static_for<0, kBatch>([&](auto X) {
       constexpr int x = decltype(X)::value;
       if (x0 + x < S) {
+        const bool mine = x0 + x == s;
 #pragma unroll
-        for (int m = 0; m < kMH; ++m) {
-          const float w = wsh[(x0 + x) * kHG + (tid >> 6) + kWaves * m];
+        for (int h = 0; h < 4; ++h) {
+          const float w = mx[h] != kNegInf ? __builtin_amdgcn_exp2f(lb[x][h] - mx[h]) * inv[h] : 0.0f;
+          const half8_t pv = mine ? own[h] : part[x][h];
           // (a fused multiply-add per element taking its FP16 operand as is: v_fma_mix)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) a[m][i] = __builtin_fmaf(w, (float)part[x][m][i], a[m][i]);
+          for (int i = 0; i < 8; ++i) a[h][i] = __builtin_fmaf(w, (float)pv[i], a[h][i]);
         }
       }
     });
-  };
-  float4_t lx[8];
-  if (wave == 0) {
-    const float4_t* src = reinterpret_cast<const float4_t*>(p.part_lse + (tg * S + (lane < S ? lane : 0)) * kHG);
+  }
+  if (wave == 0 && co == 0 && p.lse) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) lx[i] = src[i];
-  }
-  load_batch(0);
-  if (wave == 0 && lane < S) {
-    float4_t* dst = reinterpret_cast<float4_t*>(lse_sh + lane * kHG);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = lx[i];
-  }
-  lds_barrier();   // (not __syncthreads: the partials' loads stay in flight)
-  if (tid < kHG) {
-    float mx = kNegInf;
-    for (int ss = 0; ss < S; ++ss) mx = __builtin_fmaxf(mx, lse_sh[ss * kHG + tid]);
-    float sum = 0.0f;
-    if (mx != kNegInf)
-      for (int ss = 0; ss < S; ++ss) sum += __builtin_amdgcn_exp2f(lse_sh[ss * kHG + tid] - mx);
-    const float inv = mx != kNegInf ? 1.0f / sum : 0.0f;
-    for (int ss = 0; ss < S; ++ss)
-      wsh[ss * kHG + tid] = mx != kNegInf ? __builtin_amdgcn_exp2f(lse_sh[ss * kHG + tid] - mx) * inv : 0.0f;
-    const int head = g * kHG + tid;
-    if (head < p.H && p.lse) p.lse[t * H + head] = mx != kNegInf ? (mx + __log2f(sum)) * kLn2 : kNegInf;
-  }
-  lds_barrier();
-  for (int x0 = 0; x0 < S; x0 += kBatch) {
-    if (x0 > 0) load_batch(x0);
-    add_batch(x0);
+    for (int h = 0; h < 4; ++h) {
+      const int head = g * kHG + 4 * hq + h;
+      if (head < p.H) p.lse[t * H + head] = mx[h] != kNegInf ? (mx[h] + __log2f(sum[h])) * kLn2 : kNegInf;
+    }
   }
 #pragma unroll
-  for (int m = 0; m < kMH; ++m) {
-    const int hd = (tid >> 6) + kWaves * m, head = g * kHG + hd;
+  for (int h = 0; h < 4; ++h) {
+    const int head = g * kHG + 4 * hq + h;
     if (head >= p.H) continue;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[m][i] *= out_mul;
-    store8<kBf16>(reinterpret_cast<uint16_t*>(p.out) + (t * H + head) * kLatent + cc, a[m]);
+    for (int i = 0; i < 8; ++i) a[h][i] *= out_mul;
+    store8<kBf16>(reinterpret_cast<uint16_t*>(p.out) + (t * H + head) * kLatent + col, a[h]);
   }
 }
 

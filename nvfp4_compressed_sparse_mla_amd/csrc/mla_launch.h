@@ -44,7 +44,7 @@ struct DecodeParams {
   float* lse;
   uint32_t* counters;       // [T*G] arrivals per (token, head group)
   float* part_lse;          // [T*G][S][32]
-  _Float16* part_o;         // [T*G][S][32][512]
+  _Float16* part_o;         // [T*G][S][32 x 512], in the order the kernel's lanes hold it
   int S;                    // splits per (token, head group)
   int xcd_shift;            // set by launch_decode: 3 = a unit's splits share an XCD, 0 = plain order
 };
