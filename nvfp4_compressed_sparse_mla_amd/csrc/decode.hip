@@ -808,6 +808,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     float lsum[2] = {0.0f, 0.0f};         // this lane's share of that head's row sum
     Raw<kFmt> raw;
     float4_t sacc[2];
+    // (the score waves' instructions win issue arbitration against the value
+    // waves' on the same SIMD: the score waves' chain sets the round time)
+    __builtin_amdgcn_s_setprio(1);
     for (int i = 0; i < rounds; ++i) {
       const bool have = i < my_tiles;     // (only the last round can miss a tile)
       const int k = sw + kSW * i;         // tile index within the split
@@ -915,6 +918,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
       lds_barrier();   // A(i): round i's P, references and V are in LDS
     }
     if (rounds > 0) lds_barrier();   // B(rounds-1)
+    __builtin_amdgcn_s_setprio(0);
     wait_vmcnt<0>();   // no DMA may still be writing this workgroup's LDS
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
