@@ -153,10 +153,12 @@ int32_t mla_sparse_decode_num_splits(int64_t num_tokens, int32_t num_heads,
  * sizer's choice.  The workspace holds what the write-up's cooperating
  * blocks exchange ("A native NVFP4 sparse-MLA decode kernel": the blocks
  * sharing a token's rows combine their partial results without a second
- * launch): per (token, group of 32 heads) an arrival counter and, with more
- * than one split, each split's partial output and log-sum-exp.  The workspace must be zero-filled before its first use;
- * every completed call leaves it in that state again.  Returns 0 on bad
- * arguments.
+ * launch): per (token, group of 32 heads) 64 bytes of arrival state (an
+ * arrival count with a call epoch, and which split combines which slice of
+ * the partials) and, with more than one split, each split's partial output
+ * and log-sum-exp.  The arrival state must be zero before the first use (a
+ * zero-filled workspace); every completed call leaves it valid for the
+ * next one.  Returns 0 on bad arguments.
  */
 size_t mla_sparse_decode_workspace_size(int64_t num_tokens, int32_t num_heads,
                                         int32_t topk, int32_t num_splits);
@@ -231,6 +233,22 @@ int mla_sparse_decode(const void* q, int q_dtype, int64_t num_tokens,
                       int32_t num_splits, void* stream);
 
 /*
+ * mla_sparse_decode_set_merge_polls -- how long a split waits to take part
+ * in combining its token's partial results (Prime Inference write-up, "A
+ * native NVFP4 sparse-MLA decode kernel": the blocks that share a token's
+ * rows combine their results within the same launch).  With S > 1 splits,
+ * split k combines slice k of the S partials once every split has arrived;
+ * it polls for that at most `polls` times (about a microsecond each) and
+ * otherwise leaves its slice to the split that arrives last, which combines
+ * every slice no other split has taken.  0 = no split waits (the last
+ * arrival combines everything).  The result does not depend on the setting.
+ * Launches whose workgroups cannot all be resident at once never wait.
+ * Process-wide; returns the previous value, or -1 (and changes nothing)
+ * for polls < 0.  Default 256.
+ */
+int32_t mla_sparse_decode_set_merge_polls(int32_t polls);
+
+/*
  * mla_sparse_decode_noalloc -- mla_sparse_decode for callers that cannot
  * allocate device memory (code under HIP graph capture, serving loops or
  * harnesses that forbid hipMalloc).  It computes exactly what
@@ -240,12 +258,12 @@ int mla_sparse_decode(const void* q, int q_dtype, int64_t num_tokens,
  *
  * Arguments are those of mla_sparse_decode without the workspace.  Limits
  * of the scratch: at most MLA_NOALLOC_MAX_UNITS (token, head group) units
- * (T * H / 32 rounded up to H >= 32 groups), and the split partials
- * (T * ceil(H/32) * num_splits * 32 KiB plus their log-sum-exps) within
- * MLA_NOALLOC_SCRATCH_BYTES - 256 KiB; a call beyond either returns
- * MLA_ERR_WORKSPACE and enqueues nothing.  The first call on a device also
- * enqueues, on its stream and before its decode, a small kernel that zeroes
- * the scratch's arrival counters.
+ * (T * H / 32 rounded up to H >= 32 groups; 64 bytes of arrival state
+ * each), and the split partials (T * ceil(H/32) * num_splits * 32 KiB plus
+ * their log-sum-exps) within MLA_NOALLOC_SCRATCH_BYTES - 4 MiB; a call
+ * beyond either returns MLA_ERR_WORKSPACE and enqueues nothing.  The first
+ * call on a device also enqueues, on its stream and before its decode, a
+ * small kernel that zeroes the scratch's arrival state.
  *
  * Every call on a GPU shares that GPU's scratch: calls that overlap in time
  * on one GPU (different streams without ordering between them) race and

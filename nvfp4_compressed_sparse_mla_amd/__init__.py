@@ -138,6 +138,16 @@ def num_splits(tokens: int, heads: int, topk: int) -> int:
     return int(load().mla_sparse_decode_num_splits(tokens, heads, topk))
 
 
+def set_merge_polls(polls: int) -> int:
+    """How many times a split polls for the others before leaving its slice of
+    the merge to the last arrival (0 = the last arrival merges everything).
+    Process-wide; returns the previous value."""
+    prev = int(load().mla_sparse_decode_set_merge_polls(int(polls)))
+    if prev < 0:
+        raise ValueError("polls must be >= 0")
+    return prev
+
+
 def workspace_size(tokens: int, heads: int, topk: int, splits: int = 0) -> int:
     n = int(load().mla_sparse_decode_workspace_size(tokens, heads, topk, splits))
     if n == 0:

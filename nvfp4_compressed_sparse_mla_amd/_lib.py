@@ -21,6 +21,7 @@ SIGNATURES = {
     "mla_fp8_quantize_append": (c_int, [c_vp, c_i64, c_vp, c_i64, c_int, c_i64, c_vp, c_vp, c_i64, c_f32, c_vp]),
     "mla_sparse_decode_num_splits": (c_i32, [c_i64, c_i32, c_i32]),
     "mla_sparse_decode_workspace_size": (c_size, [c_i64, c_i32, c_i32, c_i32]),
+    "mla_sparse_decode_set_merge_polls": (c_i32, [c_i32]),
     "mla_sparse_decode": (c_int, [c_vp, c_int, c_i64, c_i32, c_i64, c_i64,
                                   c_vp, c_int, c_i64, c_f32,
                                   c_vp, c_i32, c_i64,

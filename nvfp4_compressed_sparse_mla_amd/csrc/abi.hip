@@ -7,11 +7,18 @@
 
 #include <math.h>
 
+#include <atomic>
 #include <mutex>
 
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// How many times a split polls for the other splits' arrival before it
+// leaves its slice of the merge to the last arrival (see mla_sparse_decode_
+// set_merge_polls).  Each poll is a short sleep and one agent-scope load,
+// about a microsecond; 256 polls bound the wait to a few hundred.
+std::atomic<int> g_merge_polls{256};
 
 bool pow2_scale(float s) {
   if (!(s > 0.0f) || !isfinite(s)) return false;
@@ -73,11 +80,11 @@ int quantize_checks(const void* latent, int64_t ls, const void* rope, int64_t rs
 }
 
 // Size of the allocation-free entry point's scratch array (see below): the
-// arrival counters of up to kScratchCounters (token, head group) units,
-// then the split partials.
+// arrival state (64 bytes) of up to kScratchCounters (token, head group)
+// units, then the split partials.
 constexpr size_t kScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
 constexpr int64_t kScratchCounters = MLA_NOALLOC_MAX_UNITS;  // (token, head group) units per call
-constexpr size_t kScratchCounterBytes = kScratchCounters * sizeof(uint32_t);
+constexpr size_t kScratchCounterBytes = kScratchCounters * 64;
 static_assert(kScratchCounterBytes % 256 == 0, "partials stay 256-byte aligned");
 
 // Shared body of the two decode entry points.  With static_layout the
@@ -135,7 +142,7 @@ int decode_call(const void* q, int q_dtype, int64_t num_tokens, int32_t num_head
     const size_t need = mla::decode_workspace_bytes(num_tokens, num_heads, S);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
     if (check_only) return MLA_OK;
-    const size_t ctr = ((size_t)tg * sizeof(uint32_t) + 255) & ~(size_t)255;
+    const size_t ctr = ((size_t)tg * 64 + 255) & ~(size_t)255;
     counters = reinterpret_cast<uint32_t*>(workspace);
     part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ctr);
   }
@@ -172,6 +179,7 @@ int decode_call(const void* q, int q_dtype, int64_t num_tokens, int32_t num_head
   p.part_lse = part_lse;
   p.part_o = part_o;
   p.S = S;
+  p.merge_polls = g_merge_polls.load(std::memory_order_relaxed);
   const mla::KernelEvents ev = timing_events();
   return launched(mla::launch_decode(p, cache_fmt, q_dtype == MLA_BF16, (hipStream_t)stream, ev), ev);
 }
@@ -204,7 +212,7 @@ int static_scratch(hipStream_t stream, void** ptr) {
   std::call_once(slot.once, [&] {
     void* p = nullptr;
     if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return;
-    if (mla::launch_zero_u32(static_cast<uint32_t*>(p), (size_t)kScratchCounters, stream) != hipSuccess)
+    if (mla::launch_zero_u32(static_cast<uint32_t*>(p), kScratchCounterBytes / sizeof(uint32_t), stream) != hipSuccess)
       return;
     slot.ptr = p;
     slot.status = MLA_OK;
@@ -286,6 +294,11 @@ size_t mla_sparse_decode_workspace_size(int64_t num_tokens, int32_t num_heads, i
   if (num_splits < 0 || num_splits > 64) return 0;
   const int S = num_splits ? num_splits : mla::decode_auto_splits(num_tokens, num_heads, topk);
   return mla::decode_workspace_bytes(num_tokens, num_heads, S);
+}
+
+int32_t mla_sparse_decode_set_merge_polls(int32_t polls) {
+  if (polls < 0) return -1;
+  return g_merge_polls.exchange(polls, std::memory_order_relaxed);
 }
 
 int mla_sparse_decode(const void* q, int q_dtype, int64_t num_tokens, int32_t num_heads,

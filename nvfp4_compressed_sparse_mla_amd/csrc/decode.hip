@@ -136,9 +136,12 @@ __device__ __forceinline__ uint32_t lds_off(const void* p) {
 #define MLA_DEVICE_ASM(...) asm volatile(__VA_ARGS__)
 // (the immediate offset is added to both the global and the LDS address)
 #define MLA_DMA16(src, lds, off) __builtin_amdgcn_global_load_lds((src), (lds), 16, (off), 0)
+// (aux 16: the sc1 cache policy, agent scope)
+#define MLA_DMA_AGENT(src, lds) __builtin_amdgcn_global_load_lds((src), (lds), 16, 0, 16)
 #else
 #define MLA_DEVICE_ASM(...) __builtin_unreachable()
 #define MLA_DMA16(src, lds, off) ((void)(src), (void)(lds))
+#define MLA_DMA_AGENT(src, lds) ((void)(src), (void)(lds))
 #endif
 
 // f(integral_constant<int, J>) for J = I .. N-1
@@ -160,6 +163,11 @@ template <int kOff = 0>
 __device__ __forceinline__ u32x2 ring_b64(uint32_t a) {
   u32x2 v;
   MLA_DEVICE_ASM("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(kOff));
+  return v;
+}
+__device__ __forceinline__ u32x4 lds_b128(uint32_t a) {
+  u32x4 v;
+  MLA_DEVICE_ASM("ds_read_b128 %0, %1" : "=v"(v) : "v"(a));
   return v;
 }
 template <int kOff = 0>
@@ -311,36 +319,37 @@ __device__ __forceinline__ void store8(T* dst, const float (&v)[8]) {
   *reinterpret_cast<u32x4*>(dst) = w;
 }
 
+
 // Split partials cross workgroups (and L2 caches): they are written with
 // the agent-scope cache policy (sc1, what an agent-scope atomic store
 // uses), which writes through this XCD's L2, so the writer needs no
-// L2-wide writeback before counting its arrival.  One 16-byte store; in
-// assembly, so the caller waits for it itself (s_waitcnt vmcnt(0) right
-// after its last store).  A store of more than 8 bytes reads its data
-// registers after it issues, and a VALU write to them needs wait states
-// after it (the store-data hazard); the compiler does not see this store,
-// so the wait states are part of the statement: without them the next
-// instruction may reuse the data registers while the late lanes' data is
-// still being read.
-__device__ __forceinline__ void store8_agent(half_t* dst, const float (&v)[8]) {
-  u32x4 w;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = as_u32((half2_t){(half_t)v[2 * i], (half_t)v[2 * i + 1]});
-  MLA_DEVICE_ASM("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" :: "v"(dst), "v"(w) : "memory");
+// L2-wide writeback before counting its arrival.  Four FP16 values (8
+// bytes) per store; in assembly, so the caller waits for it itself (s_waitcnt
+// vmcnt(0) after its last store).  The compiler does not see this store, so
+// the statement carries two wait states for its data registers (a store
+// reads them after it issues; a VALU write to them right after could
+// change the data of the late lanes).
+__device__ __forceinline__ void store4_agent(half_t* dst, float a, float b, float c, float d) {
+  const u32x2 w = {as_u32((half2_t){(half_t)a, (half_t)b}), as_u32((half2_t){(half_t)c, (half_t)d})};
+  MLA_DEVICE_ASM("global_store_dwordx2 %0, %1, off sc1\n\ts_nop 1" :: "v"(dst), "v"(w) : "memory");
+}
+// two consecutive output elements (4-byte aligned), fp16 or bf16
+template <bool kBf16, typename T>
+__device__ __forceinline__ void store2(T* dst, float a, float b) {
+  uint32_t w;
+  if constexpr (kBf16) w = (uint32_t)float_to_bf16_rne(a) | ((uint32_t)float_to_bf16_rne(b) << 16);
+  else w = as_u32((half2_t){(half_t)a, (half_t)b});
+  *reinterpret_cast<uint32_t*>(dst) = w;
 }
 
-// The merge's reads of the other splits' results: 16-byte loads with the
-// agent-scope policy (sc1, what an agent-scope atomic load uses), coherent
-// at agent scope by themselves, so no cache invalidation is needed before
-// them.  In assembly (the caller waits with vmcnt and ties the registers).
+// A load of another workgroup's result: 16 bytes with the agent-scope
+// policy (sc1, what an agent-scope atomic load uses), coherent at agent
+// scope by itself, so no cache invalidation is needed before it.  In
+// assembly (the caller waits with vmcnt and ties the registers).
 __device__ __forceinline__ u32x4 load16_agent(const void* src) {
   u32x4 v;
   MLA_DEVICE_ASM("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(src) : "memory");
   return v;
-}
-template <typename T>
-__device__ __forceinline__ void tie4(T& a, T& b, T& c, T& d) {
-  MLA_DEVICE_ASM("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
@@ -461,12 +470,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   // 8-byte writes) fall in distinct banks
   __shared__ __align__(16) half_t pbuf[kSW][kHG][kPRow];
   __shared__ __align__(16) float ref_s[kSW][kHG];           // the reference each tile's P is relative to
-  __shared__ int phys[kMaxTopk];
+  __shared__ __align__(16) int phys[kMaxTopk];
   // per head: the score waves' final references (base 2), then their row sums
   __shared__ __align__(16) float wml_s[kHG][2 * kSW];
   __shared__ __align__(16) float fac_s[kVW][kHG];           // per value wave: per-head factors
   __shared__ __align__(16) int cnt_s[kSlices][kVW];   // valid slots per (slice, value wave)
-  __shared__ int last_s;
+  __shared__ uint64_t won_s;
+  __shared__ int role_s;
+  __shared__ uint32_t epoch_s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Every kernel argument the prologue uses, in registers before anything
@@ -770,14 +781,6 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
   auto xregion = [&](int j) -> uint8_t* {
     return (j < 2 ? ring_all : reinterpret_cast<uint8_t*>(vbuf_all)) + (j & 1) * kXRegion;
   };
-  // A split's partial is kept in the order its value waves' lanes hold it
-  // after the exchange (value wave j, pass u, head 4hq + h of the lane's
-  // quad: 64 lanes x 16 bytes), so that every store and every merge load is
-  // one contiguous kilobyte per wave
-  auto part_slice = [&](int x, int j, int u, int h) -> half_t* {
-    return p.part_o + ((((tg * S + x) * kVW + j) * 2 + u) * 4 + h) * (64 * 8) + 8 * lane;
-  };
-
   if (wave < kSW) {
     // ============================================================ score wave
     // q's B operands into registers (inside this branch, so that they take
@@ -811,6 +814,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
     // (the score waves' instructions win issue arbitration against the value
     // waves' on the same SIMD: the score waves' chain sets the round time)
     __builtin_amdgcn_s_setprio(1);
+#pragma unroll 1
     for (int i = 0; i < rounds; ++i) {
       const bool have = i < my_tiles;     // (only the last round can miss a tile)
       const int k = sw + kSW * i;         // tile index within the split
@@ -979,6 +983,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
       const int e = (j + kSW * (m + kDepth)) * kRowsT + r16;
       return lds_off(&phys[r0 + (e < n ? e : n - 1)]);
     };
+#pragma unroll 1
     for (int i = 0; i < rounds; ++i) {
       const int nt = ntiles - kSW * i < kSW ? ntiles - kSW * i : kSW;   // tiles in this round
       uint32_t refill_row = 0;
@@ -1063,216 +1068,272 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_decode_kernel(DecodeParams
       if (S > 1) __hip_atomic_store(p.part_lse + (tg * S + s) * kHG + hl, lse2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else if (head < p.H && p.lse) p.lse[t * H + head] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
     }
-    // normalise this wave's columns, then store them through its exchange
-    // region: block (c * 4 + q) holds, in slot L, heads 8q + 4(L >> 5) +
-    // [0,4) of column 32c + (L & 31); a reader takes heads 4hq + [0,4) x
-    // columns 8co + [0,8) (8 consecutive slots of one block) and stores
-    // 16-byte rows of 8 columns per head.
-    if (lane < 32) fac_s[j][hl] = inv * (S > 1 ? 1.0f : out_mul);
     float fo[16];
-    read_factors(fo);
-    uint8_t* const xr = xregion(j);
-    uint8_t* const xw = xr + 16 * lane + 32 * (lane >> 4);
+    if (S > 1) {
+      // S > 1: the normalised partial goes to memory in the order the MFMA
+      // accumulators hold it: piece ((j * 4 + c) * 4 + e) * 64 + lane (8
+      // bytes) holds heads 8e + 4 (lane >> 5) + [0,4) of column 128 j +
+      // 32 c + (lane & 31), so each store instruction writes 512 contiguous
+      // bytes and no exchange through LDS is needed.
+      if (lane < 32) fac_s[j][hl] = inv;
+      read_factors(fo);
+      half_t* const pd = p.part_o + (tg * S + s) * (kHG * kLatent) + 4 * (j * 16 * 64 + lane);
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4_t*>(xw + (c * 4 + q) * kXBlock) =
-            (float4_t){acc[c][4 * q] * fo[4 * q], acc[c][4 * q + 1] * fo[4 * q + 1],
-                       acc[c][4 * q + 2] * fo[4 * q + 2], acc[c][4 * q + 3] * fo[4 * q + 3]};
-    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" ::: "memory");
+        for (int e = 0; e < 4; ++e)
+          store4_agent(pd + 4 * 64 * (c * 4 + e), acc[c][4 * e] * fo[4 * e], acc[c][4 * e + 1] * fo[4 * e + 1],
+                       acc[c][4 * e + 2] * fo[4 * e + 2], acc[c][4 * e + 3] * fo[4 * e + 3]);
+    } else {
+      // S == 1: normalise this wave's columns, then store them through its
+      // exchange region: block (c * 4 + q) holds, in slot L, heads 8q +
+      // 4(L >> 5) + [0,4) of column 32c + (L & 31); a reader takes heads
+      // 4hq + [0,4) x columns 8co + [0,8) (8 consecutive slots of one block)
+      // and stores 16-byte rows of 8 columns per head.
+      if (lane < 32) fac_s[j][hl] = inv * out_mul;
+      read_factors(fo);
+      uint8_t* const xr = xregion(j);
+      uint8_t* const xw = xr + 16 * lane + 32 * (lane >> 4);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int hq = lane & 7, co = (lane >> 3) + 8 * u;
-      const uint32_t rslot = 32 * (hq & 1) + 8 * (co & 3);
-      const uint8_t* const src = xr + ((co >> 2) * 4 + (hq >> 1)) * kXBlock + 16 * rslot + 32 * (rslot >> 4);
-      float o[4][8];
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const float4_t v = *reinterpret_cast<const float4_t*>(src + 16 * x);
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4_t*>(xw + (c * 4 + q) * kXBlock) =
+              (float4_t){acc[c][4 * q] * fo[4 * q], acc[c][4 * q + 1] * fo[4 * q + 1],
+                         acc[c][4 * q + 2] * fo[4 * q + 2], acc[c][4 * q + 3] * fo[4 * q + 3]};
+      MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int h = 0; h < 4; ++h) o[h][x] = v[h];
-      }
+      for (int u = 0; u < 2; ++u) {
+        const int hq = lane & 7, co = (lane >> 3) + 8 * u;
+        const uint32_t rslot = 32 * (hq & 1) + 8 * (co & 3);
+        const uint8_t* const src = xr + ((co >> 2) * 4 + (hq >> 1)) * kXBlock + 16 * rslot + 32 * (rslot >> 4);
+        float o[4][8];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const int hd = 4 * hq + h, head = g * kHG + hd;
-        const int col = kVCols * j + 8 * co;
-        if (S > 1) store8_agent(part_slice(s, j, u, h), o[h]);
-        else if (head < p.H)
-          store8<kBf16>(reinterpret_cast<uint16_t*>(p.out) + (t * H + head) * kLatent + col, o[h]);
+        for (int x = 0; x < 8; ++x) {
+          const float4_t v = *reinterpret_cast<const float4_t*>(src + 16 * x);
+#pragma unroll
+          for (int h = 0; h < 4; ++h) o[h][x] = v[h];
+        }
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int head = g * kHG + 4 * hq + h;
+          if (head < p.H)
+            store8<kBf16>(reinterpret_cast<uint16_t*>(p.out) + (t * H + head) * kLatent + kVCols * j + 8 * co, o[h]);
+        }
       }
     }
   }
   if (S == 1) return;
 
-  // Count arrivals once every wave's partial stores are complete (each wave
-  // waits for its own; the barrier orders them before the count); the last
-  // arrival merges.  Why a relaxed count suffices (AMDGPU memory model,
-  // GFX942/GFX950): an agent-scope release is "buffer_wbl2 sc1" (write back
-  // the L2 lines that plain stores left dirty) followed by "s_waitcnt
-  // vmcnt(0)".  Everything this protocol publishes (partials and
-  // log2-sum-exps) is stored with the agent-scope policy sc1, the one the
-  // model uses for agent-scope atomic stores, so nothing of it is dirty in
-  // L2; the vmcnt wait below completes those stores before the count, which
-  // is all that remains of the release.  The merging split reads the
-  // results with agent-scope loads (sc1), which see them without an acquire
-  // fence's cache invalidation: these loads are issued only after its count
-  // has returned, and that count follows every other split's count.
+  // Arrival and merge.  A split's partial (2,048 units of 16 bytes) is cut
+  // into S slices, slice k = units [2048 k / S, 2048 (k + 1) / S), and split
+  // k merges slice k, so that the merge's loads and arithmetic are spread
+  // over the S workgroups instead of falling on one.  Per (token, head group)
+  // the workspace holds 64 bytes: an arrival word (an epoch in the high 32
+  // bits, the current call's arrivals in the low 32) and, for each epoch
+  // parity, a mask of the slices whose owners merge them and a mask of those
+  // whose owners left them.
+  //   * Once every wave's partial stores are complete (each wave waits for
+  //     its own; the barrier orders them before the count), thread 0 counts
+  //     the split's arrival; the count returns the call's epoch E.
+  //   * The last of the S arrivals moves the arrival word to (E + 1, 0) (the
+  //     signal that every partial is complete, and the state the next call
+  //     starts from), clears the next epoch's masks, and merges its own
+  //     slice.  It then waits, a bounded number of polls, until every other
+  //     owner has either taken or left its slice, and merges the slices that
+  //     were left or are still undecided.
+  //   * Every other split polls the arrival word, a bounded number of times,
+  //     until its epoch moves past E; it then marks its slice taken and
+  //     merges it, or else marks it left and merges nothing.
+  // Every wait is bounded, and no workgroup depends on another being
+  // resident: a slice is merged by its owner, by the last arrival, or (when
+  // the last arrival stops waiting first) by both, which write the same
+  // values.
+  //
+  // Why relaxed atomics suffice (AMDGPU memory model, GFX942/GFX950): an
+  // agent-scope release is "buffer_wbl2 sc1" (write back the L2 lines that
+  // plain stores left dirty) followed by "s_waitcnt vmcnt(0)".  Everything
+  // this protocol publishes (partials and log2-sum-exps) is stored with the
+  // agent-scope policy sc1, the one the model uses for agent-scope atomic
+  // stores, so nothing of it is dirty in L2; the vmcnt wait below completes
+  // those stores before the count, which is all that remains of the
+  // release.  A merging split reads the results with agent-scope loads
+  // (sc1), which see them without an acquire fence's cache invalidation:
+  // they are issued only after the split has seen the epoch move (or was
+  // the last arrival), which follows every split's count, each of which
+  // follows the completion of that split's stores.  The masks only decide
+  // who merges; a stale view of them costs at most a repeated merge.
   MLA_DEVICE_ASM("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  uint32_t* ctr = p.counters + tg;
+  uint64_t* const state = reinterpret_cast<uint64_t*>(p.counters) + 8 * tg;   // 64 bytes per unit
+  const uint64_t all = S == 64 ? ~0ull : (1ull << S) - 1ull;
+  const bool shared_merge = p.merge_polls > 0;
   if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = old == (uint32_t)S - 1u;
-    if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
-    last_s = last;
+    const uint64_t old = __hip_atomic_fetch_add(state, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t epoch = (uint32_t)(old >> 32);
+    uint64_t* const taken = state + 1 + (epoch & 1u), * const left = state + 3 + (epoch & 1u);
+    int role = 0;   // 0: nothing to merge, 1: owner, 2: last arrival
+    if ((uint32_t)old == (uint32_t)S - 1u) {
+      __hip_atomic_store(state, (uint64_t)(epoch + 1u) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(state + 1 + ((epoch + 1u) & 1u), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(state + 3 + ((epoch + 1u) & 1u), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      role = 2;
+    } else if (shared_merge) {
+      bool moved = false;
+      for (int i = 0; i < p.merge_polls && !moved; ++i) {
+        __builtin_amdgcn_s_sleep(1);
+        moved = (uint32_t)(__hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) != epoch;
+      }
+      __hip_atomic_fetch_or(moved ? taken : left, 1ull << s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      role = moved ? 1 : 0;
+    }
+    role_s = role;
+    epoch_s = epoch;
   }
   __syncthreads();
-  if (!last_s) return;
+  const int role = role_s;
+  if (role == 0) return;
 
-  // The merge, by all eight waves: wave w takes the slice that value wave
-  // j = w / 2 stored in its pass u = w mod 2 (heads 4hq + [0,4) x columns
-  // 128j + 8co + [0,8), hq = lane mod 8, co = lane / 8 + 8u), so that this
-  // split's own partial comes from j's exchange region in LDS (rounded to
-  // FP16 as it was stored) and only the other splits' partials are read
-  // from memory.  Per batch of up to kBatch splits a lane loads its heads'
-  // log2-sum-exps (one 16-byte load per split) and then the partials, so
-  // that a batch waits for one memory round trip, and it derives the merge
-  // weights itself (no barrier).  Splits are summed in index order.
-  constexpr int kBatch = 8;                  // splits whose partials are in flight together
-  const int mj = wave >> 1, hq = lane & 7, co = (lane >> 3) + 8 * (wave & 1);
-  const int col = kVCols * mj + 8 * co;
-  const float* pl = p.part_lse + tg * S * kHG + 4 * hq;                    // split x: + x kHG
-  float4_t lb[kBatch];
-  half8_t part[kBatch][4];
-  auto load_lse = [&](int x0) {
-    static_for<0, kBatch>([&](auto X) {
-      constexpr int x = decltype(X)::value;
-      if (x0 + x < S) lb[x] = __builtin_bit_cast(float4_t, load16_agent(pl + (x0 + x) * kHG));
-    });
-  };
-  auto load_parts = [&](int x0) {
-    static_for<0, kBatch>([&](auto X) {
-      constexpr int x = decltype(X)::value;
-      if (x0 + x < S && x0 + x != s) {
+  // The merge of a range of units.  Unit u (16 bytes) of a partial holds
+  // heads h0 = 8 e + 4 (m >> 4) + [0,4) (e = (u >> 5) & 3, m = u & 31) at
+  // columns c0 = 128 (u >> 9) + 32 ((u >> 7) & 3) + 2 (m & 15) and c0 + 1
+  // (bytes [0,8) and [8,16)).  A thread takes kNU consecutive units (kNU = 4:
+  // the same four heads at eight consecutive columns, 64 contiguous bytes
+  // per split) and, eight splits at a time with all of a batch in flight
+  // together, loads each split's log2-sum-exps of the four heads and its
+  // pieces of the units.  Per head it keeps the largest log2-sum-exp so far,
+  // M, rescales what it has summed when M rises, and adds the pieces with
+  // the weights 2^(lse - M) (splits in index order; an empty split, lse =
+  // -inf, adds nothing).  Contraction is off, so that the same sums come out
+  // whichever instance of this code, and whichever split, merges a unit.
+  constexpr int kBatch = 8;
+  const half_t* const pbase = p.part_o + tg * S * (kHG * kLatent);
+  const float* const lbase = p.part_lse + tg * S * kHG;
+  auto merge_range = [&](auto NUc, int ga, int gb) {   // unit groups [ga, gb) of kNU units
+#pragma clang fp contract(off)
+    constexpr int kNU = decltype(NUc)::value;
+#pragma unroll 1
+    for (int gi = ga + tid; gi < gb; gi += kThreads) {
+      const int u = gi * kNU;
+      const int h0 = 8 * ((u >> 5) & 3) + 4 * ((u >> 4) & 1);
+      const int c0 = 128 * (u >> 9) + 32 * ((u >> 7) & 3) + 2 * (u & 15);
+      float mx[4], sum[4], a[kNU][4][2];
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
-          part[x][h] = __builtin_bit_cast(half8_t, load16_agent(part_slice(x0 + x, mj, wave & 1, h)));
+      for (int h = 0; h < 4; ++h) {
+        mx[h] = kNegInf;
+        sum[h] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kNU; ++i) a[i][h][0] = a[i][h][1] = 0.0f;
       }
-    });
-  };
-  // (all of a batch's loads complete; the ties keep every use of their
-  // registers behind the wait)
-  auto wait_loads = [&]() {
-    MLA_DEVICE_ASM("s_waitcnt vmcnt(0)" ::: "memory");
-    tie4(lb[0], lb[1], lb[2], lb[3]);
-    tie4(lb[4], lb[5], lb[6], lb[7]);
-    static_for<0, kBatch>([&](auto X) {
-      constexpr int x = decltype(X)::value;
-      tie4(part[x][0], part[x][1], part[x][2], part[x][3]);
-    });
-  };
-  // log2 of sum_x 2^lse_x per head, against the running maximum (in split
-  // order; 2^(-inf - finite) is 0, so an empty split adds nothing)
-  float mx[4], sum[4];
+#pragma unroll 1
+      for (int x0 = 0; x0 < S; x0 += kBatch) {
+        u32x4 pv[kBatch][kNU], lv[kBatch];
+        static_for<0, kBatch>([&](auto X) {
+          constexpr int x = decltype(X)::value;
+          if (x0 + x < S) {
+            lv[x] = load16_agent(lbase + (x0 + x) * kHG + h0);
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    mx[h] = kNegInf;
-    sum[h] = 0.0f;
-  }
-  auto lse_batch = [&](int x0) {
+            for (int i = 0; i < kNU; ++i) pv[x][i] = load16_agent(pbase + ((x0 + x) * 2048 + u + i) * 8);
+          }
+        });
+        MLA_DEVICE_ASM("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      float bm = mx[h];
+        for (int x = 0; x < kBatch; ++x) {
+          MLA_DEVICE_ASM("" : "+v"(lv[x]));
 #pragma unroll
-      for (int x = 0; x < kBatch; ++x)
-        if (x0 + x < S) bm = __builtin_fmaxf(bm, lb[x][h]);
-      if (bm != kNegInf) {
-        float sx = mx[h] == kNegInf ? 0.0f : sum[h] * __builtin_amdgcn_exp2f(mx[h] - bm);
-#pragma unroll
-        for (int x = 0; x < kBatch; ++x)
-          if (x0 + x < S) sx += __builtin_amdgcn_exp2f(lb[x][h] - bm);
-        sum[h] = sx;
-      }
-      mx[h] = bm;
-    }
-  };
-  if (S <= kBatch) {
-    load_lse(0);
-    load_parts(0);
-  } else {
-    for (int x0 = 0; x0 < S; x0 += kBatch) {
-      load_lse(x0);
-      wait_loads();
-      lse_batch(x0);
-    }
-    load_lse(0);
-    load_parts(0);
-  }
-  // this split's own partial, as stored (the exchange region's reader
-  // layout of the epilogue); an assembly read, so that no wait for the
-  // loads above is added in front of it
-  half8_t own[4];
-  {
-    const uint32_t rslot = 32 * (hq & 1) + 8 * (co & 3);
-    const uint32_t src = lds_off(xregion(mj) + ((co >> 2) * 4 + (hq >> 1)) * kXBlock + 16 * rslot + 32 * (rslot >> 4));
-    u32x4 v[8];
-    static_for<0, 8>([&](auto X) {
-      constexpr int x = decltype(X)::value;
-      v[x] = ring_b128<16 * x>(src);
-    });
-    MLA_DEVICE_ASM("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
-                   "+v"(v[6]), "+v"(v[7]));
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-#pragma unroll
-      for (int x = 0; x < 8; ++x) own[h][x] = (half_t)__uint_as_float(v[x][h]);
-  }
-  wait_loads();
-  if (S <= kBatch) lse_batch(0);
-  float inv[4];
-#pragma unroll
-  for (int h = 0; h < 4; ++h) inv[h] = mx[h] != kNegInf ? 1.0f / sum[h] : 0.0f;
-  float a[4][8];
-#pragma unroll
-  for (int h = 0; h < 4; ++h)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[h][i] = 0.0f;
-  for (int x0 = 0; x0 < S; x0 += kBatch) {
-    if (x0 > 0) {
-      load_lse(x0);
-      load_parts(x0);
-      wait_loads();
-    }
-    static_for<0, kBatch>([&](auto X) {
-      constexpr int x = decltype(X)::value;
-      if (x0 + x < S) {
-        const bool mine = x0 + x == s;
+          for (int i = 0; i < kNU; ++i) MLA_DEVICE_ASM("" : "+v"(pv[x][i]));
+        }
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          const float w = mx[h] != kNegInf ? __builtin_amdgcn_exp2f(lb[x][h] - mx[h]) * inv[h] : 0.0f;
-          const half8_t pv = mine ? own[h] : part[x][h];
-          // (a fused multiply-add per element taking its FP16 operand as is: v_fma_mix)
+          float bm = mx[h];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) a[h][i] = __builtin_fmaf(w, (float)pv[i], a[h][i]);
+          for (int x = 0; x < kBatch; ++x)
+            if (x0 + x < S) bm = __builtin_fmaxf(bm, __uint_as_float(lv[x][h]));
+          if (bm != kNegInf) {
+            const float f = mx[h] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mx[h] - bm);
+            sum[h] *= f;
+#pragma unroll
+            for (int i = 0; i < kNU; ++i) {
+              a[i][h][0] *= f;
+              a[i][h][1] *= f;
+            }
+#pragma unroll
+            for (int x = 0; x < kBatch; ++x) {
+              if (x0 + x < S) {
+                const float w = __builtin_amdgcn_exp2f(__uint_as_float(lv[x][h]) - bm);
+                sum[h] += w;
+#pragma unroll
+                for (int i = 0; i < kNU; ++i) {
+                  const half8_t v = __builtin_bit_cast(half8_t, pv[x][i]);
+                  a[i][h][0] = __builtin_fmaf(w, (float)v[h], a[i][h][0]);
+                  a[i][h][1] = __builtin_fmaf(w, (float)v[4 + h], a[i][h][1]);
+                }
+              }
+            }
+            mx[h] = bm;
+          }
         }
       }
-    });
-  }
-  if (wave == 0 && co == 0 && p.lse) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int head = g * kHG + 4 * hq + h;
-      if (head < p.H) p.lse[t * H + head] = mx[h] != kNegInf ? (mx[h] + __log2f(sum[h])) * kLn2 : kNegInf;
+      for (int h = 0; h < 4; ++h) {
+        const int head = g * kHG + h0 + h;
+        if (head < p.H) {
+          const float iv = mx[h] != kNegInf ? out_mul / sum[h] : 0.0f;
+          uint16_t* const dst = reinterpret_cast<uint16_t*>(p.out) + (t * H + head) * kLatent + c0;
+          if constexpr (kNU == 4) {
+            const float o[8] = {a[0][h][0] * iv, a[0][h][1] * iv, a[1][h][0] * iv, a[1][h][1] * iv,
+                                a[2][h][0] * iv, a[2][h][1] * iv, a[3][h][0] * iv, a[3][h][1] * iv};
+            store8<kBf16>(dst, o);
+          } else {
+            static_assert(kNU == 1, "units per thread: 1 or 4");
+            store2<kBf16>(dst, a[0][h][0] * iv, a[0][h][1] * iv);
+          }
+          if (c0 == 0 && p.lse) p.lse[t * H + head] = mx[h] != kNegInf ? (mx[h] + __log2f(sum[h])) * kLn2 : kNegInf;
+        }
+      }
     }
+  };
+
+  if (!shared_merge) {
+    // the last arrival merges every unit, four per thread
+    merge_range(std::integral_constant<int, 4>{}, 0, 2048 / 4);
+    return;
   }
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const int head = g * kHG + 4 * hq + h;
-    if (head >= p.H) continue;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[h][i] *= out_mul;
-    store8<kBf16>(reinterpret_cast<uint16_t*>(p.out) + (t * H + head) * kLatent + col, a[h]);
+
+  // Shared merge: the owners' slices, then (the last arrival) the slices
+  // left or still undecided.  One instance of the merge code for all of
+  // them, so that every slice is combined by the same instructions
+  // whoever merges it.
+  uint64_t todo = 1ull << s;
+  bool asked = role != 2;
+#pragma unroll 1
+  while (true) {
+    if (todo == 0) {
+      if (asked) break;
+      asked = true;
+      // The last arrival: wait until every other owner has taken or left
+      // its slice (each decides within its own bounded polling), then merge
+      // the slices left or still undecided.
+      if (tid == 0) {
+        const uint32_t epoch = epoch_s;
+        const uint64_t* const taken = state + 1 + (epoch & 1u), * const left = state + 3 + (epoch & 1u);
+        const uint64_t others = all & ~(1ull << s);
+        uint64_t t_m = 0, l_m = 0;
+        for (int i = 0; i < 4 * p.merge_polls + 64; ++i) {
+          t_m = __hip_atomic_load(taken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          l_m = __hip_atomic_load(left, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (((t_m | l_m) & others) == others) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        won_s = others & ~(t_m & ~l_m);
+      }
+      __syncthreads();
+      todo = won_s;
+      continue;
+    }
+    const int k = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    merge_range(std::integral_constant<int, 1>{}, (2048 * k) / S, (2048 * (k + 1)) / S);
   }
 }
 
@@ -1283,6 +1344,8 @@ __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* p, size_t n) {
 // ------------------------------------------------------------------ host side
 
 namespace {
+
+constexpr int kMinSharedMergeSplits = 4;
 
 int device_cus() {
   static thread_local int cached_dev = -1;
@@ -1326,7 +1389,9 @@ int decode_auto_splits(int64_t T, int H, int topk) {
 size_t decode_workspace_bytes(int64_t T, int H, int S) {
   const int G = H <= kHG ? 1 : H / kHG;
   const int64_t tg = T * G;
-  size_t ctr = (size_t)tg * sizeof(uint32_t);
+  // per (token, head group): 64 bytes of arrival state (arrival word, and
+  // the taken and left masks of both epoch parities)
+  size_t ctr = (size_t)tg * 64;
   ctr = (ctr + 255) & ~(size_t)255;
   if (S <= 1) return ctr;
   size_t pl = (size_t)tg * S * kHG * sizeof(float);
@@ -1348,6 +1413,14 @@ hipError_t launch_decode(const DecodeParams& p, int fmt, bool bf16, hipStream_t 
   const int64_t rounds_grouped = ((units + 7) / 8 * p.S + per_xcd - 1) / per_xcd;
   a.xcd_shift = p.S > 1 && rounds_grouped <= rounds_plain ? 3 : 0;
   const int64_t blocks = a.xcd_shift ? (units + 7) / 8 * 8 * p.S : units * p.S;
+  // A split waits for the others only if the whole grid can be resident at
+  // once (one workgroup per CU); otherwise a waiting split could hold a CU
+  // that a later split needs, so none waits and the last arrival merges all.
+  if (blocks > cus) a.merge_polls = 0;
+  // With few splits the merge is small and a shared one costs more (the
+  // owners' wait for the last arrival) than it spreads: the last arrival
+  // merges everything in one pass.
+  if (p.S < kMinSharedMergeSplits) a.merge_polls = 0;
   dim3 grid((unsigned)blocks), block(kThreads);
   void* args[] = {&a};
   const void* fn;

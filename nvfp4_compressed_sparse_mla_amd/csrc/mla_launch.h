@@ -42,10 +42,11 @@ struct DecodeParams {
   int q_neg;                // sm_scale < 0: q is negated on load (exact), so sm_log2 >= 0
   void* out;
   float* lse;
-  uint32_t* counters;       // [T*G] arrivals per (token, head group)
+  uint32_t* counters;       // [T*G] x 64 bytes: arrival state per (token, head group)
   float* part_lse;          // [T*G][S][32]
   _Float16* part_o;         // [T*G][S][32 x 512], in the order the kernel's lanes hold it
   int S;                    // splits per (token, head group)
+  int merge_polls;          // polls of the arrival word before a split leaves its slice to the last arrival
   int xcd_shift;            // set by launch_decode: 3 = a unit's splits share an XCD, 0 = plain order
 };
 

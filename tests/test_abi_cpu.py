@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -100,15 +100,20 @@ def test_decode_rejects_bad_arguments(lib):
 
 
 def test_workspace_size_arithmetic(lib):
-    # one split: only the arrival counters (T*G u32) rounded up to 256 bytes
-    assert lib.mla_sparse_decode_workspace_size(15, 32, 2048, 1) == 256
-    assert lib.mla_sparse_decode_workspace_size(100, 32, 2048, 1) == 512
-    # S splits add an lse block [T*G*S*32] f32 and an O block [T*G*S*32*512] fp16
-    s = 4
-    lse = 15 * s * 32 * 4
-    expect = 256 + ((lse + 255) // 256) * 256 + 15 * s * 32 * 512 * 2
-    assert lib.mla_sparse_decode_workspace_size(15, 32, 2048, s) == expect
-    assert lib.mla_sparse_decode_workspace_size(15, 64, 2048, 1) == 256       # 2 head groups
+    # one split: only the arrival state (64 bytes per (token, head group))
+    # rounded up to 256 bytes
+    assert lib.mla_sparse_decode_workspace_size(15, 32, 2048, 1) == 1024
+    assert lib.mla_sparse_decode_workspace_size(100, 32, 2048, 1) == 6400
+    # S splits add an lse block [T*G*S*32] f32 and an O block [T*G*S*32*512]
+    # fp16, each part rounded to 256 bytes
+    def expect(t, g, s):
+        ctr = ((t * g * 64 + 255) // 256) * 256
+        lse = ((t * g * s * 32 * 4 + 255) // 256) * 256
+        return ctr + lse + t * g * s * 32 * 512 * 2
+    assert lib.mla_sparse_decode_workspace_size(15, 32, 2048, 4) == expect(15, 1, 4)
+    assert lib.mla_sparse_decode_workspace_size(100, 32, 2048, 4) == expect(100, 1, 4)
+    assert lib.mla_sparse_decode_workspace_size(100, 64, 2048, 3) == expect(100, 2, 3)
+    assert lib.mla_sparse_decode_workspace_size(15, 64, 2048, 1) == 2048      # 2 head groups
     assert lib.mla_sparse_decode_workspace_size(15, 24, 2048, 1) == 0
     assert lib.mla_sparse_decode_workspace_size(15, 32, 0, 1) == 0
     assert lib.mla_sparse_decode_workspace_size(15, 32, 2048, 99) == 0
@@ -141,7 +146,7 @@ def test_noalloc_decode_rejects_bad_arguments_and_oversized_calls(lib):
     assert call(4, 33, 16, 1) == UNSUPPORTED
     assert call(4, 32, 0, 1) == INVALID
     assert call(4, 32, 16, 1, fmt=7) == UNSUPPORTED
-    assert call(70000, 32, 2048, 1) == WORKSPACE        # more units than arrival counters
+    assert call(70000, 32, 2048, 1) == WORKSPACE        # more units than arrival states
     assert call(1000, 32, 2048, 2) == WORKSPACE         # partials past the scratch array
     assert call(300, 32, 2048, 4) == WORKSPACE
 
@@ -183,3 +188,14 @@ def test_gather_probe_rejects_bad_arguments(lib):
     assert call(rows=None) == INVALID and call(sink=None) == INVALID
     assert call(cache=ctypes.c_void_p((1 << 20) + 8)) == INVALID     # cache not 16-byte aligned
     assert call(rows_n=1 << 31) == INVALID
+
+
+def test_merge_polls_setting(lib):
+    prev = lib.mla_sparse_decode_set_merge_polls(7)
+    try:
+        assert prev >= 0
+        assert lib.mla_sparse_decode_set_merge_polls(0) == 7
+        assert lib.mla_sparse_decode_set_merge_polls(-3) == -1      # rejected, unchanged
+        assert lib.mla_sparse_decode_set_merge_polls(5) == 0
+    finally:
+        lib.mla_sparse_decode_set_merge_polls(prev)

@@ -132,8 +132,41 @@ def test_workspace_reuse_across_calls():
     for _ in range(3):
         again = _run(w, cache, num_splits=6, workspace=ws)
         assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1])
-    # the counters are back to zero after every call
-    assert torch.all(ws[:256] == 0)
+    # per (token, head group), 64 bytes: the arrival word (epoch << 32 |
+    # arrivals), then the taken and left masks of each epoch parity.  After
+    # every call the arrivals are back at zero and the epoch has moved once
+    # per call; the last call (epoch 3, odd) has every slice but the last
+    # arrival's own taken or left, and the next call's masks are clear.
+    state = ws[:5 * 64].view(torch.int64).view(5, 8).cpu()
+    assert torch.all(state[:, 0] == (4 << 32)), state
+    for row in state.tolist():
+        marked = row[2] | row[4]
+        assert 0 <= marked < (1 << 6) and bin(marked).count("1") == 5, state
+        assert row[1] == 0 and row[3] == 0, state
+
+
+@pytest.mark.parametrize("tokens,splits", [(15, 8), (35, 7), (128, 2), (1, 64), (3, 3)])
+def test_merge_split_between_splits_or_by_the_last_arrival(tokens, splits):
+    # The slices of the split merge are combined by their own splits (they
+    # wait for the others' arrival) or, with no waiting, all by the last
+    # arrival: the same arithmetic in the same order, so the results are
+    # bit-identical.  Polls of 1 leave most slices to the last arrival's
+    # claim, which mixes both.
+    w = make_custom(50000, tokens, 32, 2048, seed=30 + tokens, device=DEV)
+    cache = _fill(w)
+    ws = mla.make_workspace(tokens, 32, 2048, DEV, splits=splits)
+    prev = mla.set_merge_polls(256)
+    try:
+        ref = _run(w, cache, num_splits=splits, workspace=ws)
+        _check(w, cache, *ref, tokens=[0, tokens - 1], what=f"S={splits}")
+        for polls in (0, 1, 256):
+            mla.set_merge_polls(polls)
+            got = _run(w, cache, num_splits=splits, workspace=ws)
+            assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), polls
+    finally:
+        mla.set_merge_polls(prev)
+    with pytest.raises(ValueError):
+        mla.set_merge_polls(-1)
 
 
 @pytest.mark.parametrize("heads", [16, 64, 128])
