@@ -60,10 +60,13 @@
 //             range); a higher reference first rescales O.
 //   epilogue  the value waves normalise their columns by the row sums of
 //             all score waves (weighted by 2^(m_w - M)); S == 1 stores the
-//             output, S > 1 stores the normalised partial (FP16) and its
-//             log2-sum-exp, and the split that finishes last for (t, g)
-//             merges all S partials.  Nothing waits on another workgroup, so
-//             no co-residency is needed.
+//             output, S > 1 stores the normalised partial (FP16, in the
+//             accumulators' order) and its log2-sum-exp.
+//   merge     (S > 1) once all S splits of (t, g) have arrived, split k
+//             combines slice k of the partials (from 4 splits up; with
+//             fewer, the last arrival combines everything).  Every wait is
+//             bounded and the last arrival combines whatever slice nobody
+//             took, so no co-residency is needed.
 #include "mla_device.h"
 #include "mla_launch.h"
 
