@@ -199,3 +199,16 @@ def test_merge_polls_setting(lib):
         assert lib.mla_sparse_decode_set_merge_polls(5) == 0
     finally:
         lib.mla_sparse_decode_set_merge_polls(prev)
+
+
+def test_launch_sizer_choices(lib):
+    # (no GPU here: the sizer assumes MI355X's 256 CUs in 8 XCDs)
+    # S = CUs / units, capped at topk / 256 and 64; one split fewer where
+    # that puts every unit's splits on one XCD in one round of workgroups
+    assert lib.mla_sparse_decode_num_splits(1, 16, 256) == 1        # tiny
+    assert lib.mla_sparse_decode_num_splits(15, 32, 2048) == 8      # decode15 (topk cap)
+    assert lib.mla_sparse_decode_num_splits(35, 32, 2048) == 6      # padded35: 7 would not group
+    assert lib.mla_sparse_decode_num_splits(128, 32, 2048) == 2     # batch128
+    assert lib.mla_sparse_decode_num_splits(4096, 32, 2048) == 1    # prefill4k
+    assert lib.mla_sparse_decode_num_splits(40, 32, 2048) == 6      # 6 groups already
+    assert lib.mla_sparse_decode_num_splits(1, 32, 2048) == 8
