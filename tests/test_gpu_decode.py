@@ -145,6 +145,20 @@ def test_workspace_reuse_across_calls():
         assert row[1] == 0 and row[3] == 0, state
 
 
+@pytest.mark.parametrize("tokens,splits", [(32, 16), (8, 64), (100, 5)])
+def test_split_merge_when_the_grid_cannot_all_be_resident(tokens, splits):
+    # More workgroups than CUs (one per CU): no split waits, and the last
+    # arrival merges every unit, eight splits per batch with the running
+    # maximum carried across batches.  Short and empty token lists give
+    # splits with no rows (log2-sum-exp -inf) inside and across batches.
+    valid = [2048 if t % 4 == 0 else (37 * t) % 2049 for t in range(tokens)]
+    valid[1] = 0
+    w = make_custom(20000, tokens, 32, 2048, seed=40 + splits, device=DEV, valid_per_token=valid)
+    cache = _fill(w)
+    out, lse = _run(w, cache, num_splits=splits)
+    _check(w, cache, out, lse, tokens=sorted({0, 1, 2, 3, 5, tokens - 1}), what=f"T={tokens} S={splits}")
+
+
 @pytest.mark.parametrize("tokens,splits", [(15, 8), (35, 7), (128, 2), (1, 64), (3, 3)])
 def test_merge_split_between_splits_or_by_the_last_arrival(tokens, splits):
     # The slices of the split merge are combined by their own splits (they
