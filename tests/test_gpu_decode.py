@@ -272,6 +272,44 @@ def test_block_table_small(bs):
     _check(w, cache, out, lse, what=f"blocktable-bs{bs}")
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+def test_block_table_guards_past_width_and_bad_sequences(splits):
+    # Slots the block table cannot map are masked (the oracle's reading of
+    # an index list through a block table): positions past the table's width
+    # (token 0, mixed with valid ones), and every slot of a token whose
+    # sequence is outside the table (token 1: past the last row, token 2:
+    # negative), which then has out = 0 and lse = -inf.
+    bs, width, seqs = 64, 20, 2
+    w = make_custom(bs * 48, 4, 32, 512, seed=61, device=DEV)
+    rng = np.random.default_rng(61)
+    bt = np.stack([rng.permutation(48)[:width] for _ in range(seqs)]).astype(np.int32)
+    idx = np.stack([rng.choice(width * bs, 512, replace=False) for _ in range(4)]).astype(np.int64)
+    idx[0, 100:140] = width * bs + rng.integers(0, 5 * bs, 40)      # past the table's width
+    idx[0, 500] = width * bs                                          # (first position past it)
+    w.indices = torch.from_numpy(idx.astype(np.int32)).to(DEV)
+    w.block_table = torch.from_numpy(bt).to(DEV)
+    w.token_seq = torch.tensor([0, seqs, -1, 1], dtype=torch.int32, device=DEV)
+    w.block_size = bs
+    cache = _fill(w)
+    out, lse = _run(w, cache, num_splits=splits)
+    _check(w, cache, out, lse, what=f"bt-guards-S{splits}")
+    assert torch.all(out[1:3] == 0) and torch.all(torch.isneginf(lse[1:3]))
+    # the staged gather maps (and masks) the same slots: the oracle's staged
+    # rows over each slot's physical row (-1 where the table maps none)
+    from oracle import attention, codec
+    rows, sidx = mla.gather_dequant_fp8(cache, w.indices, 1.0, block_table=w.block_table,
+                                        token_seq=w.token_seq, block_size=bs)
+    torch.cuda.synchronize()
+    seq = w.token_seq.cpu().numpy()
+    pidx = np.full(idx.shape, -1, dtype=np.int64)
+    for t in range(4):
+        pidx[t] = attention.physical_rows(idx[t], int(seq[t]), bt, bs, w.pool_rows)
+    pool = parity.encode_rows(parity.host(w.latent), parity.host(w.rope))
+    ref_rows, ref_sidx = codec.staged_fp8_rows(pool, pidx)
+    assert np.array_equal(sidx.cpu().numpy(), ref_sidx)
+    assert np.array_equal(rows.cpu().numpy(), ref_rows)
+
+
 def test_fp8_rows_path():
     w = make_custom(3000, 3, 32, 512, seed=16, device=DEV, valid_per_token=[512, 200, 1])
     for kv in (1.0, 0.5):
