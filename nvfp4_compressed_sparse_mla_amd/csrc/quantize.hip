@@ -12,11 +12,10 @@
 
 namespace mla {
 
-// Sixteen fp16 or bf16 values as floats (exact), plus their sign bits.
+// Sixteen fp16 or bf16 values (two 16-byte words) as floats (exact), plus
+// their sign bits.
 template <bool kBf16>
-__device__ __forceinline__ void load16(const uint16_t* p, float (&v)[16], uint32_t& signs) {
-  const u32x4 a = *reinterpret_cast<const u32x4*>(p);
-  const u32x4 b = *reinterpret_cast<const u32x4*>(p + 8);
+__device__ __forceinline__ void unpack16(const u32x4& a, const u32x4& b, float (&v)[16], uint32_t& signs) {
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   signs = 0;
 #pragma unroll
@@ -32,6 +31,17 @@ __device__ __forceinline__ void load16(const uint16_t* p, float (&v)[16], uint32
     signs |= ((w[i] >> 15) & 1u) << (2 * i);
     signs |= ((w[i] >> 31) & 1u) << (2 * i + 1);
   }
+}
+
+template <bool kBf16>
+__device__ __forceinline__ void load16(const uint16_t* p, float (&v)[16], uint32_t& signs) {
+  unpack16<kBf16>(*reinterpret_cast<const u32x4*>(p), *reinterpret_cast<const u32x4*>(p + 8), v, signs);
+}
+
+template <bool kBf16>
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
+  if constexpr (kBf16) return __uint_as_float(bits << 16);
+  else return (float)__builtin_bit_cast(half_t, (uint16_t)bits);
 }
 
 template <bool kBf16>
@@ -56,13 +66,23 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_append_kernel(
   const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
   const int g = threadIdx.x & 31;
   if (row >= n) return;
+  // The row's values and its slot are loaded together (one memory round
+  // trip, not the slot's and then the values'); the tie keeps the compiler
+  // from moving the value loads behind the slot test.
+  const uint16_t* const lp = latent + row * lat_stride + 16 * g;
+  const u32x4 la = *reinterpret_cast<const u32x4*>(lp);
+  const u32x4 lb = *reinterpret_cast<const u32x4*>(lp + 8);
+  const uint32_t rw = *reinterpret_cast<const uint32_t*>(rope + row * rope_stride + 2 * g);   // rope 2g, 2g+1
   const int64_t slot = slots[row];
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" :: "v"(la), "v"(lb), "v"(rw));
+#endif
   if (slot < 0 || slot >= cache_rows) return;
   uint8_t* const stage = rows_s[threadIdx.x >> 5];
 
   float v[16];
   uint32_t signs;
-  load16<kBf16>(latent + row * lat_stride + 16 * g, v, signs);
+  unpack16<kBf16>(la, lb, v, signs);
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
@@ -80,9 +100,8 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_append_kernel(
   }
   *reinterpret_cast<u32x2*>(stage + 8 * g) = (u32x2){lo, hi};
   stage[kScaleOff + g] = (uint8_t)sc;
-  const uint16_t* rp = rope + row * rope_stride + 2 * g;
-  uint32_t r0 = e4m3_encode(load_scalar<kBf16>(rp));
-  uint32_t r1 = e4m3_encode(load_scalar<kBf16>(rp + 1));
+  const uint32_t r0 = e4m3_encode(half_bits_to_float<kBf16>(rw & 0xFFFFu));
+  const uint32_t r1 = e4m3_encode(half_bits_to_float<kBf16>(rw >> 16));
   *reinterpret_cast<uint16_t*>(stage + kRopeOff + 2 * g) = (uint16_t)(r0 | (r1 << 8));
   // the row's 32 lanes belong to one wave, whose LDS operations complete in
   // order: a wave-level wait makes the staged row visible to its own lanes
